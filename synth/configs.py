@@ -1,0 +1,125 @@
+"""Named workload shapes of the DeepSeekMoE layer forward pass.
+
+The five named workloads follow the shapes the pages give for DeepSeek-V3
+(256 routed experts of intermediate width 2048, top-8, one shared expert,
+hidden 7168; "DeepSeekMoE" explainer, sections 1 and 2.1) and for the 2024
+DeepSeekMoE layout (2 shared + 64 routed experts, 2+6 active, gates not
+renormalised; course notes, sections 3 and 4). Value distributions are the
+synthetic recipe of this library: x ~ N(0, x_std^2), weights ~ N(0, w_std^2),
+bias ~ U(-bias_range, bias_range).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+from typing import Optional
+
+SCORE_SIGMOID = "sigmoid"
+SCORE_SOFTMAX = "softmax"
+NORM_SELECTED = "selected"
+NORM_NONE = "none"
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int                 # tokens in the batch
+    d: int                 # hidden size
+    E: int                 # routed experts
+    K: int                 # experts selected per token
+    I: int                 # routed expert intermediate width
+    S: int                 # shared experts
+    Is: int                # shared expert intermediate width (each)
+    score: str = SCORE_SIGMOID
+    norm: str = NORM_SELECTED
+    act_dtype: str = "bf16"      # "f32" | "bf16"
+    weight_dtype: str = "bf16"   # "f32" | "bf16" | "fp8"
+    bias_range: Optional[float] = None   # None -> no bias tensor
+    x_std: float = 1.0
+    w_std: float = 0.02
+    seed: int = 20260100
+    # Zipf-popularity router construction (stress workload)
+    zipf_s: Optional[float] = None
+    zipf_A: Optional[float] = None
+    batches: int = 1
+    gamma: float = 1e-3
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def tk(self) -> int:
+        return self.T * self.K
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs of one layer call: router GEMM, routed SwiGLU
+        experts over the T*K selected (token, expert) pairs, shared experts."""
+        router = 2.0 * self.T * self.d * self.E
+        routed = 6.0 * self.d * self.I * self.T * self.K
+        shared = 6.0 * self.d * self.Is * self.S * self.T
+        return router + routed + shared
+
+    def weight_bytes_per_expert(self) -> int:
+        wb = {"f32": 4, "bf16": 2, "fp8": 1}[self.weight_dtype]
+        b = 3 * self.d * self.I * wb
+        if self.weight_dtype == "fp8":
+            b += 4 * (2 * self.I + self.d)
+        return b
+
+    def shared_weight_bytes(self) -> int:
+        wb = {"f32": 4, "bf16": 2, "fp8": 1}[self.weight_dtype]
+        b = 3 * self.d * self.Is * self.S * wb
+        if self.weight_dtype == "fp8":
+            b += 4 * (2 * self.Is * self.S + self.d)
+        return b
+
+    def act_bytes(self) -> int:
+        return {"f32": 4, "bf16": 2}[self.act_dtype]
+
+
+_BASE = 20260100
+
+CONFIGS = {
+    "tiny_f32": MoEConfig(
+        name="tiny_f32", T=64, d=128, E=16, K=2, I=64, S=1, Is=64,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="f32", weight_dtype="f32",
+        bias_range=0.1, x_std=0.02, w_std=0.02, seed=_BASE + 1,
+        description="Tiny fp32 layer: 16 routed + 1 shared expert, sigmoid, top-2, biased selection",
+    ),
+    "dsmoe2024_bf16": MoEConfig(
+        name="dsmoe2024_bf16", T=4096, d=2048, E=64, K=6, I=1408, S=2, Is=1408,
+        score=SCORE_SOFTMAX, norm=NORM_NONE, act_dtype="bf16", weight_dtype="bf16",
+        bias_range=None, x_std=1.0, w_std=0.02, seed=_BASE + 2,
+        description="DeepSeekMoE-2024 layout: 64 routed + 2 shared, softmax, top-6, no renormalisation",
+    ),
+    "v3_prefill_bf16": MoEConfig(
+        name="v3_prefill_bf16", T=8192, d=7168, E=256, K=8, I=2048, S=1, Is=2048,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="bf16",
+        bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 3,
+        description="V3-shape prefill: 256 routed + 1 shared, sigmoid, top-8 on score+bias",
+    ),
+    "v3_decode_fp8": MoEConfig(
+        name="v3_decode_fp8", T=64, d=7168, E=256, K=8, I=2048, S=1, Is=2048,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="fp8",
+        bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 4,
+        description="V3-shape decode: fp8-e4m3 expert weights with per-output-row fp32 scales",
+    ),
+    "zipf_stress_bf16": MoEConfig(
+        name="zipf_stress_bf16", T=32768, d=7168, E=256, K=8, I=2048, S=1, Is=2048,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="bf16",
+        bias_range=None, x_std=1.0, w_std=0.02, seed=_BASE + 5,
+        zipf_s=1.1, zipf_A=2.3828, batches=20, gamma=1e-3,   # A: oracle/calibrate_zipf.py
+        description="Zipf(1.1) expert popularity (hottest ~10x mean load), 20 batches + bias update",
+    ),
+}
+
+
+def get_config(name: str) -> MoEConfig:
+    return CONFIGS[name]
+
+
+def scaled_config(name: str, **overrides) -> MoEConfig:
+    """A named workload with some fields replaced (reduced sizes for tests)."""
+    base = CONFIGS[name]
+    new_name = overrides.pop("name", base.name + "_scaled")
+    return dataclasses.replace(base, name=new_name, **overrides)

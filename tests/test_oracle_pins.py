@@ -1,0 +1,420 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each test checks one oracle function against what the method's definition
+fixes independently of the oracle's code: a hand-worked example, brute force
+on tiny inputs, a library routine that is not the one the oracle calls,
+closed forms and invariants. Chosen so that a plausible slip (a dropped term,
+a wrong sign or index, a transposed operand, the bias leaking into the gates,
+softmax instead of eq. (13), a dropped token) fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import moe as om
+
+
+def _ev(s):
+    """Evaluate a fixture expression: numbers, + - * / **, and log()."""
+    return float(eval(str(s), {"__builtins__": {}}, {"log": math.log}))
+
+
+def _arr(rows):
+    return np.array([[_ev(v) for v in r] for r in rows], dtype=np.float64)
+
+
+@pytest.fixture(scope="module")
+def hand(golden_dir):
+    with open(os.path.join(golden_dir, "hand_layer_e4k2.json")) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Hand-worked layer (eqs. 13-16, shared + routed experts)
+# --------------------------------------------------------------------------
+
+def _hand_bank(hand):
+    exps = [(_arr(e["w1"]), _arr(e["w3"]), _arr(e["w2"])) for e in hand["experts"]]
+    sh = hand["shared"]
+    shared = (_arr(sh["w1"]), _arr(sh["w3"]), _arr(sh["w2"]), None, None, None)
+    return oracle.ExpertBank(fetch=lambda e: exps[e] + (None, None, None), shared=shared, S=1)
+
+
+def test_hand_worked_routing(hand):
+    x, wr = _arr(hand["x"]), _arr(hand["wr"])
+    bias = np.array([_ev(b) for b in hand["bias"]])
+    r = oracle.route(x, wr, bias, hand["K"], "sigmoid", "selected")
+    exp = hand["expected"]
+    np.testing.assert_allclose(r["scores"], _arr(exp["scores"]), rtol=0, atol=1e-15)
+    assert r["sel"].tolist() == exp["sel"]
+    np.testing.assert_allclose(r["gate"], _arr(exp["gate"]), rtol=0, atol=1e-15)
+    assert r["load"].tolist() == exp["load"]
+    assert r["near_tie"].tolist() == exp["near_tie"]
+
+
+def test_hand_worked_without_bias(hand):
+    x, wr = _arr(hand["x"]), _arr(hand["wr"])
+    r = oracle.route(x, wr, None, hand["K"], "sigmoid", "selected")
+    exp = hand["expected"]
+    assert r["sel"].tolist() == exp["sel_without_bias"]
+    np.testing.assert_allclose(r["gate"][0], [_ev(v) for v in exp["gate_without_bias_token0"]], atol=1e-15)
+
+
+def test_hand_worked_layer_output(hand):
+    x, wr = _arr(hand["x"]), _arr(hand["wr"])
+    bias = np.array([_ev(b) for b in hand["bias"]])
+    r = oracle.route(x, wr, bias, hand["K"], "sigmoid", "selected")
+    y, _, _ = oracle.layer_rows(x, r["sel"], r["gate"], _hand_bank(hand))
+    np.testing.assert_allclose(y, _arr(hand["expected"]["y"]), rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Top-K selection (eqs. 14 and 16)
+# --------------------------------------------------------------------------
+
+def _brute_topk(keys_row, K):
+    """All C(E, K) subsets: maximal exact key sum, lexicographically smallest
+    index tuple among equal sums (= lower index wins ties)."""
+    E = len(keys_row)
+    best = None
+    for sub in itertools.combinations(range(E), K):
+        s = sum(Fraction(keys_row[i]) for i in sub)
+        if best is None or s > best[0] or (s == best[0] and sub < best[1]):
+            best = (s, sub)
+    return set(best[1])
+
+
+@pytest.mark.parametrize("E,K", [(16, 2), (8, 3), (6, 6), (7, 1)])
+def test_topk_matches_brute_force(E, K):
+    rng = np.random.default_rng(1234 + E * 10 + K)
+    # dyadic keys from a small set: many exact ties, exact sums
+    keys = rng.integers(-4, 5, size=(60, E)).astype(np.float64) / 8.0
+    sel, gap = oracle.select_topk(keys, K)
+    for t in range(keys.shape[0]):
+        assert set(sel[t].tolist()) == _brute_topk(keys[t].tolist(), K)
+        assert len(set(sel[t].tolist())) == K
+        # key-descending order, lower index first among equal keys
+        ks = keys[t, sel[t]]
+        for a in range(K - 1):
+            assert ks[a] > ks[a + 1] or (ks[a] == ks[a + 1] and sel[t, a] < sel[t, a + 1])
+        if K < E:
+            rest = np.setdiff1d(np.arange(E), sel[t])
+            assert gap[t] == ks[-1] - keys[t, rest].max()
+        else:
+            assert gap[t] == np.inf
+
+
+def test_topk_matches_lexsort_with_ties():
+    rng = np.random.default_rng(7)
+    T, E, K = 300, 64, 8
+    keys = rng.random((T, E))
+    keys[::3, 5] = keys[::3, 9]          # injected exact ties
+    keys[::7, :] = 0.25                  # fully tied rows
+    sel, _ = oracle.select_topk(keys, K)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -keys[t]))
+        assert sel[t].tolist() == order[:K].tolist()
+
+
+def test_topk_matches_torch_topk_distinct():
+    rng = np.random.default_rng(8)
+    keys = rng.standard_normal((500, 256))
+    sel, _ = oracle.select_topk(keys, 8)
+    tv, ti = torch.topk(torch.from_numpy(keys), 8, dim=1, largest=True, sorted=True)
+    assert np.array_equal(sel, ti.numpy())
+
+
+# --------------------------------------------------------------------------
+# Scores and gates (eqs. 13, 15; 2024 softmax layout)
+# --------------------------------------------------------------------------
+
+def test_scores_match_scipy():
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((50, 64)) * 5.0
+    np.testing.assert_allclose(oracle.scores(lg, "sigmoid"), scipy.special.expit(lg), rtol=1e-15, atol=0)
+    np.testing.assert_allclose(oracle.scores(lg, "softmax"), scipy.special.softmax(lg, axis=1), rtol=1e-13, atol=0)
+
+
+def test_router_logits_orientation():
+    # x [T=2, d=3], wr [E=4, d=3]: logits[t, i] = <x_t, e_i>
+    x = np.array([[1.0, 2.0, 3.0], [0.0, -1.0, 0.5]])
+    wr = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 0.0], [0.0, 0.0, 1.0], [1.0, 1.0, 1.0]])
+    np.testing.assert_array_equal(oracle.router_logits(x, wr), [[1, 2, 3, 6], [0, -1, 0.5, -0.5]])
+
+
+def test_zero_router_sigmoid():
+    T, d, E, K = 10, 16, 12, 4
+    x = np.random.default_rng(0).standard_normal((T, d))
+    r = oracle.route(x, np.zeros((E, d)), None, K, "sigmoid", "selected")
+    assert np.all(r["scores"] == 0.5)
+    assert r["sel"].tolist() == [list(range(K))] * T
+    np.testing.assert_array_equal(r["gate"], np.full((T, K), 1.0 / K))
+
+
+def test_zero_router_softmax_unnormalised():
+    T, d, E, K = 10, 16, 64, 6
+    x = np.random.default_rng(1).standard_normal((T, d))
+    r = oracle.route(x, np.zeros((E, d)), None, K, "softmax", "none")
+    np.testing.assert_allclose(r["gate"], np.full((T, K), 1.0 / E), rtol=1e-15)
+    np.testing.assert_allclose(r["gate"].sum(1), K / E, rtol=1e-14)
+
+
+def test_gates_sum_to_one_v3():
+    rng = np.random.default_rng(4)
+    x, wr = rng.standard_normal((200, 64)), rng.standard_normal((32, 64)) * 0.2
+    r = oracle.route(x, wr, rng.uniform(-0.05, 0.05, 32), 8, "sigmoid", "selected")
+    np.testing.assert_allclose(r["gate"].sum(1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(r["gate"] > 0)
+
+
+def test_gates_2024_unnormalised():
+    rng = np.random.default_rng(5)
+    x, wr = rng.standard_normal((200, 64)), rng.standard_normal((64, 64)) * 0.3
+    r = oracle.route(x, wr, None, 6, "softmax", "none")
+    tot = r["gate"].sum(1)
+    assert np.all(tot < 1.0) and np.all(tot > 0.0)
+    rest = r["scores"].sum(1) - tot
+    np.testing.assert_allclose(tot, 1.0 - rest, atol=1e-14)
+    # the gates are the selected softmax scores themselves
+    np.testing.assert_array_equal(r["gate"], np.take_along_axis(r["scores"], r["sel"], 1))
+
+
+def test_bias_changes_selection_not_gate_values():
+    rng = np.random.default_rng(6)
+    x, wr = rng.standard_normal((400, 32)), rng.standard_normal((32, 32)) * 0.3
+    b = rng.uniform(-0.05, 0.05, 32)
+    r0 = oracle.route(x, wr, None, 4, "sigmoid", "selected")
+    r1 = oracle.route(x, wr, b, 4, "sigmoid", "selected")
+    same = np.all(np.sort(r0["sel"], 1) == np.sort(r1["sel"], 1), axis=1)
+    assert same.any() and (~same).any()
+    for t in np.flatnonzero(same):
+        g0 = dict(zip(r0["sel"][t].tolist(), r0["gate"][t].tolist()))
+        g1 = dict(zip(r1["sel"][t].tolist(), r1["gate"][t].tolist()))
+        # same gate per expert; only the order of the K-term sum may differ
+        assert g0.keys() == g1.keys()
+        for e in g0:
+            assert g0[e] == pytest.approx(g1[e], rel=1e-15)
+
+
+def test_forcing_bias_selects_set_and_keeps_gates():
+    rng = np.random.default_rng(9)
+    E, K = 16, 3
+    x, wr = rng.standard_normal((50, 8)), rng.standard_normal((E, 8)) * 0.5
+    forced = [2, 11, 7]
+    b = np.zeros(E)
+    b[forced] = 10.0
+    r = oracle.route(x, wr, b, K, "sigmoid", "selected")
+    assert all(set(s) == set(forced) for s in r["sel"].tolist())
+    s = r["scores"][:, forced]
+    want = s / s.sum(1, keepdims=True)
+    got = np.stack([[dict(zip(r["sel"][t], r["gate"][t]))[e] for e in forced] for t in range(50)])
+    np.testing.assert_allclose(got, want, rtol=1e-15)
+    b2 = b * 2
+    r2 = oracle.route(x, wr, b2, K, "sigmoid", "selected")
+    np.testing.assert_array_equal(r2["gate"], r["gate"])
+
+
+def test_k_equals_e_bias_independent():
+    rng = np.random.default_rng(10)
+    E, d = 6, 8
+    x, wr = rng.standard_normal((20, d)), rng.standard_normal((E, d))
+    bank, _ = _random_bank(rng, E, d, 4, S=1, Is=4)
+    ra = oracle.route(x, wr, None, E, "sigmoid", "selected")
+    rb = oracle.route(x, wr, rng.uniform(-1, 1, E), E, "sigmoid", "selected")
+    ya, _, _ = oracle.layer_rows(x, ra["sel"], ra["gate"], bank)
+    yb, _, _ = oracle.layer_rows(x, rb["sel"], rb["gate"], bank)
+    np.testing.assert_allclose(ya, yb, rtol=1e-13, atol=1e-15)
+    assert np.all(ra["gap"] == np.inf)
+
+
+# --------------------------------------------------------------------------
+# Loads and permutation (no token dropping)
+# --------------------------------------------------------------------------
+
+def test_loads_and_permutation_vs_library():
+    rng = np.random.default_rng(11)
+    T, E, K = 333, 40, 5
+    keys = rng.random((T, E))
+    sel, _ = oracle.select_topk(keys, K)
+    load = oracle.expert_loads(sel, E)
+    assert np.array_equal(load, np.bincount(sel.ravel(), minlength=E))
+    assert load.sum() == T * K
+    assert all(len(set(r)) == K for r in sel.tolist())
+    off, perm = oracle.permutation(sel, E)
+    assert np.array_equal(perm, np.argsort(sel.ravel(), kind="stable"))
+    assert np.array_equal(off[1:], np.cumsum(np.bincount(sel.ravel(), minlength=E)))
+    assert off[0] == 0 and np.array_equal(np.sort(perm), np.arange(T * K))
+
+
+# --------------------------------------------------------------------------
+# SwiGLU expert and combine
+# --------------------------------------------------------------------------
+
+def test_swiglu_scalar_closed_form():
+    # d = I = 1: E(x) = w2 * SiLU(w1 x) * (w3 x); at w1 x = log 3, sigmoid = 3/4
+    y = oracle.swiglu_expert(np.array([[math.log(3)]]), np.array([[1.0]]), np.array([[2.0]]), np.array([[3.0]]))
+    assert y[0, 0] == pytest.approx(4.5 * math.log(3) ** 2, rel=1e-15)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_swiglu_gate_vs_up_and_orientation():
+    # I = 3, d = 2: W1, W3 are [I, d], W2 is [d, I]
+    v = np.array([[1.0, 2.0]])
+    w1 = np.array([[40.0, 0.0], [-40.0, 0.0], [0.0, 0.0]])
+    w3 = np.array([[0.0, 1.0], [0.0, 1.0], [5.0, 5.0]])
+    w2 = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, 7.0]])
+    y = oracle.swiglu_expert(v, w1, w3, w2)
+    # h = [SiLU(40)*2, SiLU(-40)*2, SiLU(0)*15] ~ [80, ~0, 0]
+    assert y[0, 0] == pytest.approx(80.0, rel=1e-15)
+    assert abs(y[0, 1]) < 1e-14
+
+
+def test_swiglu_linearity_and_zero_gate():
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal((5, 8))
+    w1, w3, w2 = rng.standard_normal((6, 8)), rng.standard_normal((6, 8)), rng.standard_normal((8, 6))
+    y = oracle.swiglu_expert(v, w1, w3, w2)
+    np.testing.assert_allclose(oracle.swiglu_expert(v, w1, w3, 2 * w2), 2 * y, rtol=1e-15)
+    np.testing.assert_allclose(oracle.swiglu_expert(v, w1, 3 * w3, w2), 3 * y, rtol=1e-13, atol=1e-13 * np.abs(y).max())
+    assert np.all(oracle.swiglu_expert(v, np.zeros_like(w1), w3, w2) == 0)
+    assert np.all(oracle.swiglu_expert(v, w1, np.zeros_like(w3), w2) == 0)
+
+
+def _random_bank(rng, E, d, I, S=0, Is=0, identical=False):
+    ws = [(rng.standard_normal((I, d)) * 0.3, rng.standard_normal((I, d)) * 0.3, rng.standard_normal((d, I)) * 0.3)
+          for _ in range(1 if identical else E)]
+    fetch = (lambda e: ws[0] + (None, None, None)) if identical else (lambda e: ws[e] + (None, None, None))
+    shared = None
+    if S:
+        shared = (rng.standard_normal((S * Is, d)) * 0.3, rng.standard_normal((S * Is, d)) * 0.3,
+                  rng.standard_normal((d, S * Is)) * 0.3, None, None, None)
+    return oracle.ExpertBank(fetch=fetch, shared=shared, S=S), ws
+
+
+@pytest.mark.parametrize("score,norm", [("sigmoid", "selected"), ("softmax", "none")])
+def test_identical_experts(score, norm):
+    rng = np.random.default_rng(13)
+    E, d, I, K = 10, 12, 7, 3
+    bank, ws = _random_bank(rng, E, d, I, identical=True)
+    x, wr = rng.standard_normal((30, d)), rng.standard_normal((E, d))
+    r = oracle.route(x, wr, None, K, score, norm)
+    y, ysh, _ = oracle.layer_rows(x, r["sel"], r["gate"], bank)
+    assert np.all(ysh == 0)
+    one = oracle.swiglu_expert(x, *ws[0])
+    np.testing.assert_allclose(y, r["gate"].sum(1, keepdims=True) * one, rtol=1e-12, atol=1e-14)
+    if norm == "selected":
+        np.testing.assert_allclose(y, one, rtol=1e-12, atol=1e-14)
+
+
+def test_shared_concat_identity():
+    rng = np.random.default_rng(14)
+    d, Is = 8, 5
+    w1s, w3s, w2s = rng.standard_normal((2 * Is, d)), rng.standard_normal((2 * Is, d)), rng.standard_normal((d, 2 * Is))
+    x = rng.standard_normal((9, d))
+    sel, gate = np.zeros((9, 1), dtype=np.int64), np.zeros((9, 1))
+    zero = oracle.ExpertBank(fetch=lambda e: (np.zeros((1, d)), np.zeros((1, d)), np.zeros((d, 1)), None, None, None),
+                             shared=(w1s, w3s, w2s, None, None, None), S=2)
+    two, ysh2, _ = oracle.layer_rows(x, sel, gate, zero)
+    zero.S = 1
+    one, ysh1, _ = oracle.layer_rows(x, sel, gate, zero)
+    np.testing.assert_allclose(two, one, rtol=1e-13, atol=1e-14)
+    # and the two halves are really two experts summed
+    a = oracle.swiglu_expert(x, w1s[:Is], w3s[:Is], w2s[:, :Is])
+    b = oracle.swiglu_expert(x, w1s[Is:], w3s[Is:], w2s[:, Is:])
+    np.testing.assert_allclose(ysh2, a + b, rtol=1e-13, atol=1e-14)
+
+
+def test_routed_linearity_in_down_projection():
+    rng = np.random.default_rng(15)
+    E, d, I, K = 6, 8, 4, 2
+    bank, ws = _random_bank(rng, E, d, I, S=1, Is=3)
+    bank2 = oracle.ExpertBank(fetch=lambda e: (ws[e][0], ws[e][1], 2 * ws[e][2], None, None, None),
+                              shared=bank.shared, S=1)
+    x, wr = rng.standard_normal((20, d)), rng.standard_normal((E, d))
+    r = oracle.route(x, wr, None, K, "sigmoid", "selected")
+    y1, s1, _ = oracle.layer_rows(x, r["sel"], r["gate"], bank)
+    y2, s2, _ = oracle.layer_rows(x, r["sel"], r["gate"], bank2)
+    np.testing.assert_allclose(y2 - s2, 2 * (y1 - s1), rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Stored formats
+# --------------------------------------------------------------------------
+
+def test_e4m3_table_vs_torch():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = oracle.E4M3_TABLE
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ref[~nan], ours[~nan])
+
+
+def test_e4m3_spot_values(golden_dir):
+    with open(os.path.join(golden_dir, "e4m3_spot_values.json")) as f:
+        g = json.load(f)
+    for code, expr in g["values"].items():
+        want = -0.0 if expr == "-0" else _ev(expr)
+        got = oracle.E4M3_TABLE[int(code)]
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+    for c in g["nan_codes"]:
+        assert math.isnan(oracle.E4M3_TABLE[c])
+    assert np.nanmax(np.abs(oracle.E4M3_TABLE)) == 448.0
+
+
+def test_bf16_decode_vs_torch():
+    bits = torch.arange(0, 65536, 37, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    ours = oracle.bf16_to_f64(bits.numpy().view(np.uint16))
+    fin = np.isfinite(ref)
+    assert np.array_equal(ref[fin], ours[fin])
+
+
+def test_fp8_row_scale_applied_per_output_row():
+    codes = np.array([[56, 64], [56, 64]], dtype=np.uint8)        # [[1, 2], [1, 2]]
+    got = oracle.decode_stored(codes, np.array([0.5, 3.0], dtype=np.float32))
+    np.testing.assert_array_equal(got, [[0.5, 1.0], [3.0, 6.0]])
+
+
+# --------------------------------------------------------------------------
+# Bias update (section 2.2)
+# --------------------------------------------------------------------------
+
+def test_bias_update_signs():
+    # E = 4, loads sum to 8, mean 2: over, at, under, under -> -g, 0, +g, +g
+    b = np.zeros(4, dtype=np.float32)
+    nb = oracle.bias_update(b, np.array([5, 2, 1, 0]))
+    g = np.float32(1e-3)
+    assert nb.dtype == np.float32
+    assert nb.tolist() == [-g, 0.0, g, g]
+    # mean is not an integer: 7/4 -> 2 is over, 1 is under
+    nb = oracle.bias_update(b, np.array([2, 1, 4, 0]))
+    assert nb.tolist() == [-g, g, -g, g]
+
+
+def test_bias_update_trajectory_closed_form():
+    # an expert overloaded in each of n batches ends near -n*gamma, with only
+    # fp32 rounding of each exact step in between
+    b = np.zeros(3, dtype=np.float32)
+    n = 20
+    for _ in range(n):
+        b = oracle.bias_update(b, np.array([10, 1, 1]))
+    g = float(np.float32(1e-3))
+    assert abs(float(b[0]) + n * g) < n * 2e-10
+    assert abs(float(b[1]) - n * g) < n * 2e-10
+    assert b[1] == b[2] == -b[0]
+
+
+def test_near_tie_flag_threshold():
+    keys = np.array([[1.0, 0.5, 0.5 - 2e-5, 0.0], [1.0, 0.5, 0.5 - 5e-6, 0.0]])
+    sel, gap = oracle.select_topk(keys, 2)
+    assert (gap < oracle.NEAR_TIE_GAP).tolist() == [False, True]
