@@ -1,0 +1,228 @@
+/*
+ * libmoe -- the DeepSeekMoE layer forward pass on one AMD Instinct MI355X
+ * (gfx950), as a C ABI.
+ *
+ * Sources of the method (web pages):
+ *   [DSMoE]  "DeepSeekMoE架构解析：共享+路由专家协同与无丢弃门控设计" (jsqmd.com):
+ *            section 1 (shared + fine-grained routed experts, no token
+ *            dropping), section 2.1 (eqs. 13-15: sigmoid affinity, top-K,
+ *            normalisation over the selected experts), section 2.2 (eq. 16
+ *            and the bias update rule), section 3.1 (layer sketch: router
+ *            weights, bias vector, gathered gate values, weighted sum).
+ *   [COURSE] "省钱第一招：把一个大厨换成专家团" (blog.zero43.top): section 三
+ *            (2 shared + 64 routed experts, 2+6 active), section 四 (the
+ *            2024 gates are not renormalised), section 五 (bias outside the
+ *            training objective), section 六 (no dropped tokens).
+ *
+ * Call sequence for one layer call (all on one stream, or the shared expert
+ * on a second stream joined before moe_combine):
+ *
+ *   moe_route -> moe_permute -> moe_expert_ffn --+--> moe_combine
+ *   moe_shared_ffn ------------------------------+
+ *   (per batch, optionally) moe_bias_update
+ *
+ * Conventions shared by every call:
+ *   - Every pointer except `cfg` and `status` strings is a DEVICE pointer to
+ *     row-major contiguous memory that the caller owns and keeps alive until
+ *     the enqueued work has finished. The library allocates nothing, keeps
+ *     no global state between calls and never synchronises the stream.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     call that returns an error has enqueued nothing. MOE_OK means
+ *     "enqueued": device faults surface at the caller's next
+ *     synchronisation.
+ *   - num_tokens == 0 is a no-op that returns MOE_OK (for moe_route the
+ *     load vector is still zeroed).
+ *   - `stream` is a hipStream_t passed as void* (0 = the null stream).
+ *   - Activations (x, x_perm, out_slots) have the activation dtype of `cfg`
+ *     (fp32 or bf16); the router weights have it too. The shared-expert
+ *     output y_shared is always fp32 and the layer output y has
+ *     cfg->out_dtype, so the sum of the shared and routed terms is formed
+ *     and kept at fp32 accumulation precision. Expert weights have the weight dtype: fp32, bf16 (with
+ *     bf16 activations) or fp8 E4M3 (OCP E4M3FN codes, with bf16
+ *     activations) plus one fp32 scale per output row.
+ *   - Inputs must be finite; results for non-finite inputs are undefined.
+ *   - Calls on different streams with disjoint outputs may run concurrently.
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes -------------------------------------------------------- */
+#define MOE_OK               0
+#define MOE_ERR_NULL         1  /* a required pointer is NULL                  */
+#define MOE_ERR_SHAPE        2  /* sizes out of range or not supported          */
+#define MOE_ERR_DTYPE        3  /* dtype enum unknown or combination invalid    */
+#define MOE_ERR_UNSUPPORTED  4  /* valid request this build does not implement  */
+#define MOE_ERR_WORKSPACE    5  /* workspace NULL or smaller than required      */
+#define MOE_ERR_HIP          6  /* the HIP runtime reported a launch error      */
+
+/* ---- enums --------------------------------------------------------------- */
+#define MOE_SCORE_SIGMOID 0  /* s = sigmoid(u^T e_i), per expert ([DSMoE] eq. 15)          */
+#define MOE_SCORE_SOFTMAX 1  /* s = softmax over all routed experts (2024 layout, [COURSE]) */
+
+#define MOE_NORM_SELECTED 0  /* g = s / sum of the K selected s ([DSMoE] eq. 13)           */
+#define MOE_NORM_NONE     1  /* g = s of the selected experts ([COURSE] section 四)        */
+
+#define MOE_DTYPE_F32      0
+#define MOE_DTYPE_BF16     1
+#define MOE_DTYPE_FP8_E4M3 2  /* weights only */
+
+#define MOE_WS_ROUTE   0
+#define MOE_WS_PERMUTE 1
+#define MOE_WS_FFN     2
+#define MOE_WS_SHARED  3
+#define MOE_WS_GEMM    4  /* moe_expert_gate_up / moe_expert_down */
+
+/* Layer shape and options. Limits (checked by moe_validate): num_tokens >= 0
+ * with num_tokens * top_k < 2^30; 1 <= num_experts <=
+ * 256; 1 <= top_k <= num_experts; hidden and inter are positive multiples
+ * of 64; num_shared >= 0 and, when positive, num_shared * shared_inter is a
+ * positive multiple of 64 (num_shared == 0 means no shared expert). */
+typedef struct moe_config {
+  int32_t num_tokens;    /* T: tokens in the batch                               */
+  int32_t hidden;        /* d: hidden size                                       */
+  int32_t num_experts;   /* E: routed experts                                    */
+  int32_t top_k;         /* K: routed experts per token ([DSMoE] K_r)            */
+  int32_t inter;         /* I: routed expert intermediate width                  */
+  int32_t num_shared;    /* S: shared experts (always on, [DSMoE] section 1)     */
+  int32_t shared_inter;  /* Is: intermediate width of each shared expert         */
+  int32_t score_fn;      /* MOE_SCORE_*                                          */
+  int32_t norm;          /* MOE_NORM_*                                           */
+  int32_t act_dtype;     /* MOE_DTYPE_F32 or MOE_DTYPE_BF16                      */
+  int32_t weight_dtype;  /* MOE_DTYPE_F32 (with f32 act), BF16 or FP8_E4M3 (bf16) */
+  int32_t out_dtype;     /* layer output y: MOE_DTYPE_F32, or MOE_DTYPE_BF16 with
+                            bf16 activations (then y carries one more bf16 rounding) */
+} moe_config;
+
+/* Validate a configuration without touching the GPU. Returns a status code. */
+int moe_validate(const moe_config* cfg);
+
+/* Bytes of workspace the call named by `which` (MOE_WS_*) needs for `cfg`,
+ * or 0 if it needs none (or cfg is invalid). Workspaces need 256-byte
+ * alignment and must not be shared by calls that may run concurrently. */
+size_t moe_workspace_size(const moe_config* cfg, int which);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* moe_status_string(int status);
+
+/* ---- moe_route ------------------------------------------------------------
+ * Gating of [DSMoE] section 2.1 with the bias of section 2.2 (eq. 16):
+ *   logits[t,i] = sum_j x[t,j] * w_router[i,j]          (u_t^T e_i)
+ *   s[t,i]      = sigmoid(logits) or softmax_i(logits)  (cfg->score_fn)
+ *   key[t,i]    = s[t,i] + bias[i]   (bias == NULL: key = s)
+ *   topk_idx[t] = the K experts with the largest key, in key-descending
+ *                 order, the lower expert index first among equal keys
+ *   topk_gate[t,k] = s[t, topk_idx[t,k]] / sum_k' s[t, topk_idx[t,k']]
+ *                 (MOE_NORM_SELECTED) or s[t, topk_idx[t,k]] (MOE_NORM_NONE);
+ *                 the bias never enters the gate values
+ *   load[i]     = number of (t, k) with topk_idx[t,k] == i (overwritten;
+ *                 sums to T*K: no token is dropped)
+ * x [T, d] act dtype; w_router [E, d] act dtype (row i = centroid e_i);
+ * bias [E] fp32 or NULL; topk_idx [T, K] int32; topk_gate [T, K] fp32;
+ * load [E] int32. Logits are accumulated in fp32; scores and keys are fp32.
+ * Workspace: moe_workspace_size(cfg, MOE_WS_ROUTE) bytes (may be 0, then ws
+ * may be NULL). */
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+              int32_t* topk_idx, float* topk_gate, int32_t* load,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_permute ----------------------------------------------------------
+ * Groups the T*K (token, slot) pairs by expert for the grouped expert GEMMs
+ * (the gather of [DSMoE] section 3.1), stable in token order. No pair is
+ * dropped ([DSMoE] section 1): every selected (token, expert) gets a row.
+ *   expert_offsets[e] = number of pairs with expert < e,  expert_offsets[E]
+ *   = T*K; rows expert_offsets[e] .. expert_offsets[e+1]-1 hold, in
+ *   increasing slot order, the slots f = t*K + k with topk_idx[t,k] == e;
+ *   perm_slot[p] = the slot at row p;   x_perm[p, :] = x[perm_slot[p] / K, :]
+ * The offsets are counted from topk_idx itself (they equal the exclusive
+ * scan of moe_route's load vector). Entries of topk_idx outside [0, E) are
+ * never produced by moe_route; if present they get no row, the last rows
+ * get perm_slot = -1 and zero x_perm rows, and expert_offsets[E] < T*K.
+ * topk_idx [T, K] int32; x [T, d] act dtype; expert_offsets [E+1] int32;
+ * perm_slot [T*K] int32; x_perm [T*K, d] act dtype. Integer results are
+ * exact. Workspace: moe_workspace_size(cfg, MOE_WS_PERMUTE) bytes. */
+int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                int32_t* expert_offsets, int32_t* perm_slot, void* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_expert_ffn -------------------------------------------------------
+ * The routed SwiGLU experts ([DSMoE] section 1: fine-grained experts of
+ * intermediate width I) on the grouped rows, weighted by their gates and
+ * written back to their slots (the weighted sum's terms, [DSMoE] section 3.1):
+ *   for row p of expert e, with slot f = perm_slot[p]:
+ *     h = SiLU(W1_e x_perm[p]) * (W3_e x_perm[p])         (SiLU(z) = z*sigmoid(z))
+ *     out_slots[f, :] = topk_gate[f] * (W2_e h)
+ * w1, w3 [E, I, d]; w2 [E, d, I] in the weight dtype. For fp8 weights s1, s3
+ * [E, I] and s2 [E, d] are the fp32 scales of each output row (the stored
+ * code times the scale is the weight); they must be NULL otherwise.
+ * x_perm, expert_offsets, perm_slot from moe_permute; topk_gate [T*K] from
+ * moe_route; out_slots [T*K, d] act dtype. Accumulation is fp32; h is held
+ * in the activation dtype. Workspace: MOE_WS_FFN bytes. */
+int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                   const int32_t* perm_slot, const float* topk_gate,
+                   const void* w1, const void* w3, const void* w2,
+                   const float* s1, const float* s3, const float* s2,
+                   void* out_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_expert_gate_up / moe_expert_down --------------------------------
+ * The two halves of moe_expert_ffn, for callers that hold the intermediate
+ * activations themselves (and to time each grouped GEMM on its own):
+ *   moe_expert_gate_up: h[p, :] = SiLU(W1_e x_perm[p]) * (W3_e x_perm[p])
+ *   moe_expert_down:    out_slots[perm_slot[p], :] = topk_gate[perm_slot[p]]
+ *                                                    * (W2_e h[p])
+ * for every row p of expert e. h [T*K, I] act dtype. Scales as for
+ * moe_expert_ffn (gate_up takes s1, s3; down takes s2). Workspace:
+ * moe_workspace_size(cfg, MOE_WS_GEMM) bytes each. moe_expert_ffn is
+ * exactly gate_up followed by down with h held in its workspace. */
+int moe_expert_gate_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                       const void* w1, const void* w3, const float* s1, const float* s3,
+                       void* h, void* ws, size_t ws_bytes, void* stream);
+int moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                    const int32_t* perm_slot, const float* topk_gate, const void* w2,
+                    const float* s2, void* out_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_shared_ffn -------------------------------------------------------
+ * The always-on shared experts ([DSMoE] section 1; [COURSE] section 三) on
+ * every token: y_shared[t] = sum_m W2s_m (SiLU(W1s_m x[t]) * (W3s_m x[t])).
+ * The S experts are passed concatenated, which computes the same sum:
+ * w1s, w3s [S*Is, d] (expert m = rows m*Is .. (m+1)*Is-1), w2s [d, S*Is]
+ * (expert m = columns m*Is ..). fp8: s1s, s3s [S*Is] and s2s [d] row scales.
+ * x [T, d] act dtype; y_shared [T, d] fp32. Requires num_shared > 0.
+ * Workspace: MOE_WS_SHARED bytes. */
+int moe_shared_ffn(const moe_config* cfg, const void* x, const void* w1s, const void* w3s,
+                   const void* w2s, const float* s1s, const float* s3s, const float* s2s,
+                   void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_combine ----------------------------------------------------------
+ * The layer output: shared experts plus the gate-weighted routed experts
+ * ([DSMoE] section 1 and the weighted sum of section 3.1; no residual):
+ *   y[t, :] = y_shared[t, :] + sum_{k=0..K-1} out_slots[t*K + k, :]
+ * summed in fp32 in exactly this order (deterministic), rounded once to
+ * cfg->out_dtype. y_shared may be NULL (then it counts as zero).
+ * out_slots [T*K, d] act dtype; y_shared [T, d] fp32; y [T, d] out_dtype. */
+int moe_combine(const moe_config* cfg, const void* out_slots, const void* y_shared,
+                void* y, void* stream);
+
+/* ---- moe_bias_update ------------------------------------------------------
+ * Auxiliary-loss-free balance step of [DSMoE] section 2.2 ([COURSE] section
+ * 五: applied after each batch, outside the gradient):
+ *   bias[i] <- bias[i] - gamma * sign(load[i] - mean(load))
+ * with mean(load) = sum(load)/E decided exactly in integers as
+ * sign(load[i]*E - sum(load)); an expert exactly at the mean is unchanged.
+ * The subtraction is one IEEE fp32 operation. load [E] int32, bias [E] fp32
+ * in place; 1 <= num_experts <= 256; gamma finite and >= 0 (the pages use
+ * 1e-3). */
+int moe_bias_update(int32_t num_experts, const int32_t* load, float gamma, float* bias,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

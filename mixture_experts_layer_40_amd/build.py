@@ -1,0 +1,70 @@
+"""Build libmoe.so (all HIP sources, gfx950) in-tree next to this file.
+
+    python -m mixture_experts_layer_40_amd.build [--verbose]
+
+The library is plain hipcc output: one shared object exporting the C ABI of
+include/libmoe.h. Packed-fp32 instruction selection is disabled for device
+code (-packed-fp32-ops); hipcc's host pass warns that it does not know the
+feature, which is harmless.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; libmoe needs ROCm's hipcc to build")
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-function",
+           f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + sources() + list(extra_flags or [])
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "is not a recognized feature for this target" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("libmoe build failed:\n" + out)
+    if verbose and out.strip():
+        print(out)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--resource-usage", action="store_true",
+                    help="print per-kernel register/LDS usage from the compiler")
+    args = ap.parse_args(argv)
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if args.resource_usage else []
+    path = build(verbose=args.verbose or args.resource_usage, extra_flags=extra)
+    print(path)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,108 @@
+// Device-side building blocks shared by the libmoe kernels (gfx950 / CDNA4).
+//
+// Conventions used throughout:
+//  * Waves are 64 lanes; blocks are 256 threads (4 waves) unless noted.
+//  * MFMA tiles use v_mfma_f32_16x16x32_bf16. For one instruction, lane l
+//    supplies 8 consecutive K-elements of row (l % 16) of the first operand
+//    and of column (l % 16) of the second; lane group g = l / 16 owns
+//    K-elements 8g .. 8g+7; the 16x16 fp32 result leaves rows 4g .. 4g+3 of
+//    column (l % 16) in lane l.
+//  * GEMMs are written in the "weights as rows" orientation: the first MFMA
+//    operand is a block of weight rows (output features), the second a block
+//    of token rows, so one lane ends up holding 4 consecutive output features
+//    of one token and can store them as one 8-byte vector.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 4 fp8 E4M3 codes (one dword) -> 4 bf16 (two dwords). Every E4M3 value is
+// exactly representable in bf16, so the conversion is lossless.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t q) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, true);
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// 16 fp8 codes -> two MFMA operands of 8 bf16 each (codes 0..7, 8..15).
+__device__ __forceinline__ void fp8x16_to_bf16x16(const u32x4& q, u32x4& a0, u32x4& a1) {
+  u32x2 p0 = fp8x4_to_bf16x4(q.x), p1 = fp8x4_to_bf16x4(q.y);
+  u32x2 p2 = fp8x4_to_bf16x4(q.z), p3 = fp8x4_to_bf16x4(q.w);
+  a0 = u32x4{p0.x, p0.y, p1.x, p1.y};
+  a1 = u32x4{p2.x, p2.y, p3.x, p3.y};
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+template <typename T>
+__device__ __forceinline__ T load_nt(const T* p) { return *p; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// Wave-wide reductions with a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Lanes below the calling lane, as a 64-bit mask.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Remap a block id so that XCD x receives a contiguous range of work items,
+// which keeps the tiles that share a weight block on one L2.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_contiguous(int bid, int total, bool& valid) {
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int xcd = bid % kNumXcd, slot = bid / kNumXcd;
+  const int item = xcd * per + slot;
+  valid = slot < per && item < total;
+  return item;
+}
+
+}  // namespace moe

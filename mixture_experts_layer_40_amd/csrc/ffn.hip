@@ -1,0 +1,499 @@
+// Grouped SwiGLU expert GEMMs: routed experts over expert-contiguous rows and
+// the always-on shared expert(s) over all tokens.
+//
+// Method: fine-grained routed experts plus shared experts ("DeepSeekMoE架构解析"
+// section 1); each expert is a SwiGLU FFN E(v) = W2 (SiLU(W1 v) * (W3 v)) and
+// each routed output is weighted by its gate (section 2.1, eq. 13) before the
+// weighted sum (section 3.1 sketch). The shared experts are passed
+// concatenated (W1, W3 stacked by rows, W2 by columns), which is the same sum.
+//
+// CDNA4 design (bf16 / fp8 weights):
+//  * Orientation: weight rows are the first MFMA operand, token rows the
+//    second. A block computes 256 weight rows x up to 128 tokens of one
+//    expert; each of its 4 waves owns 64 weight rows and all tokens of the
+//    tile. Weight rows are never shared between waves, so every wave streams
+//    its rows straight from HBM into MFMA operand registers (fp8 codes are
+//    widened to bf16 in registers, exactly); only the token tile, which all
+//    4 waves read, is staged through LDS (double buffered, XOR-swizzled
+//    16-byte chunks, conflict-free reads and writes).
+//  * Skew: token fragments of 16 beyond an expert's row count are skipped, so
+//    an expert with 3 rows costs one fragment of MFMA work while its weights
+//    are still read exactly once per token tile.
+//  * Tiles are ordered (expert, weight block, token block) with the token
+//    block fastest and dealt to XCDs in contiguous ranges, so the token tiles
+//    that share a weight block run together on one XCD and its L2.
+//  * Gate/up: the 64 rows of a wave are 32 gate (W1) rows and the 32 up (W3)
+//    rows of the same intermediate columns, so SiLU(g) * u is formed in
+//    registers and H is written once in bf16.
+//  * Down: the epilogue multiplies by the fp8 row scale and the token's gate
+//    and writes the row straight to its (token, slot) position.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBM = 128;          // tokens per tile (bf16 / fp8 path)
+constexpr int kBNGate = 128;      // intermediate columns per gate/up tile (x2 rows: W1 + W3)
+constexpr int kBNDown = 256;      // output rows per down tile
+constexpr int kBMF32 = 32;        // tokens per tile (fp32 path)
+constexpr int kBNF32 = 32;        // columns per tile (fp32 path)
+
+enum { kGateUp = 0, kDown = 1 };
+
+struct GemmArgs {
+  const void* act;            // [rows, kdim] activations (bf16 or fp32)
+  const void* wa;             // gate/up: W1; down: W2   -- expert-major
+  const void* wb;             // gate/up: W3
+  const float* sa;            // fp8 row scales of wa ([E, n]) or null
+  const float* sb;            // fp8 row scales of wb
+  const int32_t* offsets;     // [E+1] expert row offsets, or null = one group of fixed_m rows
+  const int32_t* sched;       // [E+1] first tile of each expert (with offsets)
+  int fixed_m;
+  int E;
+  int kdim;                   // reduction length
+  int n;                      // weight rows per expert (gate/up: per W1/W3)
+  int nb;                     // weight blocks per expert
+  int64_t wstride;            // elements per expert of wa / wb
+  void* h;                    // gate/up output [rows, n]
+  const int32_t* perm_slot;   // down: row -> output row (null = identity)
+  const float* gate;          // down: gate per output row (null = 1)
+  void* out;                  // down output [slots, n]
+  int out_f32;                // down output is fp32 (else the activation dtype)
+};
+
+struct Tile {
+  int e, row0, mvalid, nblk;
+};
+
+// Decode this block's tile; false when the block has no work.
+__device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) {
+  int total;
+  if (a.offsets) {
+    total = a.sched[a.E];
+  } else {
+    total = ((a.fixed_m + bm - 1) / bm) * a.nb;
+  }
+  bool valid;
+  const int tile = xcd_contiguous(blockIdx.x, total, valid);
+  if (!valid) return false;
+  int e = 0, local = tile, rbeg = 0, m = a.fixed_m;
+  if (a.offsets) {
+    int lo = 0, hi = a.E - 1;  // largest e with sched[e] <= tile
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.sched[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    local = tile - a.sched[e];
+    rbeg = a.offsets[e];
+    m = a.offsets[e + 1] - rbeg;
+  }
+  const int mt = (m + bm - 1) / bm;
+  const int mb = local % mt;
+  t.e = e;
+  t.nblk = local / mt;
+  t.row0 = rbeg + mb * bm;
+  t.mvalid = min(bm, m - mb * bm);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 activations, bf16 or fp8 weights, MFMA 16x16x32.
+// ---------------------------------------------------------------------------
+template <int MODE, bool FP8>
+__global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBM * 64];
+
+  Tile tl;
+  if (!decode_tile(a, kBM, tl)) return;
+
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
+  const int ntf = (tl.mvalid + 15) >> 4;
+
+  // ---- this wave's weight rows (4 fragments of 16) ----
+  int nrow0;      // first weight row of the wave (gate/up: first intermediate column)
+  bool wvalid;
+  const uint8_t* aptr[4];
+  const size_t wbytes = FP8 ? 1 : 2;
+  if (MODE == kGateUp) {
+    nrow0 = tl.nblk * kBNGate + 32 * w;
+    wvalid = nrow0 < a.n;
+    const int rr = wvalid ? nrow0 : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint8_t* base = static_cast<const uint8_t*>(j < 2 ? a.wa : a.wb);
+      const int row = rr + 16 * (j & 1) + r16;
+      aptr[j] = base + (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 16 * g) * wbytes;
+    }
+  } else {
+    nrow0 = tl.nblk * kBNDown + 64 * w;
+    wvalid = nrow0 < a.n;
+    const int rr = wvalid ? nrow0 : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = rr + 16 * j + r16;
+      aptr[j] = static_cast<const uint8_t*>(a.wa) +
+                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 16 * g) * wbytes;
+    }
+  }
+
+  // ---- token rows this thread stages (4 chunks of 16 bytes per stage) ----
+  const uint16_t* act = static_cast<const uint16_t*>(a.act);
+  const int bch = tid & 7;
+  const uint16_t* bsrc[4];
+  int bdst[4];
+  bool bval[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    bval[i] = row < tl.mvalid;
+    bsrc[i] = act + static_cast<size_t>(tl.row0 + (bval[i] ? row : 0)) * a.kdim + bch * 8;
+    bdst[i] = row * 64 + ((bch ^ (row & 7)) * 8);
+  }
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = a.kdim / 64;
+  // A register ring: 2 stages. bf16: 2 x 16B per fragment; fp8: 1 x 16B.
+  u32x4 ra[2][4][2];
+  u32x4 rb[4];
+
+  auto load_a = [&](u32x4 (&dst)[4][2], int ks) {
+    if (!wvalid) return;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(aptr[j] + static_cast<size_t>(ks) * 64 * wbytes);
+      dst[j][0] = p[0];
+      if (!FP8) dst[j][1] = p[1];
+    }
+  };
+  auto load_b = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (bval[i]) rb[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + ks * 64);
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (bval[i]) *reinterpret_cast<u32x4*>(&bs[buf][bdst[i]]) = rb[i];
+  };
+  auto compute = [&](const u32x4 (&src)[4][2], int buf) {
+    if (!wvalid) return;
+    u32x4 op[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (FP8) {
+        fp8x16_to_bf16x16(src[j][0], op[j][0], op[j][1]);
+      } else {
+        op[j][0] = src[j][0];
+        op[j][1] = src[j][1];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t < ntf) {
+          const int tok = 16 * t + r16, ch = 2 * g + s;
+          const u32x4 b = *reinterpret_cast<const u32x4*>(&bs[buf][tok * 64 + ((ch ^ (tok & 7)) * 8)]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][t] = mfma_16x16x32(op[j][s], b, acc[j][t]);
+        }
+      }
+  };
+
+  load_a(ra[0], 0);
+  load_b(0);
+  store_b(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += 2) {
+    if (ks + 1 < nk) { load_a(ra[1], ks + 1); load_b(ks + 1); }
+    compute(ra[0], 0);
+    if (ks + 1 < nk) store_b(1);
+    __syncthreads();
+    if (ks + 1 >= nk) break;
+    if (ks + 2 < nk) { load_a(ra[0], ks + 2); load_b(ks + 2); }
+    compute(ra[1], 1);
+    if (ks + 2 < nk) store_b(0);
+    __syncthreads();
+  }
+
+  if (!wvalid) return;
+  if (MODE == kGateUp) {
+    uint16_t* h = static_cast<uint16_t*>(a.h);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = nrow0 + 16 * jj + 4 * g;
+      float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+      if (FP8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sg[q] = a.sa[static_cast<size_t>(tl.e) * a.n + col + q];
+          su[q] = a.sb[static_cast<size_t>(tl.e) * a.n + col + q];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int tok = 16 * t + r16;
+        if (t < ntf && tok < tl.mvalid) {
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) hv[q] = silu(acc[jj][t][q] * sg[q]) * (acc[jj + 2][t][q] * su[q]);
+          u32x2 v;
+          v.x = pack_bf16x2(hv[0], hv[1]);
+          v.y = pack_bf16x2(hv[2], hv[3]);
+          *reinterpret_cast<u32x2*>(h + static_cast<size_t>(tl.row0 + tok) * a.n + col) = v;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int tok = 16 * t + r16;
+      if (!(t < ntf && tok < tl.mvalid)) continue;
+      const int p = tl.row0 + tok;
+      const int slot = a.perm_slot ? a.perm_slot[p] : p;
+      if (slot < 0) continue;
+      const float gv = a.gate ? a.gate[slot] : 1.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = nrow0 + 16 * j + 4 * g;
+        float ov[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float sc = FP8 ? a.sa[static_cast<size_t>(tl.e) * a.n + col + q] : 1.f;
+          ov[q] = (acc[j][t][q] * sc) * gv;
+        }
+        const size_t o = static_cast<size_t>(slot) * a.n + col;
+        if (a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+        } else {
+          u32x2 v;
+          v.x = pack_bf16x2(ov[0], ov[1]);
+          v.y = pack_bf16x2(ov[2], ov[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 activations and weights: LDS-tiled fp32 FMA (32 tokens x 32 columns
+// per block, 4 outputs per thread, K in chunks of 32).
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs a) {
+  __shared__ float xs[kBMF32][33];
+  __shared__ float ws1[kBNF32][33];
+  __shared__ float ws3[kBNF32][33];
+  Tile tl;
+  if (!decode_tile(a, kBMF32, tl)) return;
+  const int tid = threadIdx.x;
+  const int tok = tid >> 3, c0 = (tid & 7) * 4;
+  const int n0 = tl.nblk * kBNF32;
+  const float* act = static_cast<const float*>(a.act);
+  const float* wa = static_cast<const float*>(a.wa) + static_cast<size_t>(tl.e) * a.wstride;
+  const float* wb = MODE == kGateUp ? static_cast<const float*>(a.wb) + static_cast<size_t>(tl.e) * a.wstride : nullptr;
+  float acc1[4] = {0.f, 0.f, 0.f, 0.f}, acc3[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.kdim; k0 += 32) {
+    for (int i = tid; i < 32 * 32; i += 256) {
+      const int r = i >> 5, c = i & 31;
+      xs[r][c] = r < tl.mvalid ? act[static_cast<size_t>(tl.row0 + r) * a.kdim + k0 + c] : 0.f;
+      const int wr = n0 + r;
+      ws1[r][c] = wr < a.n ? wa[static_cast<size_t>(wr) * a.kdim + k0 + c] : 0.f;
+      if (MODE == kGateUp) ws3[r][c] = wr < a.n ? wb[static_cast<size_t>(wr) * a.kdim + k0 + c] : 0.f;
+    }
+    __syncthreads();
+    for (int k = 0; k < 32; ++k) {
+      const float xv = xs[tok][k];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc1[q] = fmaf(xv, ws1[c0 + q][k], acc1[q]);
+        if (MODE == kGateUp) acc3[q] = fmaf(xv, ws3[c0 + q][k], acc3[q]);
+      }
+    }
+    __syncthreads();
+  }
+  if (tok >= tl.mvalid) return;
+  const int p = tl.row0 + tok;
+  if (MODE == kGateUp) {
+    float* h = static_cast<float*>(a.h);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = n0 + c0 + q;
+      if (col < a.n) h[static_cast<size_t>(p) * a.n + col] = silu(acc1[q]) * acc3[q];
+    }
+  } else {
+    const int slot = a.perm_slot ? a.perm_slot[p] : p;
+    if (slot < 0) return;
+    const float gv = a.gate ? a.gate[slot] : 1.f;
+    float* out = static_cast<float*>(a.out);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = n0 + c0 + q;
+      if (col < a.n) out[static_cast<size_t>(slot) * a.n + col] = acc1[q] * gv;
+    }
+  }
+}
+
+// Tile schedule of one grouped GEMM from the expert row offsets (one block):
+// sched[e] = first tile of expert e, sched[E] = total tiles.
+__global__ __launch_bounds__(256) void ffn_schedule(const int32_t* __restrict__ offsets, int E,
+                                                    int bm, int nb, int32_t* __restrict__ sched) {
+  __shared__ int sc[256];
+  const int tid = threadIdx.x;
+  int mine = 0;
+  if (tid < E) {
+    const int m = offsets[tid + 1] - offsets[tid];
+    mine = ((m + bm - 1) / bm) * nb;
+  }
+  sc[tid] = mine;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) sched[tid] = sc[tid] - mine;
+  if (tid == 0) sched[E] = sc[255];
+}
+
+int64_t grid_for(int64_t max_tiles) {
+  const int64_t per = (max_tiles + kNumXcd - 1) / kNumXcd;
+  return per * kNumXcd;
+}
+
+hipError_t run_gemm(int mode, bool f32, bool fp8, const GemmArgs& a, int64_t max_tiles,
+                    hipStream_t s) {
+  const int64_t grid = grid_for(max_tiles);
+  if (grid <= 0) return hipSuccess;
+  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+  if (f32) {
+    if (mode == kGateUp) hipLaunchKernelGGL(grouped_gemm_f32<kGateUp>, gd, bd, 0, s, a);
+    else hipLaunchKernelGGL(grouped_gemm_f32<kDown>, gd, bd, 0, s, a);
+  } else if (fp8) {
+    if (mode == kGateUp) hipLaunchKernelGGL((grouped_gemm_mfma<kGateUp, true>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((grouped_gemm_mfma<kDown, true>), gd, bd, 0, s, a);
+  } else {
+    if (mode == kGateUp) hipLaunchKernelGGL((grouped_gemm_mfma<kGateUp, false>), gd, bd, 0, s, a);
+    else hipLaunchKernelGGL((grouped_gemm_mfma<kDown, false>), gd, bd, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+struct Blocking {
+  int bm, nb1, nb2;
+};
+
+Blocking blocking(const moe_config& c, int n_inter) {
+  if (c.act_dtype == MOE_DTYPE_F32)
+    return {kBMF32, (n_inter + kBNF32 - 1) / kBNF32, (c.hidden + kBNF32 - 1) / kBNF32};
+  return {kBM, (n_inter + kBNGate - 1) / kBNGate, (c.hidden + kBNDown - 1) / kBNDown};
+}
+
+size_t elem_bytes(const moe_config& c) { return c.act_dtype == MOE_DTYPE_F32 ? 4 : 2; }
+
+}  // namespace
+
+size_t sched_ws_bytes(const moe_config& c) { return align_up(static_cast<size_t>(c.num_experts + 1) * 4, 256); }
+
+size_t h_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_tokens) * c.top_k * c.inter * elem_bytes(c), 256);
+}
+
+size_t ffn_ws_bytes(const moe_config& c) { return h_bytes(c) + sched_ws_bytes(c); }
+
+size_t shared_ws_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_tokens) * c.num_shared * c.shared_inter * elem_bytes(c), 256);
+}
+
+hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t* expert_offsets,
+                          const void* w1, const void* w3, const float* s1, const float* s3,
+                          void* h, void* ws, hipStream_t s) {
+  const int E = c.num_experts, d = c.hidden, I = c.inter;
+  const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
+  const Blocking b = blocking(c, I);
+  int32_t* sched = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, expert_offsets, E, b.bm, b.nb1,
+                     sched);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  GemmArgs g{};
+  g.act = x_perm; g.wa = w1; g.wb = w3; g.sa = s1; g.sb = s3;
+  g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
+  g.kdim = d; g.n = I; g.nb = b.nb1; g.wstride = static_cast<int64_t>(I) * d; g.h = h;
+  return run_gemm(kGateUp, f32, fp8, g, ((TK + b.bm - 1) / b.bm + E) * b.nb1, s);
+}
+
+hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
+                       const int32_t* perm_slot, const float* topk_gate, const void* w2,
+                       const float* s2, void* out_slots, void* ws, hipStream_t s) {
+  const int E = c.num_experts, d = c.hidden, I = c.inter;
+  const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
+  const Blocking b = blocking(c, I);
+  int32_t* sched = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, expert_offsets, E, b.bm, b.nb2,
+                     sched);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  GemmArgs g{};
+  g.act = h; g.wa = w2; g.sa = s2;
+  g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
+  g.kdim = I; g.n = d; g.nb = b.nb2; g.wstride = static_cast<int64_t>(d) * I;
+  g.perm_slot = perm_slot; g.gate = topk_gate; g.out = out_slots;
+  return run_gemm(kDown, f32, fp8, g, ((TK + b.bm - 1) / b.bm + E) * b.nb2, s);
+}
+
+hipError_t launch_expert_ffn(const moe_config& c, const void* x_perm,
+                             const int32_t* expert_offsets, const int32_t* perm_slot,
+                             const float* topk_gate, const void* w1, const void* w3,
+                             const void* w2, const float* s1, const float* s3, const float* s2,
+                             void* out_slots, void* ws, hipStream_t s) {
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  void* h = wsb;
+  void* sched = wsb + h_bytes(c);
+  hipError_t err = launch_gate_up(c, x_perm, expert_offsets, w1, w3, s1, s3, h, sched, s);
+  if (err != hipSuccess) return err;
+  return launch_down(c, h, expert_offsets, perm_slot, topk_gate, w2, s2, out_slots, sched, s);
+}
+
+hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s,
+                             const void* w3s, const void* w2s, const float* s1s,
+                             const float* s3s, const float* s2s, void* y_shared, void* ws,
+                             hipStream_t s) {
+  const int T = c.num_tokens, d = c.hidden, SI = c.num_shared * c.shared_inter;
+  if (T == 0) return hipSuccess;
+  const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
+  const Blocking b = blocking(c, SI);
+  const int64_t mt = (T + b.bm - 1) / b.bm;
+
+  GemmArgs g1{};
+  g1.act = x; g1.wa = w1s; g1.wb = w3s; g1.sa = s1s; g1.sb = s3s;
+  g1.offsets = nullptr; g1.sched = nullptr; g1.fixed_m = T; g1.E = 1;
+  g1.kdim = d; g1.n = SI; g1.nb = b.nb1; g1.wstride = 0; g1.h = ws;
+  hipError_t err = run_gemm(kGateUp, f32, fp8, g1, mt * b.nb1, s);
+  if (err != hipSuccess) return err;
+
+  GemmArgs g2{};
+  g2.act = ws; g2.wa = w2s; g2.sa = s2s;
+  g2.offsets = nullptr; g2.sched = nullptr; g2.fixed_m = T; g2.E = 1;
+  g2.kdim = SI; g2.n = d; g2.nb = b.nb2; g2.wstride = 0;
+  g2.perm_slot = nullptr; g2.gate = nullptr; g2.out = y_shared; g2.out_f32 = 1;
+  return run_gemm(kDown, f32, fp8, g2, mt * b.nb2, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,365 @@
+// Router of the DeepSeekMoE layer: affinity GEMM, score, bias-adjusted top-K,
+// gate normalisation and per-expert load counts.
+//
+// Method: "DeepSeekMoE架构解析" section 2.1 (eq. 15: s = sigmoid(u^T e_i);
+// eq. 14: keep the K largest; eq. 13: divide by the sum of the kept scores)
+// and section 2.2 (eq. 16: the balance bias b_i is added to the score only
+// for the choice of experts, never to the gate value). The 2024 layout
+// (course notes "省钱第一招", sections 三-四) uses a softmax over all routed
+// experts and keeps the selected scores unnormalised.
+//
+// Top-K on CDNA4: one wave per token. Lane l holds the keys of experts
+// l, l+64, l+128, l+192 (E <= 256) in registers; each of the K rounds takes a
+// lane-local best, then a 6-step xor butterfly over (key, index) pairs with
+// the total order "larger key first, then lower index", so every lane ends
+// with the same winner and the result is deterministic.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kFusedTokens = 32;     // tokens per block of the fused router
+constexpr int kFusedMinTokens = 4096;
+
+__device__ __forceinline__ bool key_better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ __forceinline__ float pick4(const float (&v)[4], int j) {
+  return j == 0 ? v[0] : (j == 1 ? v[1] : (j == 2 ? v[2] : v[3]));
+}
+
+// Scores, top-K, gates for one token on one wave. lg[j] is the logit of
+// expert (lane + 64 j); entries with expert >= E are ignored.
+__device__ void topk_token(const float (&lg)[4], int t, int E, int K, int score_fn, int norm,
+                           const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
+                           float* __restrict__ topk_gate, int* hist) {
+  const int l = lane_id();
+  float s[4], key[4];
+  if (score_fn == MOE_SCORE_SIGMOID) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = sigmoid(lg[j]);
+  } else {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (l + 64 * j < E) m = fmaxf(m, lg[j]);
+    m = wave_max(m);
+    float ex[4], part = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ex[j] = (l + 64 * j < E) ? expf(lg[j] - m) : 0.f;
+      part += ex[j];
+    }
+    const float sum = wave_sum(part);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = ex[j] / sum;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = l + 64 * j;
+    key[j] = e < E ? (bias ? s[j] + bias[e] : s[j]) : -INFINITY;
+  }
+
+  int rec_idx[4] = {0, 0, 0, 0};
+  float rec_s[4] = {0.f, 0.f, 0.f, 0.f};
+  float ssum = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float bk = key[0];
+    int bi = l;
+#pragma unroll
+    for (int j = 1; j < 4; ++j)
+      if (key_better(key[j], l + 64 * j, bk, bi)) { bk = key[j]; bi = l + 64 * j; }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (key_better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+    }
+    const int owner = bi & 63, slot = bi >> 6;
+    const float sv = __shfl(pick4(s, slot), owner, kWave);
+    if (l == owner) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == slot) key[j] = -INFINITY;
+    }
+    ssum += sv;
+    if (l == (k & 63)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == (k >> 6)) { rec_idx[j] = bi; rec_s[j] = sv; }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int k = l + 64 * j;
+    if (k < K) {
+      const size_t o = static_cast<size_t>(t) * K + k;
+      topk_idx[o] = rec_idx[j];
+      topk_gate[o] = norm == MOE_NORM_SELECTED ? rec_s[j] / ssum : rec_s[j];
+      atomicAdd(&hist[rec_idx[j]], 1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused path (bf16, many tokens): one block = 32 tokens x all E experts.
+// Token rows are staged in LDS (double buffered, 16-byte chunks XOR-swizzled
+// by row); each wave streams its own router rows straight from global memory
+// into MFMA operands, so LDS only carries the operand all waves share.
+// Within a 64-wide K stage, lane group g consumes K-elements 16g .. 16g+15
+// (two MFMA steps of 8); both operands use the same assignment.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_fused_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int T, int d, int E, int K, int score_fn, int norm,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ load) {
+  constexpr int BT = kFusedTokens;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT * 64];
+  __shared__ float lgs[BT][257];
+  __shared__ int hist[256];
+
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
+  const int t0 = blockIdx.x * BT;
+  const int nEF = (E + 15) >> 4;
+  hist[tid] = 0;
+
+  // router rows of this lane for its (up to) 4 expert fragments
+  const uint16_t* arow[4];
+  bool fvalid[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = w + 4 * i;
+    fvalid[i] = f < nEF;
+    int row = 16 * f + r16;
+    row = row < E ? row : E - 1;
+    arow[i] = wr + static_cast<size_t>(row) * d + 16 * g;
+  }
+  // token chunk this thread stages
+  const int brow = tid >> 3, bch = tid & 7;
+  const int btok = t0 + brow;
+  const uint16_t* bsrc = x + static_cast<size_t>(btok < T ? btok : T - 1) * d + bch * 8;
+  const int bdst = brow * 64 + ((bch ^ (brow & 7)) * 8);
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = d / 64;
+  u32x4 a0[4][2], a1[4][2], bst;
+
+  auto load_a = [&](u32x4 (&a)[4][2], int ks) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (fvalid[i]) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(arow[i] + ks * 64);
+        a[i][0] = p[0];
+        a[i][1] = p[1];
+      }
+  };
+  auto load_b = [&](int ks) { bst = *reinterpret_cast<const u32x4*>(bsrc + ks * 64); };
+  auto store_b = [&](int buf) { *reinterpret_cast<u32x4*>(&xs[buf][bdst]) = bst; };
+  auto compute = [&](const u32x4 (&a)[4][2], int buf) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int tf = 0; tf < 2; ++tf) {
+        const int tok = 16 * tf + r16, ch = 2 * g + s;
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&xs[buf][tok * 64 + ((ch ^ (tok & 7)) * 8)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (fvalid[i]) acc[i][tf] = mfma_16x16x32(a[i][s], b, acc[i][tf]);
+      }
+  };
+
+  load_a(a0, 0);
+  load_b(0);
+  store_b(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ks += 2) {
+    if (ks + 1 < nk) { load_a(a1, ks + 1); load_b(ks + 1); }
+    compute(a0, 0);
+    if (ks + 1 < nk) store_b(1);
+    __syncthreads();
+    if (ks + 1 >= nk) break;
+    if (ks + 2 < nk) { load_a(a0, ks + 2); load_b(ks + 2); }
+    compute(a1, 1);
+    if (ks + 2 < nk) store_b(0);
+    __syncthreads();
+  }
+
+  // logits -> LDS [token][expert]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!fvalid[i]) continue;
+    const int f = w + 4 * i;
+#pragma unroll
+    for (int tf = 0; tf < 2; ++tf)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lgs[16 * tf + r16][16 * f + 4 * g + q] = acc[i][tf][q];
+  }
+  __syncthreads();
+
+  for (int tt = w; tt < BT; tt += 4) {
+    const int t = t0 + tt;
+    if (t >= T) break;
+    float lg[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = l + 64 * j;
+      lg[j] = e < E ? lgs[tt][e] : 0.f;
+    }
+    topk_token(lg, t, E, K, score_fn, norm, bias, topk_idx, topk_gate, hist);
+  }
+  __syncthreads();
+  if (tid < E && hist[tid] > 0) atomicAdd(&load[tid], hist[tid]);
+}
+
+// ---------------------------------------------------------------------------
+// Split path, step 1 (bf16): partial logits over a slice of the hidden axis.
+// Block = 16 tokens x 64 experts (one 16-expert fragment per wave); grid.z
+// splits the 64-wide K stages evenly. Writes part[z][t][e] in fp32.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void route_logits_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    int stages_per_split, float* __restrict__ part) {
+  const int l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
+  const int ef = blockIdx.y * 4 + w;
+  if (16 * ef >= E) return;
+  const int nk = d / 64;
+  const int ks0 = blockIdx.z * stages_per_split;
+  const int ks1 = min(nk, ks0 + stages_per_split);
+  int er = 16 * ef + r16;
+  er = er < E ? er : E - 1;
+  int tr = blockIdx.x * 16 + r16;
+  tr = tr < T ? tr : T - 1;
+  const uint16_t* pa = wr + static_cast<size_t>(er) * d + 16 * g;
+  const uint16_t* pb = x + static_cast<size_t>(tr) * d + 16 * g;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const u32x4* qa = reinterpret_cast<const u32x4*>(pa + ks * 64);
+    const u32x4* qb = reinterpret_cast<const u32x4*>(pb + ks * 64);
+    const u32x4 a0 = qa[0], a1 = qa[1], b0 = qb[0], b1 = qb[1];
+    acc = mfma_16x16x32(a0, b0, acc);
+    acc = mfma_16x16x32(a1, b1, acc);
+  }
+  const int t = blockIdx.x * 16 + r16;
+  if (t < T) {
+    float* dst = part + (static_cast<size_t>(blockIdx.z) * T + t) * E;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 16 * ef + 4 * g + q;
+      if (e < E) dst[e] = acc[q];
+    }
+  }
+}
+
+// Split path, step 1 (fp32): one thread per (token, expert), sequential fp32
+// dot product over the hidden axis.
+__global__ __launch_bounds__(256) void route_logits_f32(const float* __restrict__ x,
+                                                        const float* __restrict__ wr, int T,
+                                                        int d, int E, float* __restrict__ part) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(T) * E) return;
+  const int t = static_cast<int>(i / E), e = static_cast<int>(i % E);
+  const float* a = x + static_cast<size_t>(t) * d;
+  const float* b = wr + static_cast<size_t>(e) * d;
+  float acc = 0.f;
+  for (int j = 0; j < d; ++j) acc = fmaf(a[j], b[j], acc);
+  part[i] = acc;
+}
+
+// Split path, step 2: sum the K-splits in order, then score + top-K + gates
+// (one wave per token) and the block's load histogram.
+__global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int splits,
+                                                  const float* __restrict__ bias, int T, int E,
+                                                  int K, int score_fn, int norm,
+                                                  int32_t* __restrict__ topk_idx,
+                                                  float* __restrict__ topk_gate,
+                                                  int32_t* __restrict__ load) {
+  __shared__ int hist[256];
+  const int tid = threadIdx.x, l = lane_id();
+  hist[tid] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * 4 + wave_id();
+  if (t < T) {
+    float lg[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = l + 64 * j;
+      float v = 0.f;
+      if (e < E)
+        for (int z = 0; z < splits; ++z) v += part[(static_cast<size_t>(z) * T + t) * E + e];
+      lg[j] = v;
+    }
+    topk_token(lg, t, E, K, score_fn, norm, bias, topk_idx, topk_gate, hist);
+  }
+  __syncthreads();
+  if (tid < E && hist[tid] > 0) atomicAdd(&load[tid], hist[tid]);
+}
+
+}  // namespace
+
+bool route_uses_fused(const moe_config& c) {
+  return c.act_dtype == MOE_DTYPE_BF16 && c.num_tokens >= kFusedMinTokens;
+}
+
+int route_k_splits(const moe_config& c) {
+  if (route_uses_fused(c) || c.act_dtype == MOE_DTYPE_F32 || c.num_tokens == 0) return 1;
+  const int nk = c.hidden / 64;
+  const int64_t base = static_cast<int64_t>((c.num_tokens + 15) / 16) * ((c.num_experts + 63) / 64);
+  int64_t want = (512 + base - 1) / base;
+  if (want < 1) want = 1;
+  if (want > nk) want = nk;
+  // even split of the stages
+  const int sps = static_cast<int>((nk + want - 1) / want);
+  return (nk + sps - 1) / sps;
+}
+
+size_t route_ws_bytes(const moe_config& c) {
+  if (route_uses_fused(c)) return 0;
+  return align_up(static_cast<size_t>(route_k_splits(c)) * c.num_tokens * c.num_experts * 4, 256);
+}
+
+hipError_t launch_route(const moe_config& c, const void* x, const void* wr, const float* bias,
+                        int32_t* topk_idx, float* topk_gate, int32_t* load, void* ws,
+                        hipStream_t s) {
+  hipError_t err = launch_fill_i32(load, 0, c.num_experts, s);
+  if (err != hipSuccess || c.num_tokens == 0) return err;
+  const int T = c.num_tokens, d = c.hidden, E = c.num_experts, K = c.top_k;
+  if (route_uses_fused(c)) {
+    hipLaunchKernelGGL(route_fused_bf16, dim3((T + kFusedTokens - 1) / kFusedTokens), dim3(256),
+                       0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
+                       bias, T, d, E, K, c.score_fn, c.norm, topk_idx, topk_gate, load);
+    return hipGetLastError();
+  }
+  float* part = static_cast<float*>(ws);
+  int splits = 1;
+  if (c.act_dtype == MOE_DTYPE_BF16) {
+    splits = route_k_splits(c);
+    const int nk = d / 64;
+    const int sps = (nk + splits - 1) / splits;
+    hipLaunchKernelGGL(route_logits_bf16, dim3((T + 15) / 16, (E + 63) / 64, splits), dim3(256),
+                       0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
+                       T, d, E, sps, part);
+  } else {
+    const int64_t n = static_cast<int64_t>(T) * E;
+    hipLaunchKernelGGL(route_logits_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                       0, s, static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E,
+                       part);
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, splits, bias, T, E, K,
+                     c.score_fn, c.norm, topk_idx, topk_gate, load);
+  return hipGetLastError();
+}
+
+}  // namespace moe

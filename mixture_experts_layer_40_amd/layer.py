@@ -1,0 +1,115 @@
+"""One DeepSeekMoE layer call through the C ABI, with its buffers held in HBM.
+
+MoELayer keeps the weights the caller hands it (torch tensors on the GPU, in
+their stored formats) and allocates every intermediate buffer once, sized
+for `max_tokens`. forward() enqueues
+
+    moe_shared_ffn (second stream)  ||  moe_route -> moe_permute -> moe_expert_ffn
+    -> join -> moe_combine
+
+on the current stream and returns y (plus the routing results it kept). The
+per-batch bias step is `bias_update()`. Nothing here computes: every step is
+a libmoe kernel.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+class MoELayer:
+    def __init__(self, spec, weights: dict, max_tokens: Optional[int] = None,
+                 shared_stream: bool = True, device=None):
+        self.spec = spec
+        self.w = weights
+        self.device = torch.device(device) if device is not None else weights["wr"].device
+        self.max_tokens = spec.T if max_tokens is None else max_tokens
+        self.act = _TORCH_DT[spec.act_dtype]
+        self.cfg_max = L.config_of(spec, T=self.max_tokens)
+        st = L.moe_validate(self.cfg_max)
+        if st != L.MOE_OK:
+            raise L.MoEError("MoELayer", st, L.moe_status_string(st))
+        T, K, d, E = self.max_tokens, spec.K, spec.d, spec.E
+        dev = self.device
+        self.topk_idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.topk_gate = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.load = torch.empty((E,), dtype=torch.int32, device=dev)
+        self.expert_offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        self.perm_slot = torch.empty((T * K,), dtype=torch.int32, device=dev)
+        self.x_perm = torch.empty((T * K, d), dtype=self.act, device=dev)
+        self.out_slots = torch.empty((T * K, d), dtype=self.act, device=dev)
+        self.y_shared = torch.empty((T, d), dtype=torch.float32, device=dev) if spec.S > 0 else None
+        self.y = torch.empty((T, d), dtype=_TORCH_DT[getattr(spec, "out_dtype", "f32")], device=dev)
+
+        def ws(which):
+            n = L.moe_workspace_size(self.cfg_max, which)
+            return torch.empty(max(n, 256), dtype=torch.uint8, device=dev)
+        self.ws_route = ws(L.MOE_WS_ROUTE)
+        self.ws_perm = ws(L.MOE_WS_PERMUTE)
+        self.ws_ffn = ws(L.MOE_WS_FFN)
+        self.ws_shared = ws(L.MOE_WS_SHARED)
+        self.side = torch.cuda.Stream(device=dev) if (shared_stream and spec.S > 0) else None
+
+    def _cfg(self, T):
+        if T > self.max_tokens:
+            raise ValueError(f"{T} tokens exceed the layer's buffers ({self.max_tokens})")
+        return L.config_of(self.spec, T=T)
+
+    def route(self, x, bias=None):
+        T = x.shape[0]
+        cfg = self._cfg(T)
+        L.moe_route(cfg, x, self.w["wr"], bias, self.topk_idx[:T], self.topk_gate[:T], self.load,
+                    ws=self.ws_route)
+        return cfg
+
+    def permute(self, cfg, x):
+        T = cfg.num_tokens
+        L.moe_permute(cfg, self.topk_idx[:T], x, self.expert_offsets,
+                      self.perm_slot[:T * cfg.top_k], self.x_perm[:T * cfg.top_k], ws=self.ws_perm)
+
+    def experts(self, cfg):
+        T, w = cfg.num_tokens, self.w
+        L.moe_expert_ffn(cfg, self.x_perm[:T * cfg.top_k], self.expert_offsets,
+                         self.perm_slot[:T * cfg.top_k], self.topk_gate[:T], w["w1"], w["w3"],
+                         w["w2"], w.get("s1"), w.get("s3"), w.get("s2"),
+                         self.out_slots[:T * cfg.top_k], ws=self.ws_ffn)
+
+    def shared(self, cfg, x, stream=None):
+        T, w = cfg.num_tokens, self.w
+        L.moe_shared_ffn(cfg, x, w["w1s"], w["w3s"], w["w2s"], w.get("s1s"), w.get("s3s"),
+                         w.get("s2s"), self.y_shared[:T], ws=self.ws_shared, stream=stream)
+
+    def combine(self, cfg):
+        T = cfg.num_tokens
+        L.moe_combine(cfg, self.out_slots[:T * cfg.top_k],
+                      None if self.y_shared is None else self.y_shared[:T], self.y[:T])
+
+    def forward(self, x, bias=None):
+        """Enqueue one layer call on the current stream; returns y [T, d]."""
+        cfg = self._cfg(x.shape[0])
+        if cfg.num_tokens == 0:
+            L.moe_route(cfg, x, self.w["wr"], bias, None, None, self.load, ws=self.ws_route)
+            return self.y[:0]
+        cur = torch.cuda.current_stream(self.device)
+        if self.side is not None:
+            self.side.wait_stream(cur)
+            with torch.cuda.stream(self.side):
+                self.shared(cfg, x, stream=self.side)
+        elif self.y_shared is not None:
+            self.shared(cfg, x)
+        self.route(x, bias)
+        self.permute(cfg, x)
+        self.experts(cfg)
+        if self.side is not None:
+            cur.wait_stream(self.side)
+        self.combine(cfg)
+        return self.y[:cfg.num_tokens]
+
+    def bias_update(self, bias, gamma=None):
+        L.moe_bias_update(self.spec.E, self.load, self.spec.gamma if gamma is None else gamma, bias)

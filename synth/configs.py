@@ -35,6 +35,7 @@ class MoEConfig:
     norm: str = NORM_SELECTED
     act_dtype: str = "bf16"      # "f32" | "bf16"
     weight_dtype: str = "bf16"   # "f32" | "bf16" | "fp8"
+    out_dtype: str = "f32"       # layer output y: "f32" | "bf16"
     bias_range: Optional[float] = None   # None -> no bias tensor
     x_std: float = 1.0
     w_std: float = 0.02
@@ -118,8 +119,8 @@ def get_config(name: str) -> MoEConfig:
     return CONFIGS[name]
 
 
-def scaled_config(name: str, **overrides) -> MoEConfig:
+def scaled_config(base_name: str, **overrides) -> MoEConfig:
     """A named workload with some fields replaced (reduced sizes for tests)."""
-    base = CONFIGS[name]
+    base = CONFIGS[base_name]
     new_name = overrides.pop("name", base.name + "_scaled")
     return dataclasses.replace(base, name=new_name, **overrides)

@@ -1,0 +1,159 @@
+"""Shared helpers of the GPU parity tests: run the HIP path step by step on
+seeded inputs and compare every result with the fp64 oracle.
+
+The bar (the tolerances of the layer's specification):
+  * expert indices and load counts bit-exact, except tokens whose K-th and
+    (K+1)-th biased keys differ by less than 1e-5 in the oracle (near-ties):
+    those are counted and their GPU set must be valid within 1e-5;
+  * permutation and offsets bit-exact (they are defined by the indices);
+  * outputs: max |GPU - oracle| <= 2e-2 * RMS(oracle) for bf16/fp8 paths and
+    <= 1e-4 * RMS(oracle) for the fp32 path; near-tie tokens are compared
+    with the oracle evaluated on the GPU's selected set.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import mixture_experts_layer_40_amd as moe
+import oracle
+import synth
+
+OUT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+GATE_ATOL = 2e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return synth.to_numpy_stored(t)
+
+
+def f64(t):
+    return oracle.decode_stored(host(t))
+
+
+def bank_of(inp, spec):
+    def fetch(e):
+        sc = lambda n: None if inp.get(n) is None else inp[n][e].cpu().numpy()
+        return (host(inp["w1"][e]), host(inp["w3"][e]), host(inp["w2"][e]), sc("s1"), sc("s3"), sc("s2"))
+    shared = None
+    if spec.S > 0:
+        sc = lambda n: None if inp.get(n) is None else inp[n].cpu().numpy()
+        shared = (host(inp["w1s"]), host(inp["w3s"]), host(inp["w2s"]), sc("s1s"), sc("s3s"), sc("s2s"))
+    return oracle.ExpertBank(fetch=fetch, shared=shared, S=spec.S)
+
+
+def run_steps(spec, inp, bias=None, x=None, layer=None, side_stream=False):
+    """One layer call through the C ABI, step by step; returns host copies."""
+    x = inp["x"] if x is None else x
+    if layer is None:
+        layer = moe.MoELayer(spec, inp, max_tokens=x.shape[0], shared_stream=side_stream)
+    y = layer.forward(x, bias)
+    torch.cuda.synchronize()
+    T, K = x.shape[0], spec.K
+    return layer, {
+        "idx": layer.topk_idx[:T].cpu().numpy().astype(np.int64),
+        "gate": layer.topk_gate[:T].cpu().numpy().astype(np.float64),
+        "load": layer.load.cpu().numpy().astype(np.int64),
+        "offsets": layer.expert_offsets.cpu().numpy().astype(np.int64),
+        "perm": layer.perm_slot[:T * K].cpu().numpy().astype(np.int64),
+        "y": y,
+    }
+
+
+def oracle_route(spec, x, wr, bias, rows=None):
+    x64 = f64(x) if rows is None else f64(x[rows])
+    b64 = None if bias is None else bias.detach().cpu().numpy().astype(np.float64)
+    return oracle.route(x64, f64(wr), b64, spec.K, spec.score, spec.norm), x64
+
+
+def check_route(spec, r, idx, gate, load=None, rows=None):
+    """Routing parity on the tokens `rows` (all when None). Returns the number
+    of near-tie tokens."""
+    K, E = spec.K, spec.E
+    idx_r = idx if rows is None else idx[rows]
+    gate_r = gate if rows is None else gate[rows]
+    assert idx_r.min() >= 0 and idx_r.max() < E
+    srt = np.sort(idx_r, axis=1)
+    assert np.all(np.diff(srt, axis=1) > 0), "a token selected an expert twice"
+    if load is not None:
+        assert np.array_equal(load, np.bincount(idx.ravel(), minlength=E)), "load != histogram of indices"
+        assert int(load.sum()) == idx.shape[0] * K, "a token was dropped"
+    near = r["near_tie"]
+    ok = ~near
+    mism = np.flatnonzero(np.any(srt[ok] != np.sort(r["sel"][ok], axis=1), axis=1))
+    assert mism.size == 0, f"{mism.size} non-near-tie tokens differ, e.g. {np.flatnonzero(ok)[mism[:5]]}"
+    assert np.array_equal(np.bincount(idx_r[ok].ravel(), minlength=E),
+                          np.bincount(r["sel"][ok].ravel(), minlength=E))
+    keys = r["keys"]
+    kth = np.take_along_axis(keys, r["sel"][:, K - 1:K], axis=1)[:, 0]
+    chosen = np.take_along_axis(keys, idx_r, axis=1)
+    if near.any():
+        assert np.all(chosen[near] >= kth[near, None] - oracle.NEAR_TIE_GAP), "invalid near-tie selection"
+    g_or = oracle.gate_values(r["scores"], idx_r, spec.norm)
+    err = np.abs(gate_r - g_or).max()
+    assert err <= GATE_ATOL, f"gate error {err}"
+    return int(near.sum())
+
+
+def check_permutation(spec, idx, offsets, perm):
+    off_or, perm_or = oracle.permutation(idx, spec.E)
+    assert np.array_equal(offsets, off_or), "expert offsets differ"
+    assert np.array_equal(perm, perm_or), "permutation differs"
+
+
+def rel_err(got, want):
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    return float(np.abs(got - want).max()) / max(rms, 1e-300), rms
+
+
+def check_outputs(spec, layer, inp, res, r, x=None, rows=None):
+    """Layer output (and its shared and routed parts) on `rows` against the
+    oracle. `r` is the oracle routing of all tokens of the batch. The oracle
+    uses its own selected set, except on near-tie tokens, where any set
+    within 1e-5 is correct: there it evaluates the (validated) GPU set."""
+    x = inp["x"] if x is None else x
+    T, K, d = x.shape[0], spec.K, spec.d
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    trow = torch.as_tensor(rows, device=x.device)
+    x64 = f64(x[trow])
+    gpu_idx = res["idx"][rows]
+    sel = r["sel"][rows].copy()
+    near = r["near_tie"][rows]
+    sel[near] = gpu_idx[near]
+    g_or = oracle.gate_values(r["scores"][rows], sel, spec.norm)
+    y_or, ysh_or, routed_or = oracle.layer_rows(x64, sel, g_or, bank_of(inp, spec))
+    tol = OUT_TOL[spec.act_dtype]
+    y = oracle.decode_stored(host(res["y"][trow].contiguous()))
+    e_y, rms = rel_err(y, y_or)
+    assert e_y <= tol, f"y: max err / RMS = {e_y:.3e} > {tol}"
+    if spec.S > 0:
+        ysh = oracle.decode_stored(host(layer.y_shared[trow].contiguous()))
+        e_s, _ = rel_err(ysh, ysh_or)
+        assert e_s <= tol, f"y_shared: {e_s:.3e}"
+    # routed slot rows: GPU slot (t, k) holds expert gpu_idx[t, k]; line the
+    # oracle's terms up by expert id (the sets are equal, checked above)
+    aligned = np.empty_like(routed_or)
+    og, oo = np.argsort(gpu_idx, axis=1), np.argsort(sel, axis=1)
+    for i in range(len(rows)):
+        aligned[i, og[i]] = routed_or[i, oo[i]]
+    slot_rows = (trow[:, None] * K + torch.arange(K, device=x.device)[None, :]).reshape(-1)
+    osl = oracle.decode_stored(host(layer.out_slots[slot_rows].contiguous())).reshape(len(rows), K, d)
+    # out_slots is an intermediate held in the activation dtype: each element
+    # also carries its own storage rounding (at most 2^-9 relative in bf16,
+    # 2^-24 in fp32) on top of the arithmetic budget of the output tolerance.
+    # Each (token, slot) row is one gate-scaled expert output, so its error
+    # is measured against that row's own RMS.
+    store = 2.0 ** -9 if spec.act_dtype == "bf16" else 2.0 ** -24
+    rms_row = np.sqrt(np.mean(aligned ** 2, axis=2, keepdims=True))
+    excess = np.abs(osl - aligned) - store * np.abs(aligned)
+    e_o = float((excess / np.maximum(rms_row, 1e-300)).max())
+    assert e_o <= tol, f"out_slots: {e_o:.3e}"
+    return {"y_err": e_y, "y_rms": rms}
