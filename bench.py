@@ -1,0 +1,257 @@
+"""Throughput of the DeepSeekMoE layer forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-decode]
+
+One step = one whole layer call on one batch already resident in HBM:
+router GEMM + sigmoid + biased top-K + gates + loads, stable permutation and
+row gather, grouped gate/up and down SwiGLU GEMMs over the routed experts,
+the shared expert (on a second stream) and the combine. The workload is the
+V3-shape prefill layer: T = 8192 tokens, d = 7168, 256 routed experts of
+intermediate 2048 (top-8, score + bias selection) plus 1 shared expert,
+bf16, synthetic seeded inputs.
+
+Printed: one JSON line with tokens/s, the roofline of the dominant kernel
+(the grouped gate/up GEMM, timed live with HIP events on its stream), the
+decode workload's fraction of HBM peak, and the fp64 oracle timed on a
+bounded sample on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mixture_experts_layer_40_amd as moe  # noqa: E402
+import synth  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
+WORKLOAD = "v3_prefill_bf16"
+DECODE = "v3_decode_fp8"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
+                  for f in ("ffn.hip", "common.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
+    if they were taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timed:
+    """HIP events around one library call on the current stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def __enter__(self):
+        self.s = torch.cuda.Event(enable_timing=True)
+        self.e = torch.cuda.Event(enable_timing=True)
+        self.s.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.e.record()
+        self.pairs.append((self.s, self.e))
+
+    def mean_ms(self):
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+
+def layer_step(layer, x, bias, h, ws_gemm, gate_timer=None):
+    """One full layer call; the routed expert FFN is issued as its two grouped
+    GEMM entry points so the gate/up GEMM can be bracketed by events."""
+    cfg = layer._cfg(x.shape[0])
+    cur = torch.cuda.current_stream()
+    layer.side.wait_stream(cur)
+    with torch.cuda.stream(layer.side):
+        layer.shared(cfg, x, stream=layer.side)
+    layer.route(x, bias)
+    layer.permute(cfg, x)
+    T, K, w = cfg.num_tokens, cfg.top_k, layer.w
+    TK = T * K
+    if gate_timer is not None:
+        with gate_timer:
+            moe.moe_expert_gate_up(cfg, layer.x_perm[:TK], layer.expert_offsets, w["w1"], w["w3"],
+                                   w.get("s1"), w.get("s3"), h, ws=ws_gemm)
+    else:
+        moe.moe_expert_gate_up(cfg, layer.x_perm[:TK], layer.expert_offsets, w["w1"], w["w3"],
+                               w.get("s1"), w.get("s3"), h, ws=ws_gemm)
+    moe.moe_expert_down(cfg, h, layer.expert_offsets, layer.perm_slot[:TK], layer.topk_gate[:T],
+                        w["w2"], w.get("s2"), layer.out_slots[:TK], ws=ws_gemm)
+    cur.wait_stream(layer.side)
+    layer.combine(cfg)
+
+
+def setup(spec):
+    inp = synth.make_inputs(spec, "cuda")
+    layer = moe.MoELayer(spec, inp, max_tokens=spec.T, shared_stream=True)
+    cfg = moe.config_of(spec)
+    h = torch.empty((spec.T * spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
+    ws_gemm = torch.empty(max(moe.moe_workspace_size(cfg, moe.MOE_WS_GEMM), 256), dtype=torch.uint8,
+                          device="cuda")
+    return inp, layer, h, ws_gemm
+
+
+def time_steps(layer, x, bias, h, ws_gemm, steps, warmup, gate_timer=None):
+    for _ in range(warmup):
+        layer_step(layer, x, bias, h, ws_gemm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer_step(layer, x, bias, h, ws_gemm, gate_timer)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def cpu_baseline(spec, inp, layer, n_tokens):
+    """The fp64 oracle on a bounded sample: route n_tokens tokens and compute
+    their layer outputs, decoding each touched expert's stored weights."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(spec.T, n_tokens, replace=False))
+    trow = torch.as_tensor(rows, device="cuda")
+    host = synth.to_numpy_stored
+    x = host(inp["x"][trow])
+    wr = host(inp["wr"])
+    bias = inp["bias"].cpu().numpy()
+    sc = lambda n, e: None if inp.get(n) is None else inp[n][e].cpu().numpy()
+    shared = (host(inp["w1s"]), host(inp["w3s"]), host(inp["w2s"]),
+              None if inp.get("s1s") is None else inp["s1s"].cpu().numpy(),
+              None if inp.get("s3s") is None else inp["s3s"].cpu().numpy(),
+              None if inp.get("s2s") is None else inp["s2s"].cpu().numpy())
+    bank = oracle.ExpertBank(
+        fetch=lambda e: (host(inp["w1"][e]), host(inp["w3"][e]), host(inp["w2"][e]),
+                         sc("s1", e), sc("s3", e), sc("s2", e)),
+        shared=shared, S=spec.S)
+    t0 = time.perf_counter()
+    x64 = oracle.decode_stored(x)
+    r = oracle.route(x64, oracle.decode_stored(wr), bias.astype(np.float64), spec.K, spec.score,
+                     spec.norm)
+    oracle.layer_rows(x64, r["sel"], r["gate"], bank)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tokens} tokens of the {spec.name} batch (routing + shared + "
+                      f"{len(np.unique(r['sel']))} routed experts decoded to fp64), {dt:.1f} s"}
+
+
+def decode_measure(steps, warmup):
+    spec = synth.get_config(DECODE)
+    inp, layer, h, ws_gemm = setup(spec)
+    x, bias = inp["x"], inp["bias"]
+    sec = time_steps(layer, x, bias, h, ws_gemm, steps, warmup)
+    load = layer.load.cpu().numpy()
+    n_active = int((load > 0).sum())
+    bytes_ = ((n_active * spec.weight_bytes_per_expert() + spec.shared_weight_bytes())
+              + spec.E * spec.d * 2 + spec.E * 4                      # router rows, bias
+              + spec.T * spec.d * 2 + spec.T * spec.d * 4)            # x in, y out (fp32)
+    gbs = bytes_ / sec / 1e9
+    out = {"workload": DECODE, "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
+           "active_experts": n_active, "algorithmic_bytes": int(bytes_), "achieved_GBs": gbs,
+           "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}
+    del inp, layer, h, ws_gemm
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this layer's path is built and timed on a single "
+              "MI355X (no expert sharding or collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    moe.load_library()
+
+    spec = synth.get_config(WORKLOAD)
+    log(f"[bench] generating {WORKLOAD} inputs on the GPU")
+    inp, layer, h, ws_gemm = setup(spec)
+    x, bias = inp["x"], inp["bias"]
+    gate_timer = Timed()
+    log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
+    sec = time_steps(layer, x, bias, h, ws_gemm, args.steps, args.warmup, gate_timer)
+    tokens_per_s = spec.T / sec
+    gate_ms = gate_timer.mean_ms()
+    gate_flops = 4.0 * spec.d * spec.I * spec.T * spec.K
+    achieved = gate_flops / (gate_ms * 1e-3) / 1e12
+    layer_tflops = spec.flops() / sec / 1e12
+    load = layer.load.cpu().numpy()
+    log(f"[bench] {sec*1e3:.3f} ms/step, {tokens_per_s:.0f} tok/s, gate/up {gate_ms:.3f} ms "
+        f"({achieved:.0f} TFLOP/s)")
+
+    result = {
+        "metric": "MoE-layer tokens/s at V3 shape (T=8192) + % MFMA peak; decode % HBM peak",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": WORKLOAD, "tokens": spec.T, "hidden": spec.d, "routed_experts": spec.E,
+                   "top_k": spec.K, "inter": spec.I, "shared_experts": spec.S,
+                   "shared_inter": spec.Is, "weights": "bf16", "output": "fp32",
+                   "parallelism": "single GPU"},
+        "layer_TFLOPs": layer_tflops,
+        "layer_frac_mfma_peak": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
+        "load_max_over_mean": float(load.max() / load.mean()),
+        "roofline": {"kernel": "grouped_gemm_mfma<gate_up,bf16>", "bound": "mfma",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(),
+                     "algorithmic_flops_per_launch": gate_flops, "avg_launch_ms": gate_ms},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
+        result["cpu_baseline"] = cpu_baseline(spec, inp, layer, args.cpu_tokens)
+    del inp, layer, h, ws_gemm
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        log(f"[bench] decode workload {DECODE}")
+        result["decode"] = decode_measure(args.steps, args.warmup)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,101 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (MoELayer.forward through the C ABI).
+
+Routing (indices, gates, loads) and the permutation are compared on every
+token; the gathered rows on the device; the layer output on sampled tokens
+the oracle computes one by one (token outputs are independent), always
+including near-tie tokens when there are any.
+"""
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_parity import check_outputs, check_permutation, check_route, oracle_route, run_steps, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _sample_rows(T, n, near, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, min(n, T), replace=False).tolist())
+    rows.update(np.flatnonzero(near)[:4].tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,n_rows", [("dsmoe2024_bf16", 96), ("v3_prefill_bf16", 12),
+                                         ("v3_decode_fp8", 16)])
+def test_fullsize_layer(name, n_rows):
+    spec = synth.get_config(name)
+    say(f"[full] {name}: generating inputs")
+    inp = synth.make_inputs(spec, "cuda")
+    layer, res = run_steps(spec, inp, bias=inp["bias"], side_stream=True)
+    say(f"[full] {name}: oracle routing of {spec.T} tokens")
+    r, _ = oracle_route(spec, inp["x"], inp["wr"], inp["bias"])
+    n_near = check_route(spec, r, res["idx"], res["gate"], res["load"])
+    check_permutation(spec, res["idx"], res["offsets"], res["perm"])
+    perm = torch.as_tensor(res["perm"], device="cuda")
+    assert torch.equal(layer.x_perm[:spec.T * spec.K], inp["x"][perm // spec.K])
+    rows = _sample_rows(spec.T, n_rows, r["near_tie"])
+    say(f"[full] {name}: near-ties={n_near}, oracle outputs for {len(rows)} tokens")
+    out = check_outputs(spec, layer, inp, res, r, rows=rows)
+    load = res["load"]
+    say(f"[full] {name}: y err/rms={out['y_err']:.3e} active experts={int((load > 0).sum())} "
+        f"load max/mean={load.max() / load.mean():.2f}")
+    del layer, inp, res
+    _free()
+
+
+@pytest.mark.timeout(600)
+def test_fullsize_zipf_trajectory():
+    """20 batches of the skewed-load workload, each followed by
+    moe_bias_update: the bias after every step is bit-identical to the
+    oracle's step from the same loads; routing is checked on every token of
+    the first and last batch and on a sample of the others; layer outputs on
+    sampled tokens of the first batch."""
+    spec = synth.get_config("zipf_stress_bf16")
+    say("[zipf] generating weights")
+    inp = synth.make_inputs(spec, "cuda")
+    import mixture_experts_layer_40_amd as moe
+    layer = moe.MoELayer(spec, inp, max_tokens=spec.T)
+    bias = torch.zeros(spec.E, dtype=torch.float32, device="cuda")
+    ratios, near_total = [], 0
+    for bt in range(spec.batches):
+        x = inp["x"] if bt == 0 else synth.make_x(spec, "cuda", batch=bt)
+        b_before = bias.cpu().numpy().copy()
+        layer.forward(x, bias)
+        torch.cuda.synchronize()
+        idx = layer.topk_idx.cpu().numpy().astype(np.int64)
+        gate = layer.topk_gate.cpu().numpy().astype(np.float64)
+        load = layer.load.cpu().numpy().astype(np.int64)
+        full = bt in (0, spec.batches - 1)
+        rows = None if full else np.sort(np.random.default_rng(bt).choice(spec.T, 2048, replace=False))
+        trows = None if rows is None else torch.as_tensor(rows, device="cuda")
+        r, _ = oracle_route(spec, x, inp["wr"], bias, rows=trows)
+        near_total += check_route(spec, r, idx, gate, load, rows=rows)
+        if bt == 0:
+            res = {"idx": idx, "y": layer.y[:spec.T]}
+            check_permutation(spec, idx, layer.expert_offsets.cpu().numpy().astype(np.int64),
+                              layer.perm_slot.cpu().numpy().astype(np.int64))
+            out = check_outputs(spec, layer, inp, res, r, x=x, rows=_sample_rows(spec.T, 8, r["near_tie"]))
+            say(f"[zipf] batch 0 y err/rms={out['y_err']:.3e}")
+        layer.bias_update(bias)
+        torch.cuda.synchronize()
+        want = oracle.bias_update(b_before, load)
+        assert np.array_equal(bias.cpu().numpy().view(np.uint32), want.view(np.uint32))
+        ratios.append(float(load.max() / load.mean()))
+        say(f"[zipf] batch {bt}: max/mean load {ratios[-1]:.2f}")
+    say(f"[zipf] near-ties checked: {near_total}; max/mean per batch {np.round(ratios, 2).tolist()}")
+    assert 9.0 <= ratios[0] <= 11.0
+    del layer, inp
+    _free()
