@@ -36,7 +36,6 @@ namespace moe {
 
 namespace {
 
-constexpr int kBM = 128;          // tokens per tile (bf16 / fp8 path)
 constexpr int kBNGate = 128;      // intermediate columns per gate/up tile (x2 rows: W1 + W3)
 constexpr int kBNDown = 256;      // output rows per down tile
 constexpr int kBMF32 = 32;        // tokens per tile (fp32 path)
@@ -103,22 +102,131 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
 
 // ---------------------------------------------------------------------------
 // bf16 activations, bf16 or fp8 weights, MFMA 16x16x32.
+//
+// BM  : tokens per tile (16, 64 or 128), i.e. up to BM/16 token fragments.
+// NSA : depth of the per-wave weight register ring; the weights of stage
+//       s + NSA - 1 are requested while stage s is multiplied.
+// The K loop is specialised on the number NT of token fragments the tile
+// really has, so it is straight-line code: no exec-masked loads, no branches
+// between the LDS reads and the MFMAs, and the compiler can keep the
+// prefetched loads in flight across the multiply.
 // ---------------------------------------------------------------------------
-template <int MODE, bool FP8>
+template <bool FP8, int NSA, int BM>
+struct MainLoop {
+  static constexpr int AW = FP8 ? 1 : 2;       // 16-byte loads per fragment per stage
+  static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
+
+  // acc[j][t] += W rows (fragment j) x token fragment t, over the whole K axis.
+  // Every load, LDS write and MFMA is unconditional: token rows past the
+  // expert's end read its last row, prefetches past the last stage re-read the
+  // last stage, and when a stage has fewer 16-byte chunks than threads the
+  // extra threads repeat a chunk (writing the same bytes to the same place).
+  template <int NT>
+  __device__ __forceinline__ static void run(const uint8_t* const (&aptr)[4], const uint16_t* act,
+                                             int row0, int mvalid, int kdim, uint16_t* bs,
+                                             f32x4 (&acc)[4][BM / 16]) {
+    constexpr int CH = NT * 16 * 8;                     // 16-byte chunks per token stage
+    constexpr int BCH = (CH + 255) / 256;               // per thread
+    const int tid = threadIdx.x, l = lane_id(), g = l >> 4, r16 = l & 15;
+    const int nk = kdim / 64;
+
+    const uint16_t* bsrc[BCH];
+    int bdst[BCH];
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int q = (tid + 256 * i) % CH;
+      const int row = q >> 3, ch = q & 7;
+      const int src_row = row < mvalid ? row : mvalid - 1;
+      bsrc[i] = act + static_cast<size_t>(row0 + src_row) * kdim + ch * 8;
+      bdst[i] = row * 64 + ((ch ^ (row & 7)) * 8);
+    }
+
+    u32x4 ra[NSA][4][AW];
+    u32x4 rb[BCH];
+    auto load_a = [&](u32x4 (&dst)[4][AW], int ks) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(aptr[j] + static_cast<size_t>(ks) * 64 * WB);
+#pragma unroll
+        for (int v = 0; v < AW; ++v) dst[j][v] = p[v];
+      }
+    };
+    auto load_b = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + ks * 64);
+    };
+    auto store_b = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < BCH; ++i) *reinterpret_cast<u32x4*>(bs + buf * (BM * 64) + bdst[i]) = rb[i];
+    };
+    auto compute = [&](const u32x4 (&src)[4][AW], int buf) {
+      u32x4 op[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (FP8) {
+          fp8x16_to_bf16x16(src[j][0], op[j][0], op[j][1]);
+        } else {
+          op[j][0] = src[j][0];
+          op[j][1] = src[j][AW - 1];
+        }
+      }
+      const uint16_t* b0 = bs + buf * (BM * 64);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 b[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int tok = 16 * t + r16, ch = 2 * g + s;
+          b[t] = *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ (tok & 7)) * 8));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][t] = mfma_16x16x32(op[j][s], b[t], acc[j][t]);
+      }
+    };
+
+#pragma unroll
+    for (int p = 0; p < NSA - 1; ++p) load_a(ra[p], min(p, nk - 1));
+    load_b(0);
+    store_b(0);
+    __syncthreads();
+    for (int base = 0; base < nk; base += NSA) {
+#pragma unroll
+      for (int u = 0; u < NSA; ++u) {
+        const int s = base + u;
+        if (s >= nk) break;
+        // token tile first: waiting for it before the LDS write then leaves
+        // the (later-issued) weight prefetches in flight
+        load_b(min(s + 1, nk - 1));
+        load_a(ra[(u + NSA - 1) % NSA], min(s + NSA - 1, nk - 1));
+        // keep the prefetches issued ahead of the multiply
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra[u], s & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        store_b((s + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+};
+
+template <int MODE, bool FP8, int BM, int NSA>
 __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBM * 64];
+  constexpr int NTF = BM / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2 * BM * 64];
 
   Tile tl;
-  if (!decode_tile(a, kBM, tl)) return;
+  if (!decode_tile(a, BM, tl)) return;
 
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
+  const int l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
   const int ntf = (tl.mvalid + 15) >> 4;
 
   // ---- this wave's weight rows (4 fragments of 16) ----
   int nrow0;      // first weight row of the wave (gate/up: first intermediate column)
   bool wvalid;
   const uint8_t* aptr[4];
-  const size_t wbytes = FP8 ? 1 : 2;
+  constexpr size_t wbytes = FP8 ? 1 : 2;
   if (MODE == kGateUp) {
     nrow0 = tl.nblk * kBNGate + 32 * w;
     wvalid = nrow0 < a.n;
@@ -141,89 +249,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
     }
   }
 
-  // ---- token rows this thread stages (4 chunks of 16 bytes per stage) ----
-  const uint16_t* act = static_cast<const uint16_t*>(a.act);
-  const int bch = tid & 7;
-  const uint16_t* bsrc[4];
-  int bdst[4];
-  bool bval[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (tid >> 3) + 32 * i;
-    bval[i] = row < tl.mvalid;
-    bsrc[i] = act + static_cast<size_t>(tl.row0 + (bval[i] ? row : 0)) * a.kdim + bch * 8;
-    bdst[i] = row * 64 + ((bch ^ (row & 7)) * 8);
-  }
-
-  f32x4 acc[4][8];
+  f32x4 acc[4][NTF];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTF; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = a.kdim / 64;
-  // A register ring: 2 stages. bf16: 2 x 16B per fragment; fp8: 1 x 16B.
-  u32x4 ra[2][4][2];
-  u32x4 rb[4];
-
-  auto load_a = [&](u32x4 (&dst)[4][2], int ks) {
-    if (!wvalid) return;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(aptr[j] + static_cast<size_t>(ks) * 64 * wbytes);
-      dst[j][0] = p[0];
-      if (!FP8) dst[j][1] = p[1];
-    }
-  };
-  auto load_b = [&](int ks) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (bval[i]) rb[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + ks * 64);
-  };
-  auto store_b = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (bval[i]) *reinterpret_cast<u32x4*>(&bs[buf][bdst[i]]) = rb[i];
-  };
-  auto compute = [&](const u32x4 (&src)[4][2], int buf) {
-    if (!wvalid) return;
-    u32x4 op[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (FP8) {
-        fp8x16_to_bf16x16(src[j][0], op[j][0], op[j][1]);
-      } else {
-        op[j][0] = src[j][0];
-        op[j][1] = src[j][1];
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        if (t < ntf) {
-          const int tok = 16 * t + r16, ch = 2 * g + s;
-          const u32x4 b = *reinterpret_cast<const u32x4*>(&bs[buf][tok * 64 + ((ch ^ (tok & 7)) * 8)]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j][t] = mfma_16x16x32(op[j][s], b, acc[j][t]);
-        }
-      }
-  };
-
-  load_a(ra[0], 0);
-  load_b(0);
-  store_b(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ks += 2) {
-    if (ks + 1 < nk) { load_a(ra[1], ks + 1); load_b(ks + 1); }
-    compute(ra[0], 0);
-    if (ks + 1 < nk) store_b(1);
-    __syncthreads();
-    if (ks + 1 >= nk) break;
-    if (ks + 2 < nk) { load_a(ra[0], ks + 2); load_b(ks + 2); }
-    compute(ra[1], 1);
-    if (ks + 2 < nk) store_b(0);
-    __syncthreads();
+  const uint16_t* act = static_cast<const uint16_t*>(a.act);
+  using ML = MainLoop<FP8, NSA, BM>;
+  switch (ntf) {
+#define MOE_NT_CASE(n) \
+    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, tl.mvalid, a.kdim, bs, acc); break;
+    MOE_NT_CASE(1) MOE_NT_CASE(2) MOE_NT_CASE(3) MOE_NT_CASE(4)
+    MOE_NT_CASE(5) MOE_NT_CASE(6) MOE_NT_CASE(7) MOE_NT_CASE(8)
+#undef MOE_NT_CASE
+    default: break;
   }
 
   if (!wvalid) return;
@@ -241,12 +281,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
         }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < NTF; ++t) {
         const int tok = 16 * t + r16;
         if (t < ntf && tok < tl.mvalid) {
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu(acc[jj][t][q] * sg[q]) * (acc[jj + 2][t][q] * su[q]);
+          for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[jj][t][q] * sg[q]) * (acc[jj + 2][t][q] * su[q]);
           u32x2 v;
           v.x = pack_bf16x2(hv[0], hv[1]);
           v.y = pack_bf16x2(hv[2], hv[3]);
@@ -256,7 +296,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NTF; ++t) {
       const int tok = 16 * t + r16;
       if (!(t < ntf && tok < tl.mvalid)) continue;
       const int p = tl.row0 + tok;
@@ -373,7 +413,33 @@ int64_t grid_for(int64_t max_tiles) {
   return per * kNumXcd;
 }
 
-hipError_t run_gemm(int mode, bool f32, bool fp8, const GemmArgs& a, int64_t max_tiles,
+// Token-tile size for a group: the smallest of 16 / 64 / 128 that covers the
+// expected rows per expert (decode-like groups stream weights with one token
+// fragment; prefill groups amortise each weight tile over 128 tokens).
+int pick_bm(int64_t rows_per_group) {
+  if (rows_per_group <= 16) return 16;
+  if (rows_per_group <= 64) return 64;
+  return 128;
+}
+
+template <int MODE, bool FP8>
+void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
+#ifndef MOE_NS_BIG
+#define MOE_NS_BIG 2
+#endif
+#ifndef MOE_NS_SMALL
+#define MOE_NS_SMALL 4
+#endif
+  constexpr int NS_BIG = MOE_NS_BIG;
+  constexpr int NS_SMALL = MOE_NS_SMALL;
+  switch (bm) {
+    case 16: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 16, NS_SMALL>), gd, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL>), gd, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG>), gd, dim3(256), 0, s, a); break;
+  }
+}
+
+hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int64_t max_tiles,
                     hipStream_t s) {
   const int64_t grid = grid_for(max_tiles);
   if (grid <= 0) return hipSuccess;
@@ -382,11 +448,11 @@ hipError_t run_gemm(int mode, bool f32, bool fp8, const GemmArgs& a, int64_t max
     if (mode == kGateUp) hipLaunchKernelGGL(grouped_gemm_f32<kGateUp>, gd, bd, 0, s, a);
     else hipLaunchKernelGGL(grouped_gemm_f32<kDown>, gd, bd, 0, s, a);
   } else if (fp8) {
-    if (mode == kGateUp) hipLaunchKernelGGL((grouped_gemm_mfma<kGateUp, true>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((grouped_gemm_mfma<kDown, true>), gd, bd, 0, s, a);
+    if (mode == kGateUp) launch_mfma<kGateUp, true>(bm, gd, s, a);
+    else launch_mfma<kDown, true>(bm, gd, s, a);
   } else {
-    if (mode == kGateUp) hipLaunchKernelGGL((grouped_gemm_mfma<kGateUp, false>), gd, bd, 0, s, a);
-    else hipLaunchKernelGGL((grouped_gemm_mfma<kDown, false>), gd, bd, 0, s, a);
+    if (mode == kGateUp) launch_mfma<kGateUp, false>(bm, gd, s, a);
+    else launch_mfma<kDown, false>(bm, gd, s, a);
   }
   return hipGetLastError();
 }
@@ -395,10 +461,11 @@ struct Blocking {
   int bm, nb1, nb2;
 };
 
-Blocking blocking(const moe_config& c, int n_inter) {
+// rows_per_group: expected rows per expert (T*K/E routed, T shared)
+Blocking blocking(const moe_config& c, int n_inter, int64_t rows_per_group) {
   if (c.act_dtype == MOE_DTYPE_F32)
     return {kBMF32, (n_inter + kBNF32 - 1) / kBNF32, (c.hidden + kBNF32 - 1) / kBNF32};
-  return {kBM, (n_inter + kBNGate - 1) / kBNGate, (c.hidden + kBNDown - 1) / kBNDown};
+  return {pick_bm(rows_per_group), (n_inter + kBNGate - 1) / kBNGate, (c.hidden + kBNDown - 1) / kBNDown};
 }
 
 size_t elem_bytes(const moe_config& c) { return c.act_dtype == MOE_DTYPE_F32 ? 4 : 2; }
@@ -424,7 +491,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t
   const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
   if (TK == 0) return hipSuccess;
   const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
-  const Blocking b = blocking(c, I);
+  const Blocking b = blocking(c, I, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, expert_offsets, E, b.bm, b.nb1,
                      sched);
@@ -434,7 +501,7 @@ hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t
   g.act = x_perm; g.wa = w1; g.wb = w3; g.sa = s1; g.sb = s3;
   g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
   g.kdim = d; g.n = I; g.nb = b.nb1; g.wstride = static_cast<int64_t>(I) * d; g.h = h;
-  return run_gemm(kGateUp, f32, fp8, g, ((TK + b.bm - 1) / b.bm + E) * b.nb1, s);
+  return run_gemm(kGateUp, f32, fp8, b.bm, g, ((TK + b.bm - 1) / b.bm + E) * b.nb1, s);
 }
 
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
@@ -444,7 +511,7 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert
   const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
   if (TK == 0) return hipSuccess;
   const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
-  const Blocking b = blocking(c, I);
+  const Blocking b = blocking(c, I, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, expert_offsets, E, b.bm, b.nb2,
                      sched);
@@ -455,7 +522,7 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert
   g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
   g.kdim = I; g.n = d; g.nb = b.nb2; g.wstride = static_cast<int64_t>(d) * I;
   g.perm_slot = perm_slot; g.gate = topk_gate; g.out = out_slots;
-  return run_gemm(kDown, f32, fp8, g, ((TK + b.bm - 1) / b.bm + E) * b.nb2, s);
+  return run_gemm(kDown, f32, fp8, b.bm, g, ((TK + b.bm - 1) / b.bm + E) * b.nb2, s);
 }
 
 hipError_t launch_expert_ffn(const moe_config& c, const void* x_perm,
@@ -478,14 +545,14 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
   const int T = c.num_tokens, d = c.hidden, SI = c.num_shared * c.shared_inter;
   if (T == 0) return hipSuccess;
   const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
-  const Blocking b = blocking(c, SI);
+  const Blocking b = blocking(c, SI, T);
   const int64_t mt = (T + b.bm - 1) / b.bm;
 
   GemmArgs g1{};
   g1.act = x; g1.wa = w1s; g1.wb = w3s; g1.sa = s1s; g1.sb = s3s;
   g1.offsets = nullptr; g1.sched = nullptr; g1.fixed_m = T; g1.E = 1;
   g1.kdim = d; g1.n = SI; g1.nb = b.nb1; g1.wstride = 0; g1.h = ws;
-  hipError_t err = run_gemm(kGateUp, f32, fp8, g1, mt * b.nb1, s);
+  hipError_t err = run_gemm(kGateUp, f32, fp8, b.bm, g1, mt * b.nb1, s);
   if (err != hipSuccess) return err;
 
   GemmArgs g2{};
@@ -493,7 +560,7 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
   g2.offsets = nullptr; g2.sched = nullptr; g2.fixed_m = T; g2.E = 1;
   g2.kdim = SI; g2.n = d; g2.nb = b.nb2; g2.wstride = 0;
   g2.perm_slot = nullptr; g2.gate = nullptr; g2.out = y_shared; g2.out_f32 = 1;
-  return run_gemm(kDown, f32, fp8, g2, mt * b.nb2, s);
+  return run_gemm(kDown, f32, fp8, b.bm, g2, mt * b.nb2, s);
 }
 
 }  // namespace moe
