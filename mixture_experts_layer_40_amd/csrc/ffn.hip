@@ -14,8 +14,9 @@
 //    tile. Weight rows are never shared between waves, so every wave streams
 //    its rows straight from HBM into MFMA operand registers (fp8 codes are
 //    widened to bf16 in registers, exactly); only the token tile, which all
-//    4 waves read, is staged through LDS (double buffered, XOR-swizzled
-//    16-byte chunks, conflict-free reads and writes).
+//    4 waves read, is staged through LDS (double buffered; 16-byte chunks
+//    XOR-swizzled by row pair so the 16 rows one ds_read_b128 serves land on
+//    16 distinct groups of the 64 banks: conflict-free reads and writes).
 //  * Skew: token fragments of 16 beyond an expert's row count are skipped, so
 //    an expert with 3 rows costs one fragment of MFMA work while its weights
 //    are still read exactly once per token tile.
@@ -101,33 +102,37 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 activations, bf16 or fp8 weights, MFMA 16x16x32.
+// bf16 activations, bf16 or fp8 weights, MFMA 32x32x16.
 //
-// BM  : tokens per tile (16, 64 or 128), i.e. up to BM/16 token fragments.
-// NSA : depth of the per-wave weight register ring; the weights of stage
-//       s + NSA - 1 are requested while stage s is multiplied.
-// The K loop is specialised on the number NT of token fragments the tile
-// really has, so it is straight-line code: no exec-masked loads, no branches
-// between the LDS reads and the MFMAs, and the compiler can keep the
-// prefetched loads in flight across the multiply.
+// A block computes 256 weight rows x BM tokens (BM = 32..256) of one expert.
+// Wave w owns 64 weight rows (two 32-row fragments) and all BM tokens, so the
+// weight rows are never shared: each lane streams its 64 contiguous bytes of
+// a row per 64-wide K stage (32 K-elements: lane group g = l/32 takes
+// K-elements 32g .. 32g+31 of the stage, 8 per MFMA step) straight into a
+// register ring NSA stages deep. The token tile, read by all four waves, is
+// staged through LDS: requested at the start of a stage, written to the
+// other LDS buffer at its end. 16-byte chunks are XOR-swizzled by row pair,
+// so the 16 rows one ds_read_b128 serves land on 16 distinct bank groups.
+// The K loop is specialised on the number NT of 32-token fragments the tile
+// really has: branch-free, and a tile with 3 rows costs one fragment.
 // ---------------------------------------------------------------------------
 template <bool FP8, int NSA, int BM>
 struct MainLoop {
-  static constexpr int AW = FP8 ? 1 : 2;       // 16-byte loads per fragment per stage
+  static constexpr int AW = FP8 ? 2 : 4;       // 16-byte loads per fragment per stage
   static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
 
-  // acc[j][t] += W rows (fragment j) x token fragment t, over the whole K axis.
+  // acc[f][t] += W rows (fragment f) x token fragment t, over the whole K axis.
   // Every load, LDS write and MFMA is unconditional: token rows past the
   // expert's end read its last row, prefetches past the last stage re-read the
   // last stage, and when a stage has fewer 16-byte chunks than threads the
   // extra threads repeat a chunk (writing the same bytes to the same place).
   template <int NT>
-  __device__ __forceinline__ static void run(const uint8_t* const (&aptr)[4], const uint16_t* act,
+  __device__ __forceinline__ static void run(const uint8_t* const (&aptr)[2], const uint16_t* act,
                                              int row0, int mvalid, int kdim, uint16_t* bs,
-                                             f32x4 (&acc)[4][BM / 16]) {
-    constexpr int CH = NT * 16 * 8;                     // 16-byte chunks per token stage
+                                             f32x16 (&acc)[2][BM / 32]) {
+    constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
     constexpr int BCH = (CH + 255) / 256;               // per thread
-    const int tid = threadIdx.x, l = lane_id(), g = l >> 4, r16 = l & 15;
+    const int tid = threadIdx.x, l = lane_id(), g = l >> 5, r32 = l & 31;
     const int nk = kdim / 64;
 
     const uint16_t* bsrc[BCH];
@@ -138,17 +143,17 @@ struct MainLoop {
       const int row = q >> 3, ch = q & 7;
       const int src_row = row < mvalid ? row : mvalid - 1;
       bsrc[i] = act + static_cast<size_t>(row0 + src_row) * kdim + ch * 8;
-      bdst[i] = row * 64 + ((ch ^ (row & 7)) * 8);
+      bdst[i] = row * 64 + ((ch ^ ((row >> 1) & 7)) * 8);
     }
 
-    u32x4 ra[NSA][4][AW];
+    u32x4 ra[NSA][2][AW];
     u32x4 rb[BCH];
-    auto load_a = [&](u32x4 (&dst)[4][AW], int ks) {
+    auto load_a = [&](u32x4 (&dst)[2][AW], int ks) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(aptr[j] + static_cast<size_t>(ks) * 64 * WB);
+      for (int f = 0; f < 2; ++f) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(aptr[f] + static_cast<size_t>(ks) * 64 * WB);
 #pragma unroll
-        for (int v = 0; v < AW; ++v) dst[j][v] = p[v];
+        for (int v = 0; v < AW; ++v) dst[f][v] = p[v];
       }
     };
     auto load_b = [&](int ks) {
@@ -159,36 +164,51 @@ struct MainLoop {
 #pragma unroll
       for (int i = 0; i < BCH; ++i) *reinterpret_cast<u32x4*>(bs + buf * (BM * 64) + bdst[i]) = rb[i];
     };
-    auto compute = [&](const u32x4 (&src)[4][AW], int buf) {
-      u32x4 op[4][2];
+    // token fragments of MFMA step s (K-elements 8s .. 8s+7 of each lane group)
+    auto read_b = [&](u32x4 (&dst)[NT], const uint16_t* b0, int s) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (FP8) {
-          fp8x16_to_bf16x16(src[j][0], op[j][0], op[j][1]);
-        } else {
-          op[j][0] = src[j][0];
-          op[j][1] = src[j][AW - 1];
-        }
+      for (int t = 0; t < NT; ++t) {
+        const int tok = 32 * t + r32, ch = 4 * g + s;
+        dst[t] = *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8));
       }
+    };
+    // One 64-wide K stage: four MFMA steps. Fragment t of step s+1 is read
+    // from LDS just before the two MFMAs of fragment t of step s, and the
+    // order is pinned, so each read has 2*NT MFMAs to land before its use.
+    auto compute = [&](const u32x4 (&src)[2][AW], int buf) {
       const uint16_t* b0 = bs + buf * (BM * 64);
+      u32x4 bfr[2][NT];
+      read_b(bfr[0], b0, 0);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u32x4 b[NT];
+      for (int s = 0; s < 4; ++s) {
+        u32x4 op[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          if constexpr (FP8) {
+            u32x4 lo, hi;
+            fp8x16_to_bf16x16(src[f][s >> 1], lo, hi);
+            op[f] = (s & 1) ? hi : lo;
+          } else {
+            op[f] = src[f][s];
+          }
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const int tok = 16 * t + r16, ch = 2 * g + s;
-          b[t] = *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ (tok & 7)) * 8));
+          if (s < 3) {
+            const int tok = 32 * t + r32, ch = 4 * g + s + 1;
+            bfr[(s + 1) & 1][t] =
+                *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8));
+          }
+#pragma unroll
+          for (int f = 0; f < 2; ++f) acc[f][t] = mfma_32x32x16(op[f], bfr[s & 1][t], acc[f][t]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j][t] = mfma_16x16x32(op[j][s], b[t], acc[j][t]);
       }
     };
 
+    load_b(0);
 #pragma unroll
     for (int p = 0; p < NSA - 1; ++p) load_a(ra[p], min(p, nk - 1));
-    load_b(0);
     store_b(0);
     __syncthreads();
     for (int base = 0; base < nk; base += NSA) {
@@ -196,15 +216,14 @@ struct MainLoop {
       for (int u = 0; u < NSA; ++u) {
         const int s = base + u;
         if (s >= nk) break;
-        // token tile first: waiting for it before the LDS write then leaves
-        // the (later-issued) weight prefetches in flight
+        // tokens first: waiting for them before the LDS write leaves the
+        // later-issued weight prefetches in flight
         load_b(min(s + 1, nk - 1));
         load_a(ra[(u + NSA - 1) % NSA], min(s + NSA - 1, nk - 1));
-        // keep the prefetches issued ahead of the multiply
-        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);   // keep the requests ahead of the multiply
         compute(ra[u], s & 1);
         __builtin_amdgcn_sched_barrier(0);
-        store_b((s + 1) & 1);
+        store_b((s + 1) & 1);                // the other buffer: its readers passed the barrier
         __syncthreads();
       }
     }
@@ -213,47 +232,47 @@ struct MainLoop {
 
 template <int MODE, bool FP8, int BM, int NSA>
 __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
-  constexpr int NTF = BM / 16;
+  constexpr int NTF = BM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t bs[2 * BM * 64];
 
   Tile tl;
   if (!decode_tile(a, BM, tl)) return;
 
-  const int l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
-  const int ntf = (tl.mvalid + 15) >> 4;
+  const int l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
+  const int ntf = (tl.mvalid + 31) >> 5;
 
-  // ---- this wave's weight rows (4 fragments of 16) ----
-  int nrow0;      // first weight row of the wave (gate/up: first intermediate column)
+  // ---- this wave's weight rows: two fragments of 32 ----
+  //   gate/up: fragment 0 = W1 rows, fragment 1 = W3 rows of the same 32
+  //            intermediate columns nrow0 .. nrow0+31
+  //   down   : fragments 0 / 1 = W2 rows nrow0 .. nrow0+31 / +32 .. +63
+  int nrow0;
   bool wvalid;
-  const uint8_t* aptr[4];
+  const uint8_t* aptr[2];
   constexpr size_t wbytes = FP8 ? 1 : 2;
   if (MODE == kGateUp) {
     nrow0 = tl.nblk * kBNGate + 32 * w;
     wvalid = nrow0 < a.n;
-    const int rr = wvalid ? nrow0 : 0;
+    const int row = (wvalid ? nrow0 : 0) + r32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* base = static_cast<const uint8_t*>(j < 2 ? a.wa : a.wb);
-      const int row = rr + 16 * (j & 1) + r16;
-      aptr[j] = base + (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 16 * g) * wbytes;
-    }
+    for (int f = 0; f < 2; ++f)
+      aptr[f] = static_cast<const uint8_t*>(f == 0 ? a.wa : a.wb) +
+                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
   } else {
     nrow0 = tl.nblk * kBNDown + 64 * w;
     wvalid = nrow0 < a.n;
-    const int rr = wvalid ? nrow0 : 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = rr + 16 * j + r16;
-      aptr[j] = static_cast<const uint8_t*>(a.wa) +
-                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 16 * g) * wbytes;
+    for (int f = 0; f < 2; ++f) {
+      const int row = (wvalid ? nrow0 : 0) + 32 * f + r32;
+      aptr[f] = static_cast<const uint8_t*>(a.wa) +
+                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
     }
   }
 
-  f32x4 acc[4][NTF];
+  f32x16 acc[2][NTF];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
-    for (int t = 0; t < NTF; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTF; ++t) acc[f][t] = f32x16{};
 
   const uint16_t* act = static_cast<const uint16_t*>(a.act);
   using ML = MainLoop<FP8, NSA, BM>;
@@ -270,8 +289,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
   if (MODE == kGateUp) {
     uint16_t* h = static_cast<uint16_t*>(a.h);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int col = nrow0 + 16 * jj + 4 * g;
+    for (int i = 0; i < 4; ++i) {
+      const int col = nrow0 + 8 * i + 4 * g;
       float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
       if (FP8) {
 #pragma unroll
@@ -282,11 +301,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < NTF; ++t) {
-        const int tok = 16 * t + r16;
+        const int tok = 32 * t + r32;
         if (t < ntf && tok < tl.mvalid) {
           float hv[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) hv[q] = silu_fast(acc[jj][t][q] * sg[q]) * (acc[jj + 2][t][q] * su[q]);
+          for (int q = 0; q < 4; ++q)
+            hv[q] = silu_fast(acc[0][t][4 * i + q] * sg[q]) * (acc[1][t][4 * i + q] * su[q]);
           u32x2 v;
           v.x = pack_bf16x2(hv[0], hv[1]);
           v.y = pack_bf16x2(hv[2], hv[3]);
@@ -297,31 +317,33 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
   } else {
 #pragma unroll
     for (int t = 0; t < NTF; ++t) {
-      const int tok = 16 * t + r16;
+      const int tok = 32 * t + r32;
       if (!(t < ntf && tok < tl.mvalid)) continue;
       const int p = tl.row0 + tok;
       const int slot = a.perm_slot ? a.perm_slot[p] : p;
       if (slot < 0) continue;
       const float gv = a.gate ? a.gate[slot] : 1.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = nrow0 + 16 * j + 4 * g;
-        float ov[4];
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sc = FP8 ? a.sa[static_cast<size_t>(tl.e) * a.n + col + q] : 1.f;
-          ov[q] = (acc[j][t][q] * sc) * gv;
+        for (int i = 0; i < 4; ++i) {
+          const int col = nrow0 + 32 * f + 8 * i + 4 * g;
+          float ov[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float sc = FP8 ? a.sa[static_cast<size_t>(tl.e) * a.n + col + q] : 1.f;
+            ov[q] = (acc[f][t][4 * i + q] * sc) * gv;
+          }
+          const size_t o = static_cast<size_t>(slot) * a.n + col;
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+          } else {
+            u32x2 v;
+            v.x = pack_bf16x2(ov[0], ov[1]);
+            v.y = pack_bf16x2(ov[2], ov[3]);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
+          }
         }
-        const size_t o = static_cast<size_t>(slot) * a.n + col;
-        if (a.out_f32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{ov[0], ov[1], ov[2], ov[3]};
-        } else {
-          u32x2 v;
-          v.x = pack_bf16x2(ov[0], ov[1]);
-          v.y = pack_bf16x2(ov[2], ov[3]);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
-        }
-      }
     }
   }
 }
@@ -413,13 +435,18 @@ int64_t grid_for(int64_t max_tiles) {
   return per * kNumXcd;
 }
 
-// Token-tile size for a group: the smallest of 16 / 64 / 128 that covers the
-// expected rows per expert (decode-like groups stream weights with one token
-// fragment; prefill groups amortise each weight tile over 128 tokens).
+// Token-tile size for a group: the smallest of 32 / 64 / 128 / 256 that covers
+// the expected rows per expert (decode-like groups stream weights with one
+// token fragment; prefill groups amortise each weight tile over up to 256
+// tokens, which halves the L2-to-CU bytes per MFMA against 128).
+#ifndef MOE_MAX_BM
+#define MOE_MAX_BM 256
+#endif
 int pick_bm(int64_t rows_per_group) {
-  if (rows_per_group <= 16) return 16;
+  if (rows_per_group <= 32) return 32;
   if (rows_per_group <= 64) return 64;
-  return 128;
+  if (rows_per_group <= 128 || MOE_MAX_BM == 128) return 128;
+  return 256;
 }
 
 template <int MODE, bool FP8>
@@ -433,9 +460,10 @@ void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
   constexpr int NS_BIG = MOE_NS_BIG;
   constexpr int NS_SMALL = MOE_NS_SMALL;
   switch (bm) {
-    case 16: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 16, NS_SMALL>), gd, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL>), gd, dim3(256), 0, s, a); break;
     case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL>), gd, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG>), gd, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG>), gd, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG>), gd, dim3(256), 0, s, a); break;
   }
 }
 

@@ -109,7 +109,7 @@ __device__ void topk_token(const float (&lg)[4], int t, int E, int K, int score_
 // ---------------------------------------------------------------------------
 // Fused path (bf16, many tokens): one block = 32 tokens x all E experts.
 // Token rows are staged in LDS (double buffered, 16-byte chunks XOR-swizzled
-// by row); each wave streams its own router rows straight from global memory
+// by row pair, so the 16 rows one ds_read_b128 serves hit 16 distinct bank groups); each wave streams its own router rows straight from global memory
 // into MFMA operands, so LDS only carries the operand all waves share.
 // Within a 64-wide K stage, lane group g consumes K-elements 16g .. 16g+15
 // (two MFMA steps of 8); both operands use the same assignment.
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void route_fused_bf16(
   const int brow = tid >> 3, bch = tid & 7;
   const int btok = t0 + brow;
   const uint16_t* bsrc = x + static_cast<size_t>(btok < T ? btok : T - 1) * d + bch * 8;
-  const int bdst = brow * 64 + ((bch ^ (brow & 7)) * 8);
+  const int bdst = brow * 64 + ((bch ^ ((brow >> 1) & 7)) * 8);
 
   f32x4 acc[4][2];
 #pragma unroll
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void route_fused_bf16(
 #pragma unroll
       for (int tf = 0; tf < 2; ++tf) {
         const int tok = 16 * tf + r16, ch = 2 * g + s;
-        const u32x4 b = *reinterpret_cast<const u32x4*>(&xs[buf][tok * 64 + ((ch ^ (tok & 7)) * 8)]);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(&xs[buf][tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8)]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (fvalid[i]) acc[i][tf] = mfma_16x16x32(a[i][s], b, acc[i][tf]);

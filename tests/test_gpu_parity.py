@@ -42,6 +42,9 @@ CASES = {
     "fp8_small": _cfg("v3_decode_fp8", T=64, d=512, E=64, K=8, I=256, Is=256),
     # fp8 weights with multi-tile token blocks and 2 shared experts
     "fp8_multi": _cfg("v3_decode_fp8", T=700, d=256, E=16, K=4, I=192, S=2, Is=64),
+    # > 128 rows per expert: 256-token tiles, several per expert, ragged
+    "bm256": _cfg("v3_prefill_bf16", T=2000, d=256, E=16, K=4, I=256, Is=128),
+    "fp8_bm256": _cfg("v3_decode_fp8", T=1500, d=320, E=8, K=2, I=128, Is=64),
     # degenerate: K = E, E not a multiple of 16
     "k_eq_e": _cfg("v3_prefill_bf16", T=50, d=64, E=7, K=7, I=64, Is=64),
     "e20": _cfg("v3_prefill_bf16", T=129, d=64, E=20, K=5, I=64, Is=64),
