@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="before timing, run one 1 GiB read + 1 GiB write elementwise kernel, "
+                         "the known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer's path is built and timed on a single "
@@ -209,6 +212,13 @@ def main():
         sys.exit(2)
     moe.load_library()
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy: 1 GiB read, 1 GiB written")
     spec = synth.get_config(WORKLOAD)
     log(f"[bench] generating {WORKLOAD} inputs on the GPU")
     inp, layer, h, ws_gemm = setup(spec)
@@ -237,7 +247,8 @@ def main():
         "layer_TFLOPs": layer_tflops,
         "layer_frac_mfma_peak": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
         "load_max_over_mean": float(load.max() / load.mean()),
-        "roofline": {"kernel": "grouped_gemm_mfma<gate_up,bf16>", "bound": "mfma",
+        "roofline": {"kernel": "grouped_gemm_mfma<gate/up, bf16, 256-token tiles, routed>",
+                     "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(),
                      "algorithmic_flops_per_launch": gate_flops, "avg_launch_ms": gate_ms},

@@ -69,19 +69,17 @@ struct Tile {
   int e, row0, mvalid, nblk;
 };
 
-// Decode this block's tile; false when the block has no work.
+// Decode this block's tile; false when the block has no work. GROUPED: rows
+// of E experts at a.offsets with tile starts a.sched; otherwise one group of
+// a.fixed_m rows (the shared experts).
+template <bool GROUPED>
 __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) {
-  int total;
-  if (a.offsets) {
-    total = a.sched[a.E];
-  } else {
-    total = ((a.fixed_m + bm - 1) / bm) * a.nb;
-  }
+  const int total = GROUPED ? a.sched[a.E] : ((a.fixed_m + bm - 1) / bm) * a.nb;
   bool valid;
   const int tile = xcd_contiguous(blockIdx.x, total, valid);
   if (!valid) return false;
   int e = 0, local = tile, rbeg = 0, m = a.fixed_m;
-  if (a.offsets) {
+  if (GROUPED) {
     int lo = 0, hi = a.E - 1;  // largest e with sched[e] <= tile
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -230,13 +228,13 @@ struct MainLoop {
   }
 };
 
-template <int MODE, bool FP8, int BM, int NSA>
+template <int MODE, bool FP8, int BM, int NSA, bool GROUPED>
 __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
   constexpr int NTF = BM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t bs[2 * BM * 64];
 
   Tile tl;
-  if (!decode_tile(a, BM, tl)) return;
+  if (!decode_tile<GROUPED>(a, BM, tl)) return;
 
   const int l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
   const int ntf = (tl.mvalid + 31) >> 5;
@@ -358,7 +356,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs a) {
   __shared__ float ws1[kBNF32][33];
   __shared__ float ws3[kBNF32][33];
   Tile tl;
-  if (!decode_tile(a, kBMF32, tl)) return;
+  if (!(a.offsets ? decode_tile<true>(a, kBMF32, tl) : decode_tile<false>(a, kBMF32, tl))) return;
   const int tid = threadIdx.x;
   const int tok = tid >> 3, c0 = (tid & 7) * 4;
   const int n0 = tl.nblk * kBNF32;
@@ -449,7 +447,7 @@ int pick_bm(int64_t rows_per_group) {
   return 256;
 }
 
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, bool GROUPED>
 void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
 #ifndef MOE_NS_BIG
 #define MOE_NS_BIG 2
@@ -460,11 +458,17 @@ void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
   constexpr int NS_BIG = MOE_NS_BIG;
   constexpr int NS_SMALL = MOE_NS_SMALL;
   switch (bm) {
-    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL>), gd, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL>), gd, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG>), gd, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG>), gd, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL, GROUPED>), gd, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL, GROUPED>), gd, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG, GROUPED>), gd, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG, GROUPED>), gd, dim3(256), 0, s, a); break;
   }
+}
+
+template <int MODE, bool FP8>
+void launch_mfma_any(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
+  if (a.offsets) launch_mfma<MODE, FP8, true>(bm, gd, s, a);
+  else launch_mfma<MODE, FP8, false>(bm, gd, s, a);
 }
 
 hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int64_t max_tiles,
@@ -476,11 +480,11 @@ hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int
     if (mode == kGateUp) hipLaunchKernelGGL(grouped_gemm_f32<kGateUp>, gd, bd, 0, s, a);
     else hipLaunchKernelGGL(grouped_gemm_f32<kDown>, gd, bd, 0, s, a);
   } else if (fp8) {
-    if (mode == kGateUp) launch_mfma<kGateUp, true>(bm, gd, s, a);
-    else launch_mfma<kDown, true>(bm, gd, s, a);
+    if (mode == kGateUp) launch_mfma_any<kGateUp, true>(bm, gd, s, a);
+    else launch_mfma_any<kDown, true>(bm, gd, s, a);
   } else {
-    if (mode == kGateUp) launch_mfma<kGateUp, false>(bm, gd, s, a);
-    else launch_mfma<kDown, false>(bm, gd, s, a);
+    if (mode == kGateUp) launch_mfma_any<kGateUp, false>(bm, gd, s, a);
+    else launch_mfma_any<kDown, false>(bm, gd, s, a);
   }
   return hipGetLastError();
 }
