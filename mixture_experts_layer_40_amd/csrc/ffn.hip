@@ -102,34 +102,42 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
 // ---------------------------------------------------------------------------
 // bf16 activations, bf16 or fp8 weights, MFMA 32x32x16.
 //
-// A block computes 256 weight rows x BM tokens (BM = 32..256) of one expert.
-// Wave w owns 64 weight rows (two 32-row fragments) and all BM tokens, so the
-// weight rows are never shared: each lane streams its 64 contiguous bytes of
-// a row per 64-wide K stage (32 K-elements: lane group g = l/32 takes
+// A block (8 waves, two per SIMD) computes 256 weight rows x BM tokens
+// (BM = 32..256) of one expert. Wave w owns one 32-row weight fragment and all
+// BM tokens:
+//   gate/up: rows 0..15 of the fragment are gate (W1) rows and rows 16..31
+//            the up (W3) rows of the same 16 intermediate columns, so in the
+//            32x32 result the gate value of column c sits 16 rows above its
+//            up value, in the same lane: SiLU(g) * u is formed in registers;
+//   down   : 32 consecutive W2 rows.
+// Weight rows are never shared between waves: each lane streams its 64
+// contiguous bytes of a row per 64-wide K stage (lane group g = l/32 takes
 // K-elements 32g .. 32g+31 of the stage, 8 per MFMA step) straight into a
-// register ring NSA stages deep. The token tile, read by all four waves, is
+// register ring NSA stages deep. The token tile, read by all eight waves, is
 // staged through LDS: requested at the start of a stage, written to the
 // other LDS buffer at its end. 16-byte chunks are XOR-swizzled by row pair,
 // so the 16 rows one ds_read_b128 serves land on 16 distinct bank groups.
 // The K loop is specialised on the number NT of 32-token fragments the tile
 // really has: branch-free, and a tile with 3 rows costs one fragment.
 // ---------------------------------------------------------------------------
+constexpr int kThreads = 512;
+
 template <bool FP8, int NSA, int BM>
 struct MainLoop {
   static constexpr int AW = FP8 ? 2 : 4;       // 16-byte loads per fragment per stage
   static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
 
-  // acc[f][t] += W rows (fragment f) x token fragment t, over the whole K axis.
-  // Every load, LDS write and MFMA is unconditional: token rows past the
-  // expert's end read its last row, prefetches past the last stage re-read the
-  // last stage, and when a stage has fewer 16-byte chunks than threads the
-  // extra threads repeat a chunk (writing the same bytes to the same place).
+  // acc[t] += W fragment x token fragment t, over the whole K axis. Every
+  // load, LDS write and MFMA is unconditional: token rows past the expert's
+  // end read its last row, prefetches past the last stage re-read the last
+  // stage, and when a stage has fewer 16-byte chunks than threads the extra
+  // threads repeat a chunk (writing the same bytes to the same place).
   template <int NT>
-  __device__ __forceinline__ static void run(const uint8_t* const (&aptr)[2], const uint16_t* act,
-                                             int row0, int mvalid, int kdim, uint16_t* bs,
-                                             f32x16 (&acc)[2][BM / 32]) {
+  __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
+                                             int mvalid, int kdim, uint16_t* bs,
+                                             f32x16 (&acc)[BM / 32]) {
     constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
-    constexpr int BCH = (CH + 255) / 256;               // per thread
+    constexpr int BCH = (CH + kThreads - 1) / kThreads; // per thread
     const int tid = threadIdx.x, l = lane_id(), g = l >> 5, r32 = l & 31;
     const int nk = kdim / 64;
 
@@ -137,22 +145,19 @@ struct MainLoop {
     int bdst[BCH];
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-      const int q = (tid + 256 * i) % CH;
+      const int q = (tid + kThreads * i) % CH;
       const int row = q >> 3, ch = q & 7;
       const int src_row = row < mvalid ? row : mvalid - 1;
       bsrc[i] = act + static_cast<size_t>(row0 + src_row) * kdim + ch * 8;
       bdst[i] = row * 64 + ((ch ^ ((row >> 1) & 7)) * 8);
     }
 
-    u32x4 ra[NSA][2][AW];
+    u32x4 ra[NSA][AW];
     u32x4 rb[BCH];
-    auto load_a = [&](u32x4 (&dst)[2][AW], int ks) {
+    auto load_a = [&](u32x4 (&dst)[AW], int ks) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(aptr + static_cast<size_t>(ks) * 64 * WB);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(aptr[f] + static_cast<size_t>(ks) * 64 * WB);
-#pragma unroll
-        for (int v = 0; v < AW; ++v) dst[f][v] = p[v];
-      }
+      for (int v = 0; v < AW; ++v) dst[v] = p[v];
     };
     auto load_b = [&](int ks) {
 #pragma unroll
@@ -162,43 +167,31 @@ struct MainLoop {
 #pragma unroll
       for (int i = 0; i < BCH; ++i) *reinterpret_cast<u32x4*>(bs + buf * (BM * 64) + bdst[i]) = rb[i];
     };
-    // token fragments of MFMA step s (K-elements 8s .. 8s+7 of each lane group)
-    auto read_b = [&](u32x4 (&dst)[NT], const uint16_t* b0, int s) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int tok = 32 * t + r32, ch = 4 * g + s;
-        dst[t] = *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8));
-      }
+    auto read_b = [&](u32x4& dst, const uint16_t* b0, int t, int s) {
+      const int tok = 32 * t + r32, ch = 4 * g + s;
+      dst = *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8));
     };
     // One 64-wide K stage: four MFMA steps. Fragment t of step s+1 is read
-    // from LDS just before the two MFMAs of fragment t of step s, and the
-    // order is pinned, so each read has 2*NT MFMAs to land before its use.
-    auto compute = [&](const u32x4 (&src)[2][AW], int buf) {
+    // from LDS just before the MFMA of fragment t of step s (order pinned).
+    auto compute = [&](const u32x4 (&src)[AW], int buf) {
       const uint16_t* b0 = bs + buf * (BM * 64);
       u32x4 bfr[2][NT];
-      read_b(bfr[0], b0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) read_b(bfr[0][t], b0, t, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 op[2];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          if constexpr (FP8) {
-            u32x4 lo, hi;
-            fp8x16_to_bf16x16(src[f][s >> 1], lo, hi);
-            op[f] = (s & 1) ? hi : lo;
-          } else {
-            op[f] = src[f][s];
-          }
+        u32x4 op;
+        if constexpr (FP8) {
+          u32x4 lo, hi;
+          fp8x16_to_bf16x16(src[s >> 1], lo, hi);
+          op = (s & 1) ? hi : lo;
+        } else {
+          op = src[s];
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if (s < 3) {
-            const int tok = 32 * t + r32, ch = 4 * g + s + 1;
-            bfr[(s + 1) & 1][t] =
-                *reinterpret_cast<const u32x4*>(b0 + tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8));
-          }
-#pragma unroll
-          for (int f = 0; f < 2; ++f) acc[f][t] = mfma_32x32x16(op[f], bfr[s & 1][t], acc[f][t]);
+          if (s < 3) read_b(bfr[(s + 1) & 1][t], b0, t, s + 1);
+          acc[t] = mfma_32x32x16(op, bfr[s & 1][t], acc[t]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -229,7 +222,7 @@ struct MainLoop {
 };
 
 template <int MODE, bool FP8, int BM, int NSA, bool GROUPED>
-__global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
+__global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   constexpr int NTF = BM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t bs[2 * BM * 64];
 
@@ -239,38 +232,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
   const int l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
   const int ntf = (tl.mvalid + 31) >> 5;
 
-  // ---- this wave's weight rows: two fragments of 32 ----
-  //   gate/up: fragment 0 = W1 rows, fragment 1 = W3 rows of the same 32
-  //            intermediate columns nrow0 .. nrow0+31
-  //   down   : fragments 0 / 1 = W2 rows nrow0 .. nrow0+31 / +32 .. +63
-  int nrow0;
+  // ---- this wave's 32-row weight fragment ----
+  int nrow0;        // gate/up: first of 16 intermediate columns; down: first of 32 rows
   bool wvalid;
-  const uint8_t* aptr[2];
+  const uint8_t* aptr;
   constexpr size_t wbytes = FP8 ? 1 : 2;
   if (MODE == kGateUp) {
-    nrow0 = tl.nblk * kBNGate + 32 * w;
+    nrow0 = tl.nblk * kBNGate + 16 * w;
+    wvalid = nrow0 < a.n;
+    const int row = (wvalid ? nrow0 : 0) + (r32 & 15);
+    aptr = static_cast<const uint8_t*>(r32 < 16 ? a.wa : a.wb) +
+           (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
+  } else {
+    nrow0 = tl.nblk * kBNDown + 32 * w;
     wvalid = nrow0 < a.n;
     const int row = (wvalid ? nrow0 : 0) + r32;
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-      aptr[f] = static_cast<const uint8_t*>(f == 0 ? a.wa : a.wb) +
-                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
-  } else {
-    nrow0 = tl.nblk * kBNDown + 64 * w;
-    wvalid = nrow0 < a.n;
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      const int row = (wvalid ? nrow0 : 0) + 32 * f + r32;
-      aptr[f] = static_cast<const uint8_t*>(a.wa) +
-                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
-    }
+    aptr = static_cast<const uint8_t*>(a.wa) +
+           (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
   }
 
-  f32x16 acc[2][NTF];
+  f32x16 acc[NTF];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
-#pragma unroll
-    for (int t = 0; t < NTF; ++t) acc[f][t] = f32x16{};
+  for (int t = 0; t < NTF; ++t) acc[t] = f32x16{};
 
   const uint16_t* act = static_cast<const uint16_t*>(a.act);
   using ML = MainLoop<FP8, NSA, BM>;
@@ -287,7 +270,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
   if (MODE == kGateUp) {
     uint16_t* h = static_cast<uint16_t*>(a.h);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {          // result rows 8i+4g+q: gate; +16: up
       const int col = nrow0 + 8 * i + 4 * g;
       float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
       if (FP8) {
@@ -304,7 +287,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
           float hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            hv[q] = silu_fast(acc[0][t][4 * i + q] * sg[q]) * (acc[1][t][4 * i + q] * su[q]);
+            hv[q] = silu_fast(acc[t][4 * i + q] * sg[q]) * (acc[t][4 * (i + 2) + q] * su[q]);
           u32x2 v;
           v.x = pack_bf16x2(hv[0], hv[1]);
           v.y = pack_bf16x2(hv[2], hv[3]);
@@ -322,26 +305,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_mfma(GemmArgs a) {
       if (slot < 0) continue;
       const float gv = a.gate ? a.gate[slot] : 1.f;
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int i = 0; i < 4; ++i) {
+        const int col = nrow0 + 8 * i + 4 * g;
+        float ov[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int col = nrow0 + 32 * f + 8 * i + 4 * g;
-          float ov[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float sc = FP8 ? a.sa[static_cast<size_t>(tl.e) * a.n + col + q] : 1.f;
-            ov[q] = (acc[f][t][4 * i + q] * sc) * gv;
-          }
-          const size_t o = static_cast<size_t>(slot) * a.n + col;
-          if (a.out_f32) {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{ov[0], ov[1], ov[2], ov[3]};
-          } else {
-            u32x2 v;
-            v.x = pack_bf16x2(ov[0], ov[1]);
-            v.y = pack_bf16x2(ov[2], ov[3]);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
-          }
+        for (int q = 0; q < 4; ++q) {
+          const float sc = FP8 ? a.sa[static_cast<size_t>(tl.e) * a.n + col + q] : 1.f;
+          ov[q] = (acc[t][4 * i + q] * sc) * gv;
         }
+        const size_t o = static_cast<size_t>(slot) * a.n + col;
+        if (a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{ov[0], ov[1], ov[2], ov[3]};
+        } else {
+          u32x2 v;
+          v.x = pack_bf16x2(ov[0], ov[1]);
+          v.y = pack_bf16x2(ov[2], ov[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
+        }
+      }
     }
   }
 }
@@ -458,10 +439,10 @@ void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
   constexpr int NS_BIG = MOE_NS_BIG;
   constexpr int NS_SMALL = MOE_NS_SMALL;
   switch (bm) {
-    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL, GROUPED>), gd, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL, GROUPED>), gd, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG, GROUPED>), gd, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG, GROUPED>), gd, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
   }
 }
 
