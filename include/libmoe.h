@@ -73,6 +73,12 @@ extern "C" {
 #define MOE_DTYPE_BF16     1
 #define MOE_DTYPE_FP8_E4M3 2  /* weights only */
 
+#define MOE_LAYOUT_ROWS  0  /* expert weights row-major, as the shapes below state  */
+#define MOE_LAYOUT_TILED 1  /* expert weights pre-tiled by moe_pack_weights          */
+
+#define MOE_PACK_GATE_UP 0  /* W1 and W3 of each expert -> one tiled gate/up tensor */
+#define MOE_PACK_DOWN    1  /* W2 of each expert -> one tiled tensor                */
+
 #define MOE_WS_ROUTE   0
 #define MOE_WS_PERMUTE 1
 #define MOE_WS_FFN     2
@@ -98,6 +104,13 @@ typedef struct moe_config {
   int32_t weight_dtype;  /* MOE_DTYPE_F32 (with f32 act), BF16 or FP8_E4M3 (bf16) */
   int32_t out_dtype;     /* layer output y: MOE_DTYPE_F32, or MOE_DTYPE_BF16 with
                             bf16 activations (then y carries one more bf16 rounding) */
+  int32_t weight_layout; /* MOE_LAYOUT_ROWS, or MOE_LAYOUT_TILED (bf16 / fp8 weights):
+                            the expert-FFN calls then take the moe_pack_weights
+                            tensors -- w1 (w1s) = the tiled gate/up tensor, w3 (w3s)
+                            = NULL, w2 (w2s) = the tiled down tensor; scales are
+                            unchanged. Same results bit for bit; each weight load
+                            then reads whole 1 KB stripes, which HBM serves faster
+                            than the rows layout's 64-byte pieces of 32 rows. */
 } moe_config;
 
 /* Validate a configuration without touching the GPU. Returns a status code. */
@@ -110,6 +123,31 @@ size_t moe_workspace_size(const moe_config* cfg, int which);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* moe_status_string(int status);
+
+/* ---- moe_pack_weights -----------------------------------------------------
+ * One-time relocation of expert weights into the tiled layout that the
+ * expert-FFN calls read with MOE_LAYOUT_TILED (no arithmetic: every byte is
+ * copied once, so results are identical to the rows layout).
+ *   which = MOE_PACK_GATE_UP: src_a = W1, src_b = W3, each [groups, rows,
+ *           cols]; dst holds 2 * groups * rows * cols weights. Tiled row
+ *           32c + r (c = 0 .. rows/16 - 1) of group e is W1[e, 16c + r] for
+ *           r < 16 and W3[e, 16c + r - 16] otherwise.
+ *   which = MOE_PACK_DOWN:    src_a = W2 [groups, rows, cols], src_b = NULL;
+ *           dst holds groups * rows * cols weights; tiled row i is W2[e, i].
+ * Tiled layout of one group (R tiled rows, C = cols): tiles of 32 rows x 64
+ * columns, tile (rb, ks) at byte offset (rb * C/64 + ks) * 2048 * wb (wb =
+ * bytes per weight); inside a tile, the 16 bytes at offset v*1024 + 16*l
+ * (l = 0..63, v = 0..32*wb/16 - 1) hold row 32rb + l%32, columns 64ks +
+ * 32*(l/32) + v*16/wb onwards. Groups follow each other.
+ * Routed experts: gate/up groups = E, rows = I, cols = d; down groups = E,
+ * rows = d, cols = I. Shared experts: groups = 1, rows = S*Is, cols = d
+ * (gate/up); rows = d, cols = S*Is (down).
+ * weight_dtype MOE_DTYPE_BF16 or MOE_DTYPE_FP8_E4M3 (else MOE_ERR_DTYPE);
+ * groups >= 1; rows a positive multiple of 32 (gate/up: of 16); cols a
+ * positive multiple of 64 (else MOE_ERR_SHAPE); src and dst must not
+ * overlap. */
+int moe_pack_weights(int which, int32_t groups, int32_t rows, int32_t cols, int32_t weight_dtype,
+                     const void* src_a, const void* src_b, void* dst, void* stream);
 
 /* ---- moe_route ------------------------------------------------------------
  * Gating of [DSMoE] section 2.1 with the bias of section 2.2 (eq. 16):
@@ -158,7 +196,8 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
  *   for row p of expert e, with slot f = perm_slot[p]:
  *     h = SiLU(W1_e x_perm[p]) * (W3_e x_perm[p])         (SiLU(z) = z*sigmoid(z))
  *     out_slots[f, :] = topk_gate[f] * (W2_e h)
- * w1, w3 [E, I, d]; w2 [E, d, I] in the weight dtype. For fp8 weights s1, s3
+ * w1, w3 [E, I, d]; w2 [E, d, I] in the weight dtype (MOE_LAYOUT_TILED:
+ * w1 and w2 from moe_pack_weights, w3 = NULL). For fp8 weights s1, s3
  * [E, I] and s2 [E, d] are the fp32 scales of each output row (the stored
  * code times the scale is the weight); they must be NULL otherwise.
  * x_perm, expert_offsets, perm_slot from moe_permute; topk_gate [T*K] from
@@ -176,7 +215,7 @@ int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* exp
  *   moe_expert_gate_up: h[p, :] = SiLU(W1_e x_perm[p]) * (W3_e x_perm[p])
  *   moe_expert_down:    out_slots[perm_slot[p], :] = topk_gate[perm_slot[p]]
  *                                                    * (W2_e h[p])
- * for every row p of expert e. h [T*K, I] act dtype. Scales as for
+ * for every row p of expert e. h [T*K, I] act dtype. Weights and scales as for
  * moe_expert_ffn (gate_up takes s1, s3; down takes s2). Workspace:
  * moe_workspace_size(cfg, MOE_WS_GEMM) bytes each. moe_expert_ffn is
  * exactly gate_up followed by down with h held in its workspace. */
@@ -192,7 +231,8 @@ int moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_
  * every token: y_shared[t] = sum_m W2s_m (SiLU(W1s_m x[t]) * (W3s_m x[t])).
  * The S experts are passed concatenated, which computes the same sum:
  * w1s, w3s [S*Is, d] (expert m = rows m*Is .. (m+1)*Is-1), w2s [d, S*Is]
- * (expert m = columns m*Is ..). fp8: s1s, s3s [S*Is] and s2s [d] row scales.
+ * (expert m = columns m*Is ..); MOE_LAYOUT_TILED: w1s and w2s packed with
+ * groups = 1, w3s = NULL. fp8: s1s, s3s [S*Is] and s2s [d] row scales.
  * x [T, d] act dtype; y_shared [T, d] fp32. Requires num_shared > 0.
  * Workspace: MOE_WS_SHARED bytes. */
 int moe_shared_ffn(const moe_config* cfg, const void* x, const void* w1s, const void* w3s,

@@ -19,9 +19,13 @@ from ._lib import (  # noqa: F401
     MOE_ERR_SHAPE,
     MOE_ERR_UNSUPPORTED,
     MOE_ERR_WORKSPACE,
+    MOE_LAYOUT_ROWS,
+    MOE_LAYOUT_TILED,
     MOE_NORM_NONE,
     MOE_NORM_SELECTED,
     MOE_OK,
+    MOE_PACK_DOWN,
+    MOE_PACK_GATE_UP,
     MOE_SCORE_SIGMOID,
     MOE_SCORE_SOFTMAX,
     MOE_WS_FFN,
@@ -39,11 +43,14 @@ from ._lib import (  # noqa: F401
     moe_expert_down,
     moe_expert_ffn,
     moe_expert_gate_up,
+    moe_pack_weights,
     moe_permute,
     moe_route,
     moe_shared_ffn,
     moe_status_string,
     moe_validate,
     moe_workspace_size,
+    pack_down,
+    pack_gate_up,
 )
 from .layer import MoELayer  # noqa: F401

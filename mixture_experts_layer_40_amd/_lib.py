@@ -33,6 +33,10 @@ MOE_NORM_NONE = 1
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_DTYPE_FP8_E4M3 = 2
+MOE_LAYOUT_ROWS = 0
+MOE_LAYOUT_TILED = 1
+MOE_PACK_GATE_UP = 0
+MOE_PACK_DOWN = 1
 MOE_WS_ROUTE = 0
 MOE_WS_PERMUTE = 1
 MOE_WS_FFN = 2
@@ -41,7 +45,7 @@ MOE_WS_GEMM = 4
 
 EXPORTED = ("moe_validate", "moe_workspace_size", "moe_status_string", "moe_route",
             "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
-            "moe_shared_ffn", "moe_combine", "moe_bias_update")
+            "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights")
 
 
 class MoEError(RuntimeError):
@@ -56,29 +60,31 @@ class moe_config(ctypes.Structure):
                 ("inter", ctypes.c_int32), ("num_shared", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("score_fn", ctypes.c_int32),
                 ("norm", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("weight_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("weight_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 _DT = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3}
 _SC = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
 _NO = {"selected": MOE_NORM_SELECTED, "none": MOE_NORM_NONE}
+_LA = {"rows": MOE_LAYOUT_ROWS, "tiled": MOE_LAYOUT_TILED}
 
 
 def make_config(T, d, E, K, I, S=0, Is=0, score="sigmoid", norm="selected", act_dtype="bf16",
-                weight_dtype="bf16", out_dtype="f32") -> moe_config:
+                weight_dtype="bf16", out_dtype="f32", weight_layout="rows") -> moe_config:
     return moe_config(int(T), int(d), int(E), int(K), int(I), int(S), int(Is),
                       _SC.get(score, score), _NO.get(norm, norm),
                       _DT.get(act_dtype, act_dtype), _DT.get(weight_dtype, weight_dtype),
-                      _DT.get(out_dtype, out_dtype))
+                      _DT.get(out_dtype, out_dtype), _LA.get(weight_layout, weight_layout))
 
 
-def config_of(spec, T: Optional[int] = None) -> moe_config:
+def config_of(spec, T: Optional[int] = None, weight_layout: str = "rows") -> moe_config:
     """moe_config from any object with the fields T, d, E, K, I, S, Is, score,
     norm, act_dtype, weight_dtype (and optionally out_dtype, default fp32),
     e.g. a workload description."""
     return make_config(spec.T if T is None else T, spec.d, spec.E, spec.K, spec.I, spec.S,
                        spec.Is, spec.score, spec.norm, spec.act_dtype, spec.weight_dtype,
-                       getattr(spec, "out_dtype", "f32"))
+                       getattr(spec, "out_dtype", "f32"), weight_layout)
 
 
 _lib = None
@@ -110,8 +116,10 @@ def load_library(path: str = LIB_PATH):
     lib.moe_shared_ffn.argtypes = [CFG, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_combine.argtypes = [CFG, P, P, P, P]
     lib.moe_bias_update.argtypes = [I32, P, ctypes.c_float, P, P]
+    lib.moe_pack_weights.argtypes = [ctypes.c_int, I32, I32, I32, I32, P, P, P, P]
     for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up",
-               "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update"):
+               "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update",
+               "moe_pack_weights"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -216,3 +224,28 @@ def moe_combine(cfg, out_slots, y_shared, y, stream=None):
 def moe_bias_update(num_experts, load, gamma, bias, stream=None):
     _check("moe_bias_update", load_library().moe_bias_update(
         int(num_experts), _ptr(load), float(gamma), _ptr(bias), _stream(stream)))
+
+
+def moe_pack_weights(which, groups, rows, cols, weight_dtype, src_a, src_b, dst, stream=None):
+    _check("moe_pack_weights", load_library().moe_pack_weights(
+        int(which), int(groups), int(rows), int(cols), _DT.get(weight_dtype, weight_dtype),
+        _ptr(src_a), _ptr(src_b), _ptr(dst), _stream(stream)))
+
+
+def pack_gate_up(w1, w3, weight_dtype, stream=None):
+    """Tiled gate/up tensor of W1, W3 [G, N, C] (or [N, C]): a new uint8/bf16
+    tensor of 2*G*N*C weights in the layout moe_pack_weights documents."""
+    G = w1.shape[0] if w1.dim() == 3 else 1
+    N, C = w1.shape[-2], w1.shape[-1]
+    dst = torch.empty((G, 2 * N, C), dtype=w1.dtype, device=w1.device)
+    moe_pack_weights(MOE_PACK_GATE_UP, G, N, C, weight_dtype, w1, w3, dst, stream)
+    return dst
+
+
+def pack_down(w2, weight_dtype, stream=None):
+    """Tiled down tensor of W2 [G, N, C] (or [N, C])."""
+    G = w2.shape[0] if w2.dim() == 3 else 1
+    N, C = w2.shape[-2], w2.shape[-1]
+    dst = torch.empty((G, N, C), dtype=w2.dtype, device=w2.device)
+    moe_pack_weights(MOE_PACK_DOWN, G, N, C, weight_dtype, w2, None, dst, stream)
+    return dst

@@ -27,6 +27,15 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 bool is_fp8(const moe_config* c) { return c->weight_dtype == MOE_DTYPE_FP8_E4M3; }
 
+bool is_tiled(const moe_config* c) { return c->weight_layout == MOE_LAYOUT_TILED; }
+
+// The second gate/up weight pointer: required in the rows layout, NULL in the
+// tiled one (its rows live in the tiled gate/up tensor).
+int check_w3(const moe_config* c, const void* w3) {
+  if (is_tiled(c)) return w3 ? MOE_ERR_SHAPE : MOE_OK;
+  return w3 ? MOE_OK : MOE_ERR_NULL;
+}
+
 // fp8 weights need all three scale arrays; other weight types take none.
 int check_scales(const moe_config* c, const float* a, const float* b, const float* d) {
   if (is_fp8(c)) return (a && b && d) ? MOE_OK : MOE_ERR_NULL;
@@ -46,6 +55,10 @@ int moe_validate(const moe_config* c) {
     return MOE_ERR_DTYPE;
   if (c->out_dtype != MOE_DTYPE_F32 && c->out_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (c->act_dtype == MOE_DTYPE_F32 && c->out_dtype != MOE_DTYPE_F32) return MOE_ERR_DTYPE;
+  if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_TILED)
+    return MOE_ERR_SHAPE;
+  if (c->weight_layout == MOE_LAYOUT_TILED && c->weight_dtype == MOE_DTYPE_F32)
+    return MOE_ERR_DTYPE;
   if (c->score_fn != MOE_SCORE_SIGMOID && c->score_fn != MOE_SCORE_SOFTMAX) return MOE_ERR_SHAPE;
   if (c->norm != MOE_NORM_SELECTED && c->norm != MOE_NORM_NONE) return MOE_ERR_SHAPE;
   if (c->num_tokens < 0) return MOE_ERR_SHAPE;
@@ -88,6 +101,21 @@ const char* moe_status_string(int status) {
   }
 }
 
+int moe_pack_weights(int which, int32_t groups, int32_t rows, int32_t cols, int32_t weight_dtype,
+                     const void* src_a, const void* src_b, void* dst, void* stream) {
+  if (which != MOE_PACK_GATE_UP && which != MOE_PACK_DOWN) return MOE_ERR_SHAPE;
+  if (weight_dtype != MOE_DTYPE_BF16 && weight_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_DTYPE;
+  if (groups < 1 || rows < 1 || cols < 1 || cols % 64 != 0) return MOE_ERR_SHAPE;
+  if (rows % (which == MOE_PACK_GATE_UP ? 16 : 32) != 0) return MOE_ERR_SHAPE;
+  if (!src_a || !dst) return MOE_ERR_NULL;
+  if (which == MOE_PACK_GATE_UP ? !src_b : src_b != nullptr)
+    return which == MOE_PACK_GATE_UP ? MOE_ERR_NULL : MOE_ERR_SHAPE;
+  const int wbytes = weight_dtype == MOE_DTYPE_BF16 ? 2 : 1;
+  (void)hipGetLastError();
+  return from_hip(launch_pack(which == MOE_PACK_GATE_UP ? 0 : 1, groups, rows, cols, wbytes, src_a,
+                              src_b, dst, as_stream(stream)));
+}
+
 int moe_route(const moe_config* c, const void* x, const void* w_router, const float* bias,
               int32_t* topk_idx, float* topk_gate, int32_t* load, void* ws, size_t ws_bytes,
               void* stream) {
@@ -122,7 +150,8 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   if (st != MOE_OK) return st;
   if ((st = check_scales(c, s1, s3, s2)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
-  if (!x_perm || !expert_offsets || !perm_slot || !topk_gate || !w1 || !w3 || !w2 || !out_slots)
+  if ((st = check_w3(c, w3)) != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !perm_slot || !topk_gate || !w1 || !w2 || !out_slots)
     return MOE_ERR_NULL;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_FFN), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
@@ -137,7 +166,8 @@ int moe_expert_gate_up(const moe_config* c, const void* x_perm, const int32_t* e
   if (st != MOE_OK) return st;
   if ((st = check_scales(c, s1, s3, s3)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
-  if (!x_perm || !expert_offsets || !w1 || !w3 || !h) return MOE_ERR_NULL;
+  if ((st = check_w3(c, w3)) != MOE_OK) return st;
+  if (!x_perm || !expert_offsets || !w1 || !h) return MOE_ERR_NULL;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_gate_up(*c, x_perm, expert_offsets, w1, w3, s1, s3, h, ws,
@@ -166,7 +196,8 @@ int moe_shared_ffn(const moe_config* c, const void* x, const void* w1s, const vo
   if (c->num_shared == 0) return MOE_ERR_SHAPE;
   if ((st = check_scales(c, s1s, s3s, s2s)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
-  if (!x || !w1s || !w3s || !w2s || !y_shared) return MOE_ERR_NULL;
+  if ((st = check_w3(c, w3s)) != MOE_OK) return st;
+  if (!x || !w1s || !w2s || !y_shared) return MOE_ERR_NULL;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_SHARED), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_shared_ffn(*c, x, w1s, w3s, w2s, s1s, s3s, s2s, y_shared, ws,

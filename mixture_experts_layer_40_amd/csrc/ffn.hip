@@ -8,27 +8,32 @@
 // concatenated (W1, W3 stacked by rows, W2 by columns), which is the same sum.
 //
 // CDNA4 design (bf16 / fp8 weights):
-//  * Orientation: weight rows are the first MFMA operand, token rows the
-//    second. A block computes 256 weight rows x up to 128 tokens of one
-//    expert; each of its 4 waves owns 64 weight rows and all tokens of the
-//    tile. Weight rows are never shared between waves, so every wave streams
-//    its rows straight from HBM into MFMA operand registers (fp8 codes are
-//    widened to bf16 in registers, exactly); only the token tile, which all
-//    4 waves read, is staged through LDS (double buffered; 16-byte chunks
+//  * Orientation: weight rows are the first MFMA operand (v_mfma 32x32x16),
+//    token rows the second. A block (8 waves, two per SIMD) computes 256
+//    weight rows x up to 256 tokens of one expert; each wave owns one 32-row
+//    weight fragment and all tokens of the tile. Weight rows are never shared
+//    between waves, so every wave streams its rows from HBM straight into
+//    MFMA operand registers, two stages ahead (fp8 codes are widened to bf16
+//    in registers, exactly). In the tiled weight layout each of those loads
+//    reads a whole 1 KB stripe.
+//  * The token tile, which all 8 waves read, goes global -> LDS by direct
+//    LDS loads (no registers), three stages deep; 16-byte chunks are
 //    XOR-swizzled by row pair so the 16 rows one ds_read_b128 serves land on
-//    16 distinct groups of the 64 banks: conflict-free reads and writes).
-//  * Skew: token fragments of 16 beyond an expert's row count are skipped, so
-//    an expert with 3 rows costs one fragment of MFMA work while its weights
-//    are still read exactly once per token tile.
+//    16 distinct groups of the 64 banks.
+//  * Skew: the K loop is specialised on the number of 32-token fragments a
+//    tile really has, so an expert with 3 rows costs one fragment of MFMA
+//    work while its weights are still read exactly once per token tile.
 //  * Tiles are ordered (expert, weight block, token block) with the token
 //    block fastest and dealt to XCDs in contiguous ranges, so the token tiles
 //    that share a weight block run together on one XCD and its L2.
-//  * Gate/up: the 64 rows of a wave are 32 gate (W1) rows and the 32 up (W3)
-//    rows of the same intermediate columns, so SiLU(g) * u is formed in
-//    registers and H is written once in bf16.
+//  * Gate/up: a wave's 32 rows are 16 gate (W1) rows and the 16 up (W3) rows
+//    of the same intermediate columns, so SiLU(g) * u is formed in registers
+//    and H is written once in bf16.
 //  * Down: the epilogue multiplies by the fp8 row scale and the token's gate
 //    and writes the row straight to its (token, slot) position.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -63,6 +68,7 @@ struct GemmArgs {
   const float* gate;          // down: gate per output row (null = 1)
   void* out;                  // down output [slots, n]
   int out_f32;                // down output is fp32 (else the activation dtype)
+  int tiled;                  // weights in the tiled layout (wa only; see pack_tiles)
 };
 
 struct Tile {
@@ -122,50 +128,84 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 512;
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+typedef __attribute__((address_space(1))) void glb_ptr_t;
+
+// One 16-byte global -> LDS copy per lane, bypassing registers: lane l of the
+// wave writes its 16 bytes at lds_wave_base + 16 * l.
+__device__ __forceinline__ void dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t*)src, (lds_ptr_t*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool FP8, int NSA, int BM>
 struct MainLoop {
   static constexpr int AW = FP8 ? 2 : 4;       // 16-byte loads per fragment per stage
   static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
+  static constexpr int ND = 3;                 // LDS token stages (two in flight)
+  static constexpr int U = ND * NSA / (NSA % ND == 0 ? ND : 1);  // unroll: lcm(ND, NSA)
 
   // acc[t] += W fragment x token fragment t, over the whole K axis. Every
-  // load, LDS write and MFMA is unconditional: token rows past the expert's
-  // end read its last row, prefetches past the last stage re-read the last
-  // stage, and when a stage has fewer 16-byte chunks than threads the extra
-  // threads repeat a chunk (writing the same bytes to the same place).
+  // load and MFMA is unconditional: token rows past the expert's end read
+  // its last row, prefetches past the last stage re-read the last stage, and
+  // when a stage has fewer 16-byte chunks than threads the extra threads
+  // repeat a chunk (writing the same bytes to the same place).
   template <int NT>
   __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
-                                             int mvalid, int kdim, uint16_t* bs,
-                                             f32x16 (&acc)[BM / 32]) {
+                                             int mvalid, int kdim, int astage, int avs,
+                                             uint16_t* bs0, uint16_t* bs1,
+                                             uint16_t* bs2, f32x16 (&acc)[BM / 32]) {
     constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
-    constexpr int BCH = (CH + kThreads - 1) / kThreads; // per thread
-    const int tid = threadIdx.x, l = lane_id(), g = l >> 5, r32 = l & 31;
+    constexpr int BCH = (CH + kThreads - 1) / kThreads; // copies per thread per stage
+    const int l = lane_id(), g = l >> 5, r32 = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int nk = kdim / 64;
 
+    // Copy i of a wave fills 64 consecutive 16-byte LDS slots starting at
+    // slot q0; slot q holds token row q/8, physical chunk q%8, which carries
+    // the logical K-chunk (q%8) ^ ((row/2)%8).
     const uint16_t* bsrc[BCH];
     int bdst[BCH];
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-      const int q = (tid + kThreads * i) % CH;
-      const int row = q >> 3, ch = q & 7;
+      const int q0 = (w * kWave + kThreads * i) % CH;
+      const int q = q0 + l, row = q >> 3, ch = (q & 7) ^ ((row >> 1) & 7);
       const int src_row = row < mvalid ? row : mvalid - 1;
       bsrc[i] = act + static_cast<size_t>(row0 + src_row) * kdim + ch * 8;
-      bdst[i] = row * 64 + ((ch ^ ((row >> 1) & 7)) * 8);
+      bdst[i] = q0 * 8;
     }
 
     u32x4 ra[NSA][AW];
-    u32x4 rb[BCH];
+    // This lane's AW 16-byte pieces of K stage ks: at aptr + ks * astage +
+    // v * avs (rows layout: 16 consecutive bytes of its row; tiled layout:
+    // one 1 KB stripe per piece, so each load instruction reads 1 KB).
     auto load_a = [&](u32x4 (&dst)[AW], int ks) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(aptr + static_cast<size_t>(ks) * 64 * WB);
+      const uint8_t* p = aptr + static_cast<size_t>(ks) * astage;
 #pragma unroll
-      for (int v = 0; v < AW; ++v) dst[v] = p[v];
+      for (int v = 0; v < AW; ++v) dst[v] = *reinterpret_cast<const u32x4*>(p + v * avs);
     };
-    auto load_b = [&](int ks) {
+    auto load_b = [&](uint16_t* buf, int ks) {
 #pragma unroll
-      for (int i = 0; i < BCH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bsrc[i] + ks * 64);
-    };
-    auto store_b = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < BCH; ++i) *reinterpret_cast<u32x4*>(bs + buf * (BM * 64) + bdst[i]) = rb[i];
+      for (int i = 0; i < BCH; ++i) dma16(bsrc[i] + ks * 64, buf + bdst[i]);
     };
     auto read_b = [&](u32x4& dst, const uint16_t* b0, int t, int s) {
       const int tok = 32 * t + r32, ch = 4 * g + s;
@@ -173,8 +213,7 @@ struct MainLoop {
     };
     // One 64-wide K stage: four MFMA steps. Fragment t of step s+1 is read
     // from LDS just before the MFMA of fragment t of step s (order pinned).
-    auto compute = [&](const u32x4 (&src)[AW], int buf) {
-      const uint16_t* b0 = bs + buf * (BM * 64);
+    auto compute = [&](const u32x4 (&src)[AW], const uint16_t* b0) {
       u32x4 bfr[2][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) read_b(bfr[0][t], b0, t, 0);
@@ -196,35 +235,59 @@ struct MainLoop {
         }
       }
     };
+    auto buf = [&](int i) { return i == 0 ? bs0 : (i == 1 ? bs1 : bs2); };
 
-    load_b(0);
+    // Issue order (the counter waits below depend on it): prologue
+    // T(0), T(1), W(0) .. W(NSA-2); stage s: T(s+2), W(s+NSA-1).
+    load_b(bs0, 0);
+    load_b(bs1, min(1, nk - 1));
 #pragma unroll
     for (int p = 0; p < NSA - 1; ++p) load_a(ra[p], min(p, nk - 1));
-    store_b(0);
-    __syncthreads();
-    for (int base = 0; base < nk; base += NSA) {
-#pragma unroll
-      for (int u = 0; u < NSA; ++u) {
-        const int s = base + u;
-        if (s >= nk) break;
-        // tokens first: waiting for them before the LDS write leaves the
-        // later-issued weight prefetches in flight
-        load_b(min(s + 1, nk - 1));
-        load_a(ra[(u + NSA - 1) % NSA], min(s + NSA - 1, nk - 1));
-        __builtin_amdgcn_sched_barrier(0);   // keep the requests ahead of the multiply
-        compute(ra[u], s & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        store_b((s + 1) & 1);                // the other buffer: its readers passed the barrier
-        __syncthreads();
-      }
+    __builtin_amdgcn_sched_barrier(0);
+    // Everything of the prologue landed. T(1) and the first weights were
+    // requested together with T(0), so this costs little more than waiting
+    // for T(0), and it leaves the K loop one clean state to carry (with
+    // requests of the prologue still counted, the compiler's own waits at
+    // the loop head fall back to draining every request each iteration).
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    // One K stage s; u = s mod U fixes its LDS buffer and ring slot at
+    // compile time.
+    auto stage = [&](auto uc, int s) {
+      constexpr int u = decltype(uc)::value;
+      load_b(buf((u + 2) % ND), min(s + 2, nk - 1));   // its readers passed the last barrier
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(ra[(u + NSA - 1) % NSA], min(s + NSA - 1, nk - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      // W(s) landed: after it were issued T and W of each of NSA-1 stages
+      wait_vmcnt<(NSA - 1) * (AW + BCH)>();
+      compute(ra[u % NSA], buf(u % ND));
+      __builtin_amdgcn_sched_barrier(0);
+      // T(s+1) landed: after it were issued at most W, T(s+2), W. A plain
+      // barrier: the fence of __syncthreads would wait for every copy in
+      // flight; this stage's LDS reads are complete, their MFMAs issued.
+      wait_vmcnt<2 * AW + BCH>();
+      __builtin_amdgcn_s_barrier();
+    };
+    // Whole groups of U stages, then the remainder, outside the loop so the
+    // loop carries one pipeline state (a break inside it would merge the
+    // states of every stage into the loop head and force full drains).
+    const int full = nk - nk % U;
+    for (int base = 0; base < full; base += U) {
+      static_for<U>([&](auto uc) { stage(uc, base + decltype(uc)::value); });
     }
+    static_for<U - 1>([&](auto uc) {
+      if (full + decltype(uc)::value < nk) stage(uc, full + decltype(uc)::value);
+    });
   }
 };
 
 template <int MODE, bool FP8, int BM, int NSA, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   constexpr int NTF = BM / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2 * BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs0[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs1[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs2[BM * 64];
 
   Tile tl;
   if (!decode_tile<GROUPED>(a, BM, tl)) return;
@@ -233,20 +296,31 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   const int ntf = (tl.mvalid + 31) >> 5;
 
   // ---- this wave's 32-row weight fragment ----
+  // Rows layout: lane l reads row (l % 32) of the fragment, K-elements
+  // 32g .. 32g+31 of each 64-wide stage (g = l / 32), 16 bytes at a time.
+  // Tiled layout: fragment rb, stage ks is one contiguous tile of 32 x 64
+  // weights; lane l's piece v sits at byte v * 1024 + 16 l of it.
   int nrow0;        // gate/up: first of 16 intermediate columns; down: first of 32 rows
   bool wvalid;
   const uint8_t* aptr;
-  constexpr size_t wbytes = FP8 ? 1 : 2;
-  if (MODE == kGateUp) {
-    nrow0 = tl.nblk * kBNGate + 16 * w;
-    wvalid = nrow0 < a.n;
-    const int row = (wvalid ? nrow0 : 0) + (r32 & 15);
+  constexpr int wbytes = FP8 ? 1 : 2;
+  const int nk = a.kdim / 64;
+  int astage = 64 * wbytes, avs = 16;
+  const int rb = (MODE == kGateUp ? tl.nblk * kBNGate / 16 : tl.nblk * kBNDown / 32) + w;
+  nrow0 = MODE == kGateUp ? 16 * rb : 32 * rb;
+  wvalid = nrow0 < a.n;
+  const int rbv = wvalid ? rb : 0;
+  if (a.tiled) {
+    astage = 32 * 64 * wbytes;
+    avs = 1024;
+    aptr = static_cast<const uint8_t*>(a.wa) + static_cast<size_t>(tl.e) * a.wstride * wbytes +
+           static_cast<size_t>(rbv) * nk * astage + 16 * l;
+  } else if (MODE == kGateUp) {
+    const int row = 16 * rbv + (r32 & 15);
     aptr = static_cast<const uint8_t*>(r32 < 16 ? a.wa : a.wb) +
            (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
   } else {
-    nrow0 = tl.nblk * kBNDown + 32 * w;
-    wvalid = nrow0 < a.n;
-    const int row = (wvalid ? nrow0 : 0) + r32;
+    const int row = 32 * rbv + r32;
     aptr = static_cast<const uint8_t*>(a.wa) +
            (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
   }
@@ -259,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   using ML = MainLoop<FP8, NSA, BM>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
-    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, tl.mvalid, a.kdim, bs, acc); break;
+    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, acc); break;
     MOE_NT_CASE(1) MOE_NT_CASE(2) MOE_NT_CASE(3) MOE_NT_CASE(4)
     MOE_NT_CASE(5) MOE_NT_CASE(6) MOE_NT_CASE(7) MOE_NT_CASE(8)
 #undef MOE_NT_CASE
@@ -409,6 +483,49 @@ __global__ __launch_bounds__(256) void ffn_schedule(const int32_t* __restrict__ 
   if (tid == 0) sched[E] = sc[255];
 }
 
+// Rows -> tiled weight layout (a pure relocation of 16-byte pieces).
+// Tiled matrix of a group: R rows x C columns (R % 32 == 0, C % 64 == 0),
+// cut into tiles of 32 rows x 64 columns, tile (rb, ks) at index rb*C/64+ks,
+// each AW*1024 bytes (AW = 64 * wbytes / 32). Piece v of lane l in a tile
+// holds row 32rb + l%32, columns 64ks + 32(l/32) + v*(16/wbytes) onwards,
+// at byte v*1024 + 16l. interleave: row 32rb + r of the tiled matrix is
+// row 16rb + r of `a` for r < 16 and row 16rb + r - 16 of `b` otherwise
+// (gate and up rows of the same 16 intermediate columns in one tile);
+// else it is row 32rb + r of `a`.
+__global__ __launch_bounds__(256) void pack_tiles(const uint8_t* __restrict__ a,
+                                                  const uint8_t* __restrict__ b,
+                                                  uint8_t* __restrict__ dst, int64_t groups,
+                                                  int rows_out, int cols, int wbytes,
+                                                  int interleave) {
+  const int aw = 64 * wbytes / 32;
+  const int nk = cols / 64;
+  const int64_t row_bytes = static_cast<int64_t>(cols) * wbytes;
+  const int64_t src_group = static_cast<int64_t>(interleave ? rows_out / 2 : rows_out) * row_bytes;
+  const int64_t per_group = static_cast<int64_t>(rows_out) * row_bytes / 16;
+  const int64_t total = groups * per_group;
+  for (int64_t o = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; o < total;
+       o += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e = o / per_group, local = o % per_group;
+    const int64_t tile = local / (aw * 64);
+    const int within = static_cast<int>(local % (aw * 64));
+    const int v = within / 64, lane = within % 64;
+    const int rb = static_cast<int>(tile / nk), ks = static_cast<int>(tile % nk);
+    const int rr = lane % 32, gg = lane / 32;
+    const uint8_t* src;
+    int64_t row;
+    if (interleave) {
+      src = rr < 16 ? a : b;
+      row = 16LL * rb + (rr & 15);
+    } else {
+      src = a;
+      row = 32LL * rb + rr;
+    }
+    const int64_t col_byte = (64LL * ks + 32 * gg) * wbytes + 16LL * v;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(src + e * src_group + row * row_bytes + col_byte);
+    *reinterpret_cast<u32x4*>(dst + o * 16) = val;
+  }
+}
+
 int64_t grid_for(int64_t max_tiles) {
   const int64_t per = (max_tiles + kNumXcd - 1) / kNumXcd;
   return per * kNumXcd;
@@ -431,10 +548,10 @@ int pick_bm(int64_t rows_per_group) {
 template <int MODE, bool FP8, bool GROUPED>
 void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
 #ifndef MOE_NS_BIG
-#define MOE_NS_BIG 2
+#define MOE_NS_BIG 3
 #endif
 #ifndef MOE_NS_SMALL
-#define MOE_NS_SMALL 4
+#define MOE_NS_SMALL 3
 #endif
   constexpr int NS_BIG = MOE_NS_BIG;
   constexpr int NS_SMALL = MOE_NS_SMALL;
@@ -513,7 +630,9 @@ hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t
   GemmArgs g{};
   g.act = x_perm; g.wa = w1; g.wb = w3; g.sa = s1; g.sb = s3;
   g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
-  g.kdim = d; g.n = I; g.nb = b.nb1; g.wstride = static_cast<int64_t>(I) * d; g.h = h;
+  g.kdim = d; g.n = I; g.nb = b.nb1; g.h = h;
+  g.tiled = c.weight_layout == MOE_LAYOUT_TILED;
+  g.wstride = static_cast<int64_t>(I) * d * (g.tiled ? 2 : 1);
   return run_gemm(kGateUp, f32, fp8, b.bm, g, ((TK + b.bm - 1) / b.bm + E) * b.nb1, s);
 }
 
@@ -534,6 +653,7 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert
   g.act = h; g.wa = w2; g.sa = s2;
   g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
   g.kdim = I; g.n = d; g.nb = b.nb2; g.wstride = static_cast<int64_t>(d) * I;
+  g.tiled = c.weight_layout == MOE_LAYOUT_TILED;
   g.perm_slot = perm_slot; g.gate = topk_gate; g.out = out_slots;
   return run_gemm(kDown, f32, fp8, b.bm, g, ((TK + b.bm - 1) / b.bm + E) * b.nb2, s);
 }
@@ -565,6 +685,7 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
   g1.act = x; g1.wa = w1s; g1.wb = w3s; g1.sa = s1s; g1.sb = s3s;
   g1.offsets = nullptr; g1.sched = nullptr; g1.fixed_m = T; g1.E = 1;
   g1.kdim = d; g1.n = SI; g1.nb = b.nb1; g1.wstride = 0; g1.h = ws;
+  g1.tiled = c.weight_layout == MOE_LAYOUT_TILED;
   hipError_t err = run_gemm(kGateUp, f32, fp8, b.bm, g1, mt * b.nb1, s);
   if (err != hipSuccess) return err;
 
@@ -573,7 +694,21 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
   g2.offsets = nullptr; g2.sched = nullptr; g2.fixed_m = T; g2.E = 1;
   g2.kdim = SI; g2.n = d; g2.nb = b.nb2; g2.wstride = 0;
   g2.perm_slot = nullptr; g2.gate = nullptr; g2.out = y_shared; g2.out_f32 = 1;
+  g2.tiled = c.weight_layout == MOE_LAYOUT_TILED;
   return run_gemm(kDown, f32, fp8, b.bm, g2, mt * b.nb2, s);
+}
+
+hipError_t launch_pack(int which, int64_t groups, int rows, int cols, int wbytes,
+                       const void* a, const void* b, void* dst, hipStream_t s) {
+  const int interleave = which == 0;
+  const int rows_out = interleave ? 2 * rows : rows;
+  const int64_t total = groups * rows_out * static_cast<int64_t>(cols) * wbytes / 16;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(pack_tiles, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(a), static_cast<const uint8_t*>(b),
+                     static_cast<uint8_t*>(dst), groups, rows_out, cols, wbytes, interleave);
+  return hipGetLastError();
 }
 
 }  // namespace moe

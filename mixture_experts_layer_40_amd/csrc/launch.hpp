@@ -47,6 +47,11 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
                              const float* s3s, const float* s2s, void* y_shared, void* ws,
                              hipStream_t s);
 
+// Rows -> tiled layout of expert weights. which: 0 = gate/up (a = W1, b = W3,
+// each [groups, rows, cols]), 1 = down (a = W2 [groups, rows, cols], b unused).
+hipError_t launch_pack(int which, int64_t groups, int rows, int cols, int wbytes,
+                       const void* a, const void* b, void* dst, hipStream_t s);
+
 // ---- combine / bias ----------------------------------------------------------
 hipError_t launch_combine(const moe_config& c, const void* out_slots, const void* y_shared,
                           void* y, hipStream_t s);

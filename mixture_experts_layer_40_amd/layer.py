@@ -2,7 +2,10 @@
 
 MoELayer keeps the weights the caller hands it (torch tensors on the GPU, in
 their stored formats) and allocates every intermediate buffer once, sized
-for `max_tokens`. forward() enqueues
+for `max_tokens`. With layout="tiled" (the default for bf16 / fp8 weights)
+it relocates the expert weights once into the tiled layout of
+moe_pack_weights and keeps only that copy's references for the calls.
+forward() enqueues
 
     moe_shared_ffn (second stream)  ||  moe_route -> moe_permute -> moe_expert_ffn
     -> join -> moe_combine
@@ -25,13 +28,25 @@ _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 class MoELayer:
     def __init__(self, spec, weights: dict, max_tokens: Optional[int] = None,
-                 shared_stream: bool = True, device=None):
+                 shared_stream: bool = True, device=None, layout: Optional[str] = None):
         self.spec = spec
-        self.w = weights
         self.device = torch.device(device) if device is not None else weights["wr"].device
         self.max_tokens = spec.T if max_tokens is None else max_tokens
         self.act = _TORCH_DT[spec.act_dtype]
-        self.cfg_max = L.config_of(spec, T=self.max_tokens)
+        if layout is None:
+            layout = "rows" if spec.weight_dtype == "f32" else "tiled"
+        self.layout = layout
+        self.w = dict(weights)
+        if layout == "tiled":
+            wd = spec.weight_dtype
+            self.w["w1"] = L.pack_gate_up(weights["w1"], weights["w3"], wd)
+            self.w["w3"] = None
+            self.w["w2"] = L.pack_down(weights["w2"], wd)
+            if spec.S > 0:
+                self.w["w1s"] = L.pack_gate_up(weights["w1s"], weights["w3s"], wd)
+                self.w["w3s"] = None
+                self.w["w2s"] = L.pack_down(weights["w2s"], wd)
+        self.cfg_max = L.config_of(spec, T=self.max_tokens, weight_layout=layout)
         st = L.moe_validate(self.cfg_max)
         if st != L.MOE_OK:
             raise L.MoEError("MoELayer", st, L.moe_status_string(st))
@@ -59,7 +74,7 @@ class MoELayer:
     def _cfg(self, T):
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens exceed the layer's buffers ({self.max_tokens})")
-        return L.config_of(self.spec, T=T)
+        return L.config_of(self.spec, T=T, weight_layout=self.layout)
 
     def route(self, x, bias=None):
         T = x.shape[0]

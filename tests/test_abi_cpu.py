@@ -62,6 +62,8 @@ def test_validate_accepts_named_workload_shapes():
     (dict(out_dtype="bf16"), L.MOE_ERR_DTYPE),  # fp32 activations need an fp32 output
     (dict(out_dtype="fp8"), L.MOE_ERR_DTYPE),
     (dict(act_dtype="bf16", weight_dtype="bf16", out_dtype=5), L.MOE_ERR_DTYPE),
+    (dict(weight_layout=7), L.MOE_ERR_SHAPE),
+    (dict(weight_layout="tiled"), L.MOE_ERR_DTYPE),   # fp32 weights have no tiled form
 ])
 def test_validate_rejects(kw, status):
     assert moe.moe_validate(_cfg(**kw)) == status
@@ -123,6 +125,35 @@ def test_entry_points_reject_before_any_device_call():
     assert lib.moe_bias_update(8, None, ctypes.c_float(1e-3), fake, None) == L.MOE_ERR_NULL
     assert lib.moe_bias_update(8, fake, ctypes.c_float(-1.0), fake, None) == L.MOE_ERR_SHAPE
     assert lib.moe_bias_update(8, fake, ctypes.c_float(float("nan")), fake, None) == L.MOE_ERR_SHAPE
+
+
+def test_tiled_layout_and_pack_validation():
+    lib = moe.load_library()
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    by = ctypes.byref
+    for wd in ("bf16", "fp8"):
+        assert moe.moe_validate(_cfg(act_dtype="bf16", weight_dtype=wd, weight_layout="tiled")) == L.MOE_OK
+    t = _cfg(act_dtype="bf16", weight_dtype="bf16", weight_layout="tiled")
+    r = _cfg(act_dtype="bf16", weight_dtype="bf16")
+    # the tiled layout takes the gate/up tensor in w1 and no w3; the rows layout needs w3
+    assert lib.moe_expert_ffn(by(t), *[fake] * 5, fake, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_expert_ffn(by(r), *[fake] * 5, None, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_NULL
+    assert lib.moe_expert_gate_up(by(t), fake, fake, fake, fake, None, None, fake, fake, 1 << 20, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_shared_ffn(by(t), fake, fake, fake, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_shared_ffn(by(r), fake, fake, None, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_NULL
+    pk = lib.moe_pack_weights
+    G, UP, DN = L.MOE_PACK_GATE_UP, L.MOE_PACK_GATE_UP, L.MOE_PACK_DOWN
+    assert pk(2, 1, 32, 64, L.MOE_DTYPE_BF16, fake, None, fake, None) == L.MOE_ERR_SHAPE
+    assert pk(DN, 1, 32, 64, L.MOE_DTYPE_F32, fake, None, fake, None) == L.MOE_ERR_DTYPE
+    assert pk(DN, 1, 16, 64, L.MOE_DTYPE_BF16, fake, None, fake, None) == L.MOE_ERR_SHAPE   # 32-row tiles
+    assert pk(DN, 1, 32, 96, L.MOE_DTYPE_BF16, fake, None, fake, None) == L.MOE_ERR_SHAPE   # 64-column tiles
+    assert pk(UP, 1, 8, 64, L.MOE_DTYPE_BF16, fake, fake, fake, None) == L.MOE_ERR_SHAPE
+    assert pk(DN, 0, 32, 64, L.MOE_DTYPE_BF16, fake, None, fake, None) == L.MOE_ERR_SHAPE
+    assert pk(UP, 1, 16, 64, L.MOE_DTYPE_BF16, fake, None, fake, None) == L.MOE_ERR_NULL    # W3 missing
+    assert pk(DN, 1, 32, 64, L.MOE_DTYPE_BF16, fake, fake, fake, None) == L.MOE_ERR_SHAPE   # down takes one source
+    assert pk(DN, 1, 32, 64, L.MOE_DTYPE_FP8_E4M3, None, None, fake, None) == L.MOE_ERR_NULL
+    assert G == 0
 
 
 def test_zero_tokens_is_a_noop_without_device_work():
