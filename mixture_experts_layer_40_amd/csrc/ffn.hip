@@ -96,12 +96,16 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
     rbeg = a.offsets[e];
     m = a.offsets[e + 1] - rbeg;
   }
+  // An expert's rows are split into mt = ceil(m / bm) tiles of nearly equal
+  // size (multiples of 32 rows): the tiles that share a weight block then
+  // run for about as long, in step, and the later ones find its lines in L2.
   const int mt = (m + bm - 1) / bm;
   const int mb = local % mt;
+  const int per = (((m + mt - 1) / mt) + 31) & ~31;
   t.e = e;
   t.nblk = local / mt;
-  t.row0 = rbeg + mb * bm;
-  t.mvalid = min(bm, m - mb * bm);
+  t.row0 = rbeg + mb * per;
+  t.mvalid = min(per, m - mb * per);
   return true;
 }
 
