@@ -217,7 +217,11 @@ struct MainLoop {
     };
     // One 64-wide K stage: four MFMA steps. Fragment t of step s+1 is read
     // from LDS just before the MFMA of fragment t of step s (order pinned).
-    auto compute = [&](const u32x4 (&src)[AW], const uint16_t* b0) {
+    // The stage's NV memory requests (issue(0 .. NV-1)) are spread evenly
+    // over its 4*NT MFMAs: issued in one burst they queue at the CU's
+    // address unit and hold every wave's MFMAs back behind them.
+    constexpr int NV = BCH + AW;
+    auto compute = [&](const u32x4 (&src)[AW], const uint16_t* b0, auto&& issue) {
       u32x4 bfr[2][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) read_b(bfr[0][t], b0, t, 0);
@@ -235,6 +239,11 @@ struct MainLoop {
         for (int t = 0; t < NT; ++t) {
           if (s < 3) read_b(bfr[(s + 1) & 1][t], b0, t, s + 1);
           acc[t] = mfma_32x32x16(op, bfr[s & 1][t], acc[t]);
+          const int i = s * NT + t;
+          static_for<NV>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if ((k * 4 * NT) / NV == i) issue(kc);
+          });
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -259,13 +268,19 @@ struct MainLoop {
     // compile time.
     auto stage = [&](auto uc, int s) {
       constexpr int u = decltype(uc)::value;
-      load_b(buf((u + 2) % ND), min(s + 2, nk - 1));   // its readers passed the last barrier
-      __builtin_amdgcn_sched_barrier(0);
-      load_a(ra[(u + NSA - 1) % NSA], min(s + NSA - 1, nk - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      // W(s) landed: after it were issued T and W of each of NSA-1 stages
-      wait_vmcnt<(NSA - 1) * (AW + BCH)>();
-      compute(ra[u % NSA], buf(u % ND));
+      uint16_t* tdst = buf((u + 2) % ND);               // its readers passed the last barrier
+      const int ts = min(s + 2, nk - 1);
+      u32x4 (&wdst)[AW] = ra[(u + NSA - 1) % NSA];      // consumed in the previous stage
+      const uint8_t* wsrc = aptr + static_cast<size_t>(min(s + NSA - 1, nk - 1)) * astage;
+      // requests 0 .. BCH-1: T(s+2); BCH .. NV-1: W(s+NSA-1)
+      auto issue = [&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < BCH) dma16(bsrc[k] + ts * 64, tdst + bdst[k]);
+        else wdst[k - BCH] = *reinterpret_cast<const u32x4*>(wsrc + (k - BCH) * avs);
+      };
+      // W(s) landed: after its last piece came the NV requests of stage s-1
+      wait_vmcnt<NV>();
+      compute(ra[u % NSA], buf(u % ND), issue);
       __builtin_amdgcn_sched_barrier(0);
       // T(s+1) landed: after it were issued at most W, T(s+2), W. A plain
       // barrier: the fence of __syncthreads would wait for every copy in
