@@ -131,6 +131,9 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
 // really has: branch-free, and a tile with 3 rows costs one fragment.
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 512;
+#ifndef MOE_TOKEN_STAGES
+#define MOE_TOKEN_STAGES 3
+#endif
 
 template <int V>
 struct IntC {
@@ -165,8 +168,9 @@ template <bool FP8, int NSA, int BM>
 struct MainLoop {
   static constexpr int AW = FP8 ? 2 : 4;       // 16-byte loads per fragment per stage
   static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
-  static constexpr int ND = 3;                 // LDS token stages (two in flight)
-  static constexpr int U = ND * NSA / (NSA % ND == 0 ? ND : 1);  // unroll: lcm(ND, NSA)
+  static constexpr int ND = MOE_TOKEN_STAGES;  // LDS token stages (ND-1 in flight)
+  static constexpr int gcd(int x, int y) { return y == 0 ? x : gcd(y, x % y); }
+  static constexpr int U = ND * NSA / gcd(ND, NSA);   // unroll: lcm(ND, NSA)
 
   // acc[t] += W fragment x token fragment t, over the whole K axis. Every
   // load and MFMA is unconditional: token rows past the expert's end read
@@ -176,8 +180,8 @@ struct MainLoop {
   template <int NT>
   __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
                                              int mvalid, int kdim, int astage, int avs,
-                                             uint16_t* bs0, uint16_t* bs1,
-                                             uint16_t* bs2, f32x16 (&acc)[BM / 32]) {
+                                             uint16_t* bs0, uint16_t* bs1, uint16_t* bs2,
+                                             uint16_t* bs3, f32x16 (&acc)[BM / 32]) {
     constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
     constexpr int BCH = (CH + kThreads - 1) / kThreads; // copies per thread per stage
     const int l = lane_id(), g = l >> 5, r32 = l & 31;
@@ -248,12 +252,13 @@ struct MainLoop {
         }
       }
     };
-    auto buf = [&](int i) { return i == 0 ? bs0 : (i == 1 ? bs1 : bs2); };
+    auto buf = [&](int i) { return i == 0 ? bs0 : (i == 1 ? bs1 : (i == 2 ? bs2 : bs3)); };
 
     // Issue order (the counter waits below depend on it): prologue
-    // T(0), T(1), W(0) .. W(NSA-2); stage s: T(s+2), W(s+NSA-1).
-    load_b(bs0, 0);
-    load_b(bs1, min(1, nk - 1));
+    // T(0) .. T(ND-2), W(0) .. W(NSA-2); stage s: the pieces of T(s+ND-1),
+    // then those of W(s+NSA-1), spread over its MFMAs.
+#pragma unroll
+    for (int p = 0; p < ND - 1; ++p) load_b(buf(p), min(p, nk - 1));
 #pragma unroll
     for (int p = 0; p < NSA - 1; ++p) load_a(ra[p], min(p, nk - 1));
     __builtin_amdgcn_sched_barrier(0);
@@ -268,24 +273,25 @@ struct MainLoop {
     // compile time.
     auto stage = [&](auto uc, int s) {
       constexpr int u = decltype(uc)::value;
-      uint16_t* tdst = buf((u + 2) % ND);               // its readers passed the last barrier
-      const int ts = min(s + 2, nk - 1);
+      uint16_t* tdst = buf((u + ND - 1) % ND);          // its readers passed the last barrier
+      const int ts = min(s + ND - 1, nk - 1);
       u32x4 (&wdst)[AW] = ra[(u + NSA - 1) % NSA];      // consumed in the previous stage
       const uint8_t* wsrc = aptr + static_cast<size_t>(min(s + NSA - 1, nk - 1)) * astage;
-      // requests 0 .. BCH-1: T(s+2); BCH .. NV-1: W(s+NSA-1)
+      // requests 0 .. BCH-1: T(s+ND-1); BCH .. NV-1: W(s+NSA-1)
       auto issue = [&](auto kc) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k < BCH) dma16(bsrc[k] + ts * 64, tdst + bdst[k]);
         else wdst[k - BCH] = *reinterpret_cast<const u32x4*>(wsrc + (k - BCH) * avs);
       };
-      // W(s) landed: after its last piece came the NV requests of stage s-1
-      wait_vmcnt<NV>();
+      // W(s) landed: after its last piece came the requests of NSA-2 stages
+      wait_vmcnt<(NSA - 2) * NV>();
       compute(ra[u % NSA], buf(u % ND), issue);
       __builtin_amdgcn_sched_barrier(0);
-      // T(s+1) landed: after it were issued at most W, T(s+2), W. A plain
-      // barrier: the fence of __syncthreads would wait for every copy in
-      // flight; this stage's LDS reads are complete, their MFMAs issued.
-      wait_vmcnt<2 * AW + BCH>();
+      // T(s+1) landed: after it were issued the W of its stage and the
+      // T and W of ND-2 stages. A plain barrier: the fence of __syncthreads
+      // would wait for every copy in flight; this stage's LDS reads are
+      // complete, their MFMAs issued.
+      wait_vmcnt<AW + (ND - 2) * NV>();
       __builtin_amdgcn_s_barrier();
     };
     // Whole groups of U stages, then the remainder, outside the loop so the
@@ -307,6 +313,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t bs0[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t bs1[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t bs2[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs3[MOE_TOKEN_STAGES > 3 ? BM * 64 : 8];
 
   Tile tl;
   if (!decode_tile<GROUPED>(a, BM, tl)) return;
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   using ML = MainLoop<FP8, NSA, BM>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
-    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, acc); break;
+    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, bs3, acc); break;
     MOE_NT_CASE(1) MOE_NT_CASE(2) MOE_NT_CASE(3) MOE_NT_CASE(4)
     MOE_NT_CASE(5) MOE_NT_CASE(6) MOE_NT_CASE(7) MOE_NT_CASE(8)
 #undef MOE_NT_CASE
