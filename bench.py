@@ -3,12 +3,13 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-decode]
 
 One step = one whole layer call on one batch already resident in HBM:
-router GEMM + sigmoid + biased top-K + gates + loads, stable permutation and
-row gather, grouped gate/up and down SwiGLU GEMMs over the routed experts,
-the shared expert (on a second stream) and the combine. The workload is the
-V3-shape prefill layer: T = 8192 tokens, d = 7168, 256 routed experts of
-intermediate 2048 (top-8, score + bias selection) plus 1 shared expert,
-bf16, synthetic seeded inputs.
+router GEMM + sigmoid + biased top-K + gates + loads, the stable permutation,
+the grouped gate/up and down SwiGLU GEMMs over the routed experts and the
+shared expert (one launch each, routed token rows read through the
+permutation), and the combine. The workload is the V3-shape prefill layer:
+T = 8192 tokens, d = 7168, 256 routed experts of intermediate 2048 (top-8,
+score + bias selection) plus 1 shared expert, bf16, synthetic seeded inputs,
+expert weights relocated once into the tiled layout before timing.
 
 Printed: one JSON line with tokens/s, the roofline of the dominant kernel
 (the grouped gate/up GEMM, timed live with HIP events on its stream), the
@@ -94,54 +95,68 @@ class Timed:
 
 
 def gate_up_bytes(spec) -> float:
-    """Algorithmic HBM bytes of one routed gate/up launch: W1 and W3 of every
-    expert once, the gathered token rows once, H written once (bf16)."""
-    TK = spec.T * spec.K
-    return float(spec.E * 2 * spec.I * spec.d * 2 + TK * spec.d * 2 + TK * spec.I * 2)
+    """Algorithmic HBM bytes of one gate/up launch (routed and shared experts):
+    W1 and W3 of every routed expert and of the shared experts once, x once,
+    H and the shared H written once (bf16)."""
+    TK, SI = spec.T * spec.K, spec.S * spec.Is
+    return float(spec.E * 2 * spec.I * spec.d * 2 + 2 * SI * spec.d * 2 + spec.T * spec.d * 2
+                 + TK * spec.I * 2 + spec.T * SI * 2)
 
 
-def layer_step(layer, x, bias, h, ws_gemm, gate_timer=None):
-    """One full layer call; the routed expert FFN is issued as its two grouped
-    GEMM entry points so the gate/up GEMM can be bracketed by events."""
+def gate_up_flops(spec) -> float:
+    return 4.0 * spec.d * (spec.I * spec.T * spec.K + spec.S * spec.Is * spec.T)
+
+
+def layer_step(layer, x, bias, bufs, gate_timer=None):
+    """One full layer call (the fused path of MoELayer.forward), with the
+    expert FFNs issued as their two grouped launches so the gate/up launch
+    can be bracketed by events on its stream."""
+    h, hs, ws_gemm = bufs
     cfg = layer._cfg(x.shape[0])
-    cur = torch.cuda.current_stream()
-    layer.side.wait_stream(cur)
-    with torch.cuda.stream(layer.side):
-        layer.shared(cfg, x, stream=layer.side)
     layer.route(x, bias)
-    layer.permute(cfg, x)
+    layer.permute(cfg, x, gather=False)
     T, K, w = cfg.num_tokens, cfg.top_k, layer.w
     TK = T * K
+
+    def gate_up():
+        moe.moe_experts_gate_up(cfg, x, layer.expert_offsets, layer.perm_slot[:TK], w["w1"],
+                                w["w3"], w.get("s1"), w.get("s3"), w.get("w1s"), w.get("w3s"),
+                                w.get("s1s"), w.get("s3s"), h, hs, ws=ws_gemm)
     if gate_timer is not None:
         with gate_timer:
-            moe.moe_expert_gate_up(cfg, layer.x_perm[:TK], layer.expert_offsets, w["w1"], w["w3"],
-                                   w.get("s1"), w.get("s3"), h, ws=ws_gemm)
+            gate_up()
     else:
-        moe.moe_expert_gate_up(cfg, layer.x_perm[:TK], layer.expert_offsets, w["w1"], w["w3"],
-                               w.get("s1"), w.get("s3"), h, ws=ws_gemm)
-    moe.moe_expert_down(cfg, h, layer.expert_offsets, layer.perm_slot[:TK], layer.topk_gate[:T],
-                        w["w2"], w.get("s2"), layer.out_slots[:TK], ws=ws_gemm)
-    cur.wait_stream(layer.side)
+        gate_up()
+    moe.moe_experts_down(cfg, h, hs, layer.expert_offsets, layer.perm_slot[:TK],
+                         layer.topk_gate[:T], w["w2"], w.get("s2"), w.get("w2s"), w.get("s2s"),
+                         layer.out_slots[:TK], layer.y_shared[:T] if spec_has_shared(layer) else None,
+                         ws=ws_gemm)
     layer.combine(cfg)
+
+
+def spec_has_shared(layer) -> bool:
+    return layer.y_shared is not None
 
 
 def setup(spec):
     inp = synth.make_inputs(spec, "cuda")
-    layer = moe.MoELayer(spec, inp, max_tokens=spec.T, shared_stream=True)
-    cfg = moe.config_of(spec)
+    layer = moe.MoELayer(spec, inp, max_tokens=spec.T, fused=True)
+    cfg = layer._cfg(spec.T)
     h = torch.empty((spec.T * spec.K, spec.I), dtype=torch.bfloat16, device="cuda")
+    hs = (torch.empty((spec.T, spec.S * spec.Is), dtype=torch.bfloat16, device="cuda")
+          if spec.S > 0 else None)
     ws_gemm = torch.empty(max(moe.moe_workspace_size(cfg, moe.MOE_WS_GEMM), 256), dtype=torch.uint8,
                           device="cuda")
-    return inp, layer, h, ws_gemm
+    return inp, layer, (h, hs, ws_gemm)
 
 
-def time_steps(layer, x, bias, h, ws_gemm, steps, warmup, gate_timer=None):
+def time_steps(layer, x, bias, bufs, steps, warmup, gate_timer=None):
     for _ in range(warmup):
-        layer_step(layer, x, bias, h, ws_gemm)
+        layer_step(layer, x, bias, bufs)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        layer_step(layer, x, bias, h, ws_gemm, gate_timer)
+        layer_step(layer, x, bias, bufs, gate_timer)
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
 
@@ -181,9 +196,9 @@ def cpu_baseline(spec, inp, layer, n_tokens):
 
 def decode_measure(steps, warmup):
     spec = synth.get_config(DECODE)
-    inp, layer, h, ws_gemm = setup(spec)
+    inp, layer, bufs = setup(spec)
     x, bias = inp["x"], inp["bias"]
-    sec = time_steps(layer, x, bias, h, ws_gemm, steps, warmup)
+    sec = time_steps(layer, x, bias, bufs, steps, warmup)
     load = layer.load.cpu().numpy()
     n_active = int((load > 0).sum())
     bytes_ = ((n_active * spec.weight_bytes_per_expert() + spec.shared_weight_bytes())
@@ -193,7 +208,7 @@ def decode_measure(steps, warmup):
     out = {"workload": DECODE, "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
            "active_experts": n_active, "algorithmic_bytes": int(bytes_), "achieved_GBs": gbs,
            "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}
-    del inp, layer, h, ws_gemm
+    del inp, layer, bufs
     torch.cuda.empty_cache()
     return out
 
@@ -228,14 +243,14 @@ def main():
         log("[bench] calibration copy: 1 GiB read, 1 GiB written")
     spec = synth.get_config(WORKLOAD)
     log(f"[bench] generating {WORKLOAD} inputs on the GPU")
-    inp, layer, h, ws_gemm = setup(spec)
+    inp, layer, bufs = setup(spec)
     x, bias = inp["x"], inp["bias"]
     gate_timer = Timed()
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
-    sec = time_steps(layer, x, bias, h, ws_gemm, args.steps, args.warmup, gate_timer)
+    sec = time_steps(layer, x, bias, bufs, args.steps, args.warmup, gate_timer)
     tokens_per_s = spec.T / sec
     gate_ms = gate_timer.mean_ms()
-    gate_flops = 4.0 * spec.d * spec.I * spec.T * spec.K
+    gate_flops = gate_up_flops(spec)
     gate_bytes = gate_up_bytes(spec)
     achieved = gate_flops / (gate_ms * 1e-3) / 1e12
     achieved_gbs = gate_bytes / (gate_ms * 1e-3) / 1e9
@@ -256,11 +271,11 @@ def main():
         "layer_TFLOPs": layer_tflops,
         "layer_frac_mfma_peak": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
         "load_max_over_mean": float(load.max() / load.mean()),
-        # The routed gate/up GEMM does 4*d*I flops per (token, slot) on weights it
-        # must stream once: arithmetic intensity flops/bytes = 237 flop/B at this
+        # The gate/up launch (shared + routed experts) does 4*d*I flops per
+        # (token, slot) on weights it must stream once: 279 flop/B at this
         # shape, below the MI355X ridge (2500 TFLOP/s / 8 TB/s = 312 flop/B), so
         # the roofline that binds it is HBM; the MFMA view is reported beside it.
-        "roofline": {"kernel": "grouped_gemm_mfma<gate/up, bf16, 256-token tiles, routed>",
+        "roofline": {"kernel": "grouped_gemm_mfma<gate/up, bf16, 256-token tiles, shared + routed>",
                      "bound": "hbm",
                      "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
@@ -273,7 +288,7 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(spec, inp, layer, args.cpu_tokens)
-    del inp, layer, h, ws_gemm
+    del inp, layer, bufs
     torch.cuda.empty_cache()
     if not args.no_decode:
         log(f"[bench] decode workload {DECODE}")

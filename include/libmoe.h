@@ -21,6 +21,11 @@
  *   moe_shared_ffn ------------------------------+
  *   (per batch, optionally) moe_bias_update
  *
+ * or, with the routed and shared experts in one pair of grouped launches
+ * that read the routed token rows straight from x (no gathered copy):
+ *
+ *   moe_route -> moe_permute (x_perm = NULL) -> moe_experts -> moe_combine
+ *
  * Conventions shared by every call:
  *   - Every pointer except `cfg` and `status` strings is a DEVICE pointer to
  *     row-major contiguous memory that the caller owns and keeps alive until
@@ -84,6 +89,7 @@ extern "C" {
 #define MOE_WS_FFN     2
 #define MOE_WS_SHARED  3
 #define MOE_WS_GEMM    4  /* moe_expert_gate_up / moe_expert_down */
+#define MOE_WS_EXPERTS 5  /* moe_experts */
 
 /* Layer shape and options. Limits (checked by moe_validate): num_tokens >= 0
  * with num_tokens * top_k < 2^30; 1 <= num_experts <=
@@ -183,8 +189,10 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
  * never produced by moe_route; if present they get no row, the last rows
  * get perm_slot = -1 and zero x_perm rows, and expert_offsets[E] < T*K.
  * topk_idx [T, K] int32; x [T, d] act dtype; expert_offsets [E+1] int32;
- * perm_slot [T*K] int32; x_perm [T*K, d] act dtype. Integer results are
- * exact. Workspace: moe_workspace_size(cfg, MOE_WS_PERMUTE) bytes. */
+ * perm_slot [T*K] int32; x_perm [T*K, d] act dtype, or NULL to skip the row
+ * gather (x is then not read and may be NULL; moe_experts reads the rows of
+ * x through perm_slot itself). Integer results are exact. Workspace:
+ * moe_workspace_size(cfg, MOE_WS_PERMUTE) bytes. */
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                 int32_t* expert_offsets, int32_t* perm_slot, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
@@ -238,6 +246,48 @@ int moe_expert_down(const moe_config* cfg, const void* h, const int32_t* expert_
 int moe_shared_ffn(const moe_config* cfg, const void* x, const void* w1s, const void* w3s,
                    const void* w2s, const float* s1s, const float* s3s, const float* s2s,
                    void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_experts ----------------------------------------------------------
+ * moe_expert_ffn and moe_shared_ffn together: one grouped gate/up launch and
+ * one grouped down launch cover the shared experts' tiles and the routed
+ * experts' tiles, so neither waits behind the other's tail. The routed rows
+ * are read from x through perm_slot (row p of expert e is x[perm_slot[p] /
+ * K]), so moe_permute need not write x_perm. Results are bit-identical to
+ * moe_expert_ffn on the gathered rows followed by moe_shared_ffn.
+ * x [T, d]; expert_offsets, perm_slot from moe_permute; topk_gate [T*K];
+ * routed weights and scales as for moe_expert_ffn, shared ones as for
+ * moe_shared_ffn (all NULL when num_shared == 0, y_shared too); out_slots
+ * [T*K, d] act dtype; y_shared [T, d] fp32. bf16 activations only
+ * (MOE_ERR_DTYPE otherwise). Workspace: MOE_WS_EXPERTS bytes. */
+int moe_experts(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
+                const int32_t* perm_slot, const float* topk_gate,
+                const void* w1, const void* w3, const void* w2,
+                const float* s1, const float* s3, const float* s2,
+                const void* w1s, const void* w3s, const void* w2s,
+                const float* s1s, const float* s3s, const float* s2s,
+                void* out_slots, void* y_shared, void* ws, size_t ws_bytes, void* stream);
+
+/* The two launches of moe_experts, for callers that hold the intermediate
+ * activations themselves (and to time each grouped GEMM on its own):
+ *   moe_experts_gate_up: h[p] = SiLU(W1_e x[perm_slot[p]/K]) * (W3_e ...) for
+ *       the routed rows, hs[t] = SiLU(W1s x[t]) * (W3s x[t]) for the shared
+ *       experts; h [T*K, I], hs [T, S*Is], both act dtype (hs NULL when
+ *       num_shared == 0).
+ *   moe_experts_down: out_slots[perm_slot[p]] = topk_gate[perm_slot[p]] *
+ *       (W2_e h[p]) and y_shared[t] = W2s hs[t].
+ * Arguments as for moe_experts. Workspace: MOE_WS_GEMM bytes each.
+ * moe_experts is exactly gate_up followed by down with h, hs held in its
+ * workspace. */
+int moe_experts_gate_up(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
+                        const int32_t* perm_slot, const void* w1, const void* w3,
+                        const float* s1, const float* s3, const void* w1s, const void* w3s,
+                        const float* s1s, const float* s3s, void* h, void* hs,
+                        void* ws, size_t ws_bytes, void* stream);
+int moe_experts_down(const moe_config* cfg, const void* h, const void* hs,
+                     const int32_t* expert_offsets, const int32_t* perm_slot,
+                     const float* topk_gate, const void* w2, const float* s2, const void* w2s,
+                     const float* s2s, void* out_slots, void* y_shared,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* ---- moe_combine ----------------------------------------------------------
  * The layer output: shared experts plus the gate-weighted routed experts

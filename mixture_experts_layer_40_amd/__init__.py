@@ -28,6 +28,7 @@ from ._lib import (  # noqa: F401
     MOE_PACK_GATE_UP,
     MOE_SCORE_SIGMOID,
     MOE_SCORE_SOFTMAX,
+    MOE_WS_EXPERTS,
     MOE_WS_FFN,
     MOE_WS_GEMM,
     MOE_WS_PERMUTE,
@@ -43,6 +44,9 @@ from ._lib import (  # noqa: F401
     moe_expert_down,
     moe_expert_ffn,
     moe_expert_gate_up,
+    moe_experts,
+    moe_experts_down,
+    moe_experts_gate_up,
     moe_pack_weights,
     moe_permute,
     moe_route,

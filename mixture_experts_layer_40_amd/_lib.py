@@ -42,10 +42,12 @@ MOE_WS_PERMUTE = 1
 MOE_WS_FFN = 2
 MOE_WS_SHARED = 3
 MOE_WS_GEMM = 4
+MOE_WS_EXPERTS = 5
 
 EXPORTED = ("moe_validate", "moe_workspace_size", "moe_status_string", "moe_route",
             "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
-            "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights")
+            "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights",
+            "moe_experts", "moe_experts_gate_up", "moe_experts_down")
 
 
 class MoEError(RuntimeError):
@@ -117,9 +119,12 @@ def load_library(path: str = LIB_PATH):
     lib.moe_combine.argtypes = [CFG, P, P, P, P]
     lib.moe_bias_update.argtypes = [I32, P, ctypes.c_float, P, P]
     lib.moe_pack_weights.argtypes = [ctypes.c_int, I32, I32, I32, I32, P, P, P, P]
+    lib.moe_experts.argtypes = [CFG] + [P] * 19 + [SZ, P]
+    lib.moe_experts_gate_up.argtypes = [CFG] + [P] * 14 + [SZ, P]
+    lib.moe_experts_down.argtypes = [CFG] + [P] * 12 + [SZ, P]
     for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up",
                "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update",
-               "moe_pack_weights"):
+               "moe_pack_weights", "moe_experts", "moe_experts_gate_up", "moe_experts_down"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -249,3 +254,31 @@ def pack_down(w2, weight_dtype, stream=None):
     dst = torch.empty((G, N, C), dtype=w2.dtype, device=w2.device)
     moe_pack_weights(MOE_PACK_DOWN, G, N, C, weight_dtype, w2, None, dst, stream)
     return dst
+
+
+def moe_experts(cfg, x, expert_offsets, perm_slot, topk_gate, w1, w3, w2, s1, s3, s2,
+                w1s, w3s, w2s, s1s, s3s, s2s, out_slots, y_shared, ws=None, stream=None):
+    wsb, nbytes = _ws(cfg, MOE_WS_EXPERTS, ws, out_slots)
+    _check("moe_experts", load_library().moe_experts(
+        ctypes.byref(cfg), _ptr(x), _ptr(expert_offsets), _ptr(perm_slot), _ptr(topk_gate),
+        _ptr(w1), _ptr(w3), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(w1s), _ptr(w3s),
+        _ptr(w2s), _ptr(s1s), _ptr(s3s), _ptr(s2s), _ptr(out_slots), _ptr(y_shared), _ptr(wsb),
+        nbytes, _stream(stream)))
+
+
+def moe_experts_gate_up(cfg, x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s, w3s, s1s, s3s,
+                        h, hs, ws=None, stream=None):
+    wsb, nbytes = _ws(cfg, MOE_WS_GEMM, ws, h)
+    _check("moe_experts_gate_up", load_library().moe_experts_gate_up(
+        ctypes.byref(cfg), _ptr(x), _ptr(expert_offsets), _ptr(perm_slot), _ptr(w1), _ptr(w3),
+        _ptr(s1), _ptr(s3), _ptr(w1s), _ptr(w3s), _ptr(s1s), _ptr(s3s), _ptr(h), _ptr(hs),
+        _ptr(wsb), nbytes, _stream(stream)))
+
+
+def moe_experts_down(cfg, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w2s, s2s,
+                     out_slots, y_shared, ws=None, stream=None):
+    wsb, nbytes = _ws(cfg, MOE_WS_GEMM, ws, out_slots)
+    _check("moe_experts_down", load_library().moe_experts_down(
+        ctypes.byref(cfg), _ptr(h), _ptr(hs), _ptr(expert_offsets), _ptr(perm_slot),
+        _ptr(topk_gate), _ptr(w2), _ptr(s2), _ptr(w2s), _ptr(s2s), _ptr(out_slots),
+        _ptr(y_shared), _ptr(wsb), nbytes, _stream(stream)))

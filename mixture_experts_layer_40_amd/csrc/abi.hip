@@ -84,6 +84,7 @@ size_t moe_workspace_size(const moe_config* c, int which) {
     case MOE_WS_FFN: return c->num_tokens == 0 ? 0 : ffn_ws_bytes(*c);
     case MOE_WS_SHARED: return (c->num_tokens == 0 || c->num_shared == 0) ? 0 : shared_ws_bytes(*c);
     case MOE_WS_GEMM: return c->num_tokens == 0 ? 0 : sched_ws_bytes(*c);
+    case MOE_WS_EXPERTS: return c->num_tokens == 0 ? 0 : experts_ws_bytes(*c);
     default: return 0;
   }
 }
@@ -135,7 +136,7 @@ int moe_permute(const moe_config* c, const int32_t* topk_idx, const void* x,
   int st = moe_validate(c);
   if (st != MOE_OK) return st;
   if (!expert_offsets) return MOE_ERR_NULL;
-  if (c->num_tokens > 0 && (!topk_idx || !x || !perm_slot || !x_perm)) return MOE_ERR_NULL;
+  if (c->num_tokens > 0 && (!topk_idx || !perm_slot || (x_perm && !x))) return MOE_ERR_NULL;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_PERMUTE), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_permute(*c, topk_idx, x, expert_offsets, perm_slot, x_perm, ws,
@@ -202,6 +203,86 @@ int moe_shared_ffn(const moe_config* c, const void* x, const void* w1s, const vo
   (void)hipGetLastError();
   return from_hip(launch_shared_ffn(*c, x, w1s, w3s, w2s, s1s, s3s, s2s, y_shared, ws,
                                     as_stream(stream)));
+}
+
+int moe_experts(const moe_config* c, const void* x, const int32_t* expert_offsets,
+                const int32_t* perm_slot, const float* topk_gate, const void* w1, const void* w3,
+                const void* w2, const float* s1, const float* s3, const float* s2,
+                const void* w1s, const void* w3s, const void* w2s, const float* s1s,
+                const float* s3s, const float* s2s, void* out_slots, void* y_shared, void* ws,
+                size_t ws_bytes, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if ((st = check_scales(c, s1, s3, s2)) != MOE_OK) return st;
+  if (c->num_shared > 0) {
+    if ((st = check_scales(c, s1s, s3s, s2s)) != MOE_OK) return st;
+  } else if (w1s || w3s || w2s || s1s || s3s || s2s || y_shared) {
+    return MOE_ERR_SHAPE;
+  }
+  if (c->num_tokens == 0) return MOE_OK;
+  if ((st = check_w3(c, w3)) != MOE_OK) return st;
+  if (!x || !expert_offsets || !perm_slot || !topk_gate || !w1 || !w2 || !out_slots)
+    return MOE_ERR_NULL;
+  if (c->num_shared > 0) {
+    if ((st = check_w3(c, w3s)) != MOE_OK) return st;
+    if (!w1s || !w2s || !y_shared) return MOE_ERR_NULL;
+  }
+  if ((st = check_ws(moe_workspace_size(c, MOE_WS_EXPERTS), ws, ws_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return from_hip(launch_experts(*c, x, expert_offsets, perm_slot, topk_gate, w1, w3, w2, s1, s3,
+                                 s2, w1s, w3s, w2s, s1s, s3s, s2s, out_slots, y_shared, ws,
+                                 as_stream(stream)));
+}
+
+int moe_experts_gate_up(const moe_config* c, const void* x, const int32_t* expert_offsets,
+                        const int32_t* perm_slot, const void* w1, const void* w3,
+                        const float* s1, const float* s3, const void* w1s, const void* w3s,
+                        const float* s1s, const float* s3s, void* h, void* hs, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if ((st = check_scales(c, s1, s3, s3)) != MOE_OK) return st;
+  if (c->num_shared > 0) {
+    if ((st = check_scales(c, s1s, s3s, s3s)) != MOE_OK) return st;
+  } else if (w1s || w3s || s1s || s3s || hs) {
+    return MOE_ERR_SHAPE;
+  }
+  if (c->num_tokens == 0) return MOE_OK;
+  if ((st = check_w3(c, w3)) != MOE_OK) return st;
+  if (!x || !expert_offsets || !perm_slot || !w1 || !h) return MOE_ERR_NULL;
+  if (c->num_shared > 0) {
+    if ((st = check_w3(c, w3s)) != MOE_OK) return st;
+    if (!w1s || !hs) return MOE_ERR_NULL;
+  }
+  if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return from_hip(launch_experts_gate_up(*c, x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s,
+                                         w3s, s1s, s3s, h, hs, ws, as_stream(stream)));
+}
+
+int moe_experts_down(const moe_config* c, const void* h, const void* hs,
+                     const int32_t* expert_offsets, const int32_t* perm_slot,
+                     const float* topk_gate, const void* w2, const float* s2, const void* w2s,
+                     const float* s2s, void* out_slots, void* y_shared, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if ((st = check_scales(c, s2, s2, s2)) != MOE_OK) return st;
+  if (c->num_shared > 0) {
+    if ((st = check_scales(c, s2s, s2s, s2s)) != MOE_OK) return st;
+  } else if (hs || w2s || s2s || y_shared) {
+    return MOE_ERR_SHAPE;
+  }
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!h || !expert_offsets || !perm_slot || !topk_gate || !w2 || !out_slots) return MOE_ERR_NULL;
+  if (c->num_shared > 0 && (!hs || !w2s || !y_shared)) return MOE_ERR_NULL;
+  if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return from_hip(launch_experts_down(*c, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2,
+                                      w2s, s2s, out_slots, y_shared, ws, as_stream(stream)));
 }
 
 int moe_combine(const moe_config* c, const void* out_slots, const void* y_shared, void* y,

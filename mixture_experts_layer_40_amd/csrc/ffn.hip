@@ -49,10 +49,14 @@ constexpr int kBNF32 = 32;        // columns per tile (fp32 path)
 
 enum { kGateUp = 0, kDown = 1 };
 
-struct GemmArgs {
-  const void* act;            // [rows, kdim] activations (bf16 or fp32)
-  const void* wa;             // gate/up: W1; down: W2   -- expert-major
-  const void* wb;             // gate/up: W3
+// One set of GEMM groups over one pair of weight tensors: E expert groups
+// over expert-contiguous rows (offsets != null) or one group of fixed_m rows.
+struct GemmSet {
+  const void* act;            // activations (bf16 or fp32), kdim per row
+  const int32_t* act_rows;    // row p of the GEMM reads act row act_rows[p] / act_div
+  int act_div;                //   (null: act row p)
+  const void* wa;             // gate/up: W1 (or the tiled gate/up tensor); down: W2
+  const void* wb;             // gate/up: W3 (rows layout)
   const float* sa;            // fp8 row scales of wa ([E, n]) or null
   const float* sb;            // fp8 row scales of wb
   const int32_t* offsets;     // [E+1] expert row offsets, or null = one group of fixed_m rows
@@ -71,30 +75,42 @@ struct GemmArgs {
   int tiled;                  // weights in the tiled layout (wa only; see pack_tiles)
 };
 
-struct Tile {
-  int e, row0, mvalid, nblk;
+// A launch covers the tiles of one or two sets (set 0's tiles first), e.g.
+// the shared expert and the routed experts in one grid.
+struct GemmArgs {
+  GemmSet s[2];
+  int nsets;
 };
 
-// Decode this block's tile; false when the block has no work. GROUPED: rows
-// of E experts at a.offsets with tile starts a.sched; otherwise one group of
-// a.fixed_m rows (the shared experts).
-template <bool GROUPED>
+struct Tile {
+  int set, e, row0, mvalid, nblk;
+};
+
+__device__ __forceinline__ int set_tiles(const GemmSet& g, int bm) {
+  return g.offsets ? g.sched[g.E] : ((g.fixed_m + bm - 1) / bm) * g.nb;
+}
+
+// Decode this block's tile; false when the block has no work.
 __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) {
-  const int total = GROUPED ? a.sched[a.E] : ((a.fixed_m + bm - 1) / bm) * a.nb;
+  const int n0 = set_tiles(a.s[0], bm);
+  const int total = n0 + (a.nsets > 1 ? set_tiles(a.s[1], bm) : 0);
   bool valid;
-  const int tile = xcd_contiguous(blockIdx.x, total, valid);
+  int tile = xcd_contiguous(blockIdx.x, total, valid);
   if (!valid) return false;
-  int e = 0, local = tile, rbeg = 0, m = a.fixed_m;
-  if (GROUPED) {
-    int lo = 0, hi = a.E - 1;  // largest e with sched[e] <= tile
+  t.set = tile < n0 ? 0 : 1;
+  if (t.set) tile -= n0;
+  const GemmSet& g = a.s[t.set];
+  int e = 0, local = tile, rbeg = 0, m = g.fixed_m;
+  if (g.offsets) {
+    int lo = 0, hi = g.E - 1;  // largest e with sched[e] <= tile
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (a.sched[mid] <= tile) lo = mid; else hi = mid - 1;
+      if (g.sched[mid] <= tile) lo = mid; else hi = mid - 1;
     }
     e = lo;
-    local = tile - a.sched[e];
-    rbeg = a.offsets[e];
-    m = a.offsets[e + 1] - rbeg;
+    local = tile - g.sched[e];
+    rbeg = g.offsets[e];
+    m = g.offsets[e + 1] - rbeg;
   }
   // An expert's rows are split into mt = ceil(m / bm) tiles of nearly equal
   // size (multiples of 32 rows): the tiles that share a weight block then
@@ -179,7 +195,8 @@ struct MainLoop {
   // repeat a chunk (writing the same bytes to the same place).
   template <int NT>
   __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
-                                             int mvalid, int kdim, int astage, int avs,
+                                             const int32_t* act_rows, int act_div, int mvalid,
+                                             int kdim, int astage, int avs,
                                              uint16_t* bs0, uint16_t* bs1, uint16_t* bs2,
                                              uint16_t* bs3, f32x16 (&acc)[BM / 32]) {
     constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
@@ -197,8 +214,9 @@ struct MainLoop {
     for (int i = 0; i < BCH; ++i) {
       const int q0 = (w * kWave + kThreads * i) % CH;
       const int q = q0 + l, row = q >> 3, ch = (q & 7) ^ ((row >> 1) & 7);
-      const int src_row = row < mvalid ? row : mvalid - 1;
-      bsrc[i] = act + static_cast<size_t>(row0 + src_row) * kdim + ch * 8;
+      const int p = row0 + (row < mvalid ? row : mvalid - 1);
+      const int src = act_rows ? max(act_rows[p], 0) / act_div : p;
+      bsrc[i] = act + static_cast<size_t>(src) * kdim + ch * 8;
       bdst[i] = q0 * 8;
     }
 
@@ -307,8 +325,8 @@ struct MainLoop {
   }
 };
 
-template <int MODE, bool FP8, int BM, int NSA, bool GROUPED>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
+template <int MODE, bool FP8, int BM, int NSA>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
   constexpr int NTF = BM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t bs0[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t bs1[BM * 64];
@@ -316,7 +334,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t bs3[MOE_TOKEN_STAGES > 3 ? BM * 64 : 8];
 
   Tile tl;
-  if (!decode_tile<GROUPED>(a, BM, tl)) return;
+  if (!decode_tile(args, BM, tl)) return;
+  const GemmSet& a = args.s[tl.set];
 
   const int l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
   const int ntf = (tl.mvalid + 31) >> 5;
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
   using ML = MainLoop<FP8, NSA, BM>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
-    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, bs3, acc); break;
+    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, bs3, acc); break;
     MOE_NT_CASE(1) MOE_NT_CASE(2) MOE_NT_CASE(3) MOE_NT_CASE(4)
     MOE_NT_CASE(5) MOE_NT_CASE(6) MOE_NT_CASE(7) MOE_NT_CASE(8)
 #undef MOE_NT_CASE
@@ -432,12 +451,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs a) {
 // per block, 4 outputs per thread, K in chunks of 32).
 // ---------------------------------------------------------------------------
 template <int MODE>
-__global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs a) {
+__global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs args) {
   __shared__ float xs[kBMF32][33];
   __shared__ float ws1[kBNF32][33];
   __shared__ float ws3[kBNF32][33];
   Tile tl;
-  if (!(a.offsets ? decode_tile<true>(a, kBMF32, tl) : decode_tile<false>(a, kBMF32, tl))) return;
+  if (!decode_tile(args, kBMF32, tl)) return;
+  const GemmSet& a = args.s[tl.set];
   const int tid = threadIdx.x;
   const int tok = tid >> 3, c0 = (tid & 7) * 4;
   const int n0 = tl.nblk * kBNF32;
@@ -448,7 +468,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs a) {
   for (int k0 = 0; k0 < a.kdim; k0 += 32) {
     for (int i = tid; i < 32 * 32; i += 256) {
       const int r = i >> 5, c = i & 31;
-      xs[r][c] = r < tl.mvalid ? act[static_cast<size_t>(tl.row0 + r) * a.kdim + k0 + c] : 0.f;
+      const int src = r < tl.mvalid ? (a.act_rows ? max(a.act_rows[tl.row0 + r], 0) / a.act_div
+                                                  : tl.row0 + r) : 0;
+      xs[r][c] = r < tl.mvalid ? act[static_cast<size_t>(src) * a.kdim + k0 + c] : 0.f;
       const int wr = n0 + r;
       ws1[r][c] = wr < a.n ? wa[static_cast<size_t>(wr) * a.kdim + k0 + c] : 0.f;
       if (MODE == kGateUp) ws3[r][c] = wr < a.n ? wb[static_cast<size_t>(wr) * a.kdim + k0 + c] : 0.f;
@@ -571,7 +593,7 @@ int pick_bm(int64_t rows_per_group) {
   return 256;
 }
 
-template <int MODE, bool FP8, bool GROUPED>
+template <int MODE, bool FP8>
 void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
 #ifndef MOE_NS_BIG
 #define MOE_NS_BIG 3
@@ -582,17 +604,11 @@ void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
   constexpr int NS_BIG = MOE_NS_BIG;
   constexpr int NS_SMALL = MOE_NS_SMALL;
   switch (bm) {
-    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG, GROUPED>), gd, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL>), gd, dim3(kThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL>), gd, dim3(kThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG>), gd, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG>), gd, dim3(kThreads), 0, s, a); break;
   }
-}
-
-template <int MODE, bool FP8>
-void launch_mfma_any(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
-  if (a.offsets) launch_mfma<MODE, FP8, true>(bm, gd, s, a);
-  else launch_mfma<MODE, FP8, false>(bm, gd, s, a);
 }
 
 hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int64_t max_tiles,
@@ -604,11 +620,11 @@ hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int
     if (mode == kGateUp) hipLaunchKernelGGL(grouped_gemm_f32<kGateUp>, gd, bd, 0, s, a);
     else hipLaunchKernelGGL(grouped_gemm_f32<kDown>, gd, bd, 0, s, a);
   } else if (fp8) {
-    if (mode == kGateUp) launch_mfma_any<kGateUp, true>(bm, gd, s, a);
-    else launch_mfma_any<kDown, true>(bm, gd, s, a);
+    if (mode == kGateUp) launch_mfma<kGateUp, true>(bm, gd, s, a);
+    else launch_mfma<kDown, true>(bm, gd, s, a);
   } else {
-    if (mode == kGateUp) launch_mfma_any<kGateUp, false>(bm, gd, s, a);
-    else launch_mfma_any<kDown, false>(bm, gd, s, a);
+    if (mode == kGateUp) launch_mfma<kGateUp, false>(bm, gd, s, a);
+    else launch_mfma<kDown, false>(bm, gd, s, a);
   }
   return hipGetLastError();
 }
@@ -626,6 +642,69 @@ Blocking blocking(const moe_config& c, int n_inter, int64_t rows_per_group) {
 
 size_t elem_bytes(const moe_config& c) { return c.act_dtype == MOE_DTYPE_F32 ? 4 : 2; }
 
+bool is_f32(const moe_config& c) { return c.act_dtype == MOE_DTYPE_F32; }
+bool is_fp8(const moe_config& c) { return c.weight_dtype == MOE_DTYPE_FP8_E4M3; }
+int tiled(const moe_config& c) { return c.weight_layout == MOE_LAYOUT_TILED; }
+
+// The routed experts' gate/up set: rows grouped by expert; token rows read
+// through act_rows (x and perm_slot) or directly (x_perm, act_rows null).
+GemmSet routed_gate_up(const moe_config& c, const Blocking& b, const void* act,
+                       const int32_t* act_rows, const int32_t* offsets, const int32_t* sched,
+                       const void* w1, const void* w3, const float* s1, const float* s3, void* h) {
+  GemmSet g{};
+  g.act = act; g.act_rows = act_rows; g.act_div = c.top_k;
+  g.wa = w1; g.wb = w3; g.sa = s1; g.sb = s3;
+  g.offsets = offsets; g.sched = sched; g.fixed_m = 0; g.E = c.num_experts;
+  g.kdim = c.hidden; g.n = c.inter; g.nb = b.nb1; g.h = h;
+  g.tiled = tiled(c);
+  g.wstride = static_cast<int64_t>(c.inter) * c.hidden * (g.tiled ? 2 : 1);
+  return g;
+}
+
+GemmSet routed_down(const moe_config& c, const Blocking& b, const void* h, const int32_t* offsets,
+                    const int32_t* sched, const int32_t* perm_slot, const float* gate,
+                    const void* w2, const float* s2, void* out_slots) {
+  GemmSet g{};
+  g.act = h; g.wa = w2; g.sa = s2;
+  g.offsets = offsets; g.sched = sched; g.fixed_m = 0; g.E = c.num_experts;
+  g.kdim = c.inter; g.n = c.hidden; g.nb = b.nb2;
+  g.wstride = static_cast<int64_t>(c.hidden) * c.inter;
+  g.perm_slot = perm_slot; g.gate = gate; g.out = out_slots;
+  g.tiled = tiled(c);
+  return g;
+}
+
+GemmSet shared_gate_up(const moe_config& c, const Blocking& b, const void* x, const void* w1s,
+                       const void* w3s, const float* s1s, const float* s3s, void* hs) {
+  GemmSet g{};
+  g.act = x; g.wa = w1s; g.wb = w3s; g.sa = s1s; g.sb = s3s;
+  g.fixed_m = c.num_tokens; g.E = 1;
+  g.kdim = c.hidden; g.n = c.num_shared * c.shared_inter; g.nb = b.nb1; g.h = hs;
+  g.tiled = tiled(c);
+  return g;
+}
+
+GemmSet shared_down(const moe_config& c, const Blocking& b, const void* hs, const void* w2s,
+                    const float* s2s, void* y_shared) {
+  GemmSet g{};
+  g.act = hs; g.wa = w2s; g.sa = s2s;
+  g.fixed_m = c.num_tokens; g.E = 1;
+  g.kdim = c.num_shared * c.shared_inter; g.n = c.hidden; g.nb = b.nb2;
+  g.out = y_shared; g.out_f32 = 1;
+  g.tiled = tiled(c);
+  return g;
+}
+
+hipError_t schedule(const int32_t* offsets, int E, int bm, int nb, int32_t* sched, hipStream_t s) {
+  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, offsets, E, bm, nb, sched);
+  return hipGetLastError();
+}
+
+int64_t routed_max_tiles(const moe_config& c, int bm, int nb) {
+  const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
+  return ((TK + bm - 1) / bm + c.num_experts) * nb;
+}
+
 }  // namespace
 
 size_t sched_ws_bytes(const moe_config& c) { return align_up(static_cast<size_t>(c.num_experts + 1) * 4, 256); }
@@ -640,48 +719,40 @@ size_t shared_ws_bytes(const moe_config& c) {
   return align_up(static_cast<size_t>(c.num_tokens) * c.num_shared * c.shared_inter * elem_bytes(c), 256);
 }
 
+size_t experts_ws_bytes(const moe_config& c) {
+  return h_bytes(c) + (c.num_shared > 0 ? shared_ws_bytes(c) : 0) + sched_ws_bytes(c);
+}
+
 hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t* expert_offsets,
                           const void* w1, const void* w3, const float* s1, const float* s3,
                           void* h, void* ws, hipStream_t s) {
-  const int E = c.num_experts, d = c.hidden, I = c.inter;
+  const int E = c.num_experts;
   const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
   if (TK == 0) return hipSuccess;
-  const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
-  const Blocking b = blocking(c, I, (TK + E - 1) / E);
+  const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, expert_offsets, E, b.bm, b.nb1,
-                     sched);
-  hipError_t err = hipGetLastError();
+  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb1, sched, s);
   if (err != hipSuccess) return err;
-  GemmArgs g{};
-  g.act = x_perm; g.wa = w1; g.wb = w3; g.sa = s1; g.sb = s3;
-  g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
-  g.kdim = d; g.n = I; g.nb = b.nb1; g.h = h;
-  g.tiled = c.weight_layout == MOE_LAYOUT_TILED;
-  g.wstride = static_cast<int64_t>(I) * d * (g.tiled ? 2 : 1);
-  return run_gemm(kGateUp, f32, fp8, b.bm, g, ((TK + b.bm - 1) / b.bm + E) * b.nb1, s);
+  GemmArgs a{};
+  a.nsets = 1;
+  a.s[0] = routed_gate_up(c, b, x_perm, nullptr, expert_offsets, sched, w1, w3, s1, s3, h);
+  return run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a, routed_max_tiles(c, b.bm, b.nb1), s);
 }
 
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
                        const int32_t* perm_slot, const float* topk_gate, const void* w2,
                        const float* s2, void* out_slots, void* ws, hipStream_t s) {
-  const int E = c.num_experts, d = c.hidden, I = c.inter;
+  const int E = c.num_experts;
   const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
   if (TK == 0) return hipSuccess;
-  const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
-  const Blocking b = blocking(c, I, (TK + E - 1) / E);
+  const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, expert_offsets, E, b.bm, b.nb2,
-                     sched);
-  hipError_t err = hipGetLastError();
+  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb2, sched, s);
   if (err != hipSuccess) return err;
-  GemmArgs g{};
-  g.act = h; g.wa = w2; g.sa = s2;
-  g.offsets = expert_offsets; g.sched = sched; g.fixed_m = 0; g.E = E;
-  g.kdim = I; g.n = d; g.nb = b.nb2; g.wstride = static_cast<int64_t>(d) * I;
-  g.tiled = c.weight_layout == MOE_LAYOUT_TILED;
-  g.perm_slot = perm_slot; g.gate = topk_gate; g.out = out_slots;
-  return run_gemm(kDown, f32, fp8, b.bm, g, ((TK + b.bm - 1) / b.bm + E) * b.nb2, s);
+  GemmArgs a{};
+  a.nsets = 1;
+  a.s[0] = routed_down(c, b, h, expert_offsets, sched, perm_slot, topk_gate, w2, s2, out_slots);
+  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a, routed_max_tiles(c, b.bm, b.nb2), s);
 }
 
 hipError_t launch_expert_ffn(const moe_config& c, const void* x_perm,
@@ -701,27 +772,86 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
                              const void* w3s, const void* w2s, const float* s1s,
                              const float* s3s, const float* s2s, void* y_shared, void* ws,
                              hipStream_t s) {
-  const int T = c.num_tokens, d = c.hidden, SI = c.num_shared * c.shared_inter;
+  const int T = c.num_tokens, SI = c.num_shared * c.shared_inter;
   if (T == 0) return hipSuccess;
-  const bool f32 = c.act_dtype == MOE_DTYPE_F32, fp8 = c.weight_dtype == MOE_DTYPE_FP8_E4M3;
   const Blocking b = blocking(c, SI, T);
   const int64_t mt = (T + b.bm - 1) / b.bm;
-
-  GemmArgs g1{};
-  g1.act = x; g1.wa = w1s; g1.wb = w3s; g1.sa = s1s; g1.sb = s3s;
-  g1.offsets = nullptr; g1.sched = nullptr; g1.fixed_m = T; g1.E = 1;
-  g1.kdim = d; g1.n = SI; g1.nb = b.nb1; g1.wstride = 0; g1.h = ws;
-  g1.tiled = c.weight_layout == MOE_LAYOUT_TILED;
-  hipError_t err = run_gemm(kGateUp, f32, fp8, b.bm, g1, mt * b.nb1, s);
+  GemmArgs a1{};
+  a1.nsets = 1;
+  a1.s[0] = shared_gate_up(c, b, x, w1s, w3s, s1s, s3s, ws);
+  hipError_t err = run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a1, mt * b.nb1, s);
   if (err != hipSuccess) return err;
+  GemmArgs a2{};
+  a2.nsets = 1;
+  a2.s[0] = shared_down(c, b, ws, w2s, s2s, y_shared);
+  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a2, mt * b.nb2, s);
+}
 
-  GemmArgs g2{};
-  g2.act = ws; g2.wa = w2s; g2.sa = s2s;
-  g2.offsets = nullptr; g2.sched = nullptr; g2.fixed_m = T; g2.E = 1;
-  g2.kdim = SI; g2.n = d; g2.nb = b.nb2; g2.wstride = 0;
-  g2.perm_slot = nullptr; g2.gate = nullptr; g2.out = y_shared; g2.out_f32 = 1;
-  g2.tiled = c.weight_layout == MOE_LAYOUT_TILED;
-  return run_gemm(kDown, f32, fp8, b.bm, g2, mt * b.nb2, s);
+// Shared and routed experts in one gate/up and one down launch (shared tiles
+// first), the routed token rows read from x through perm_slot.
+hipError_t launch_experts_gate_up(const moe_config& c, const void* x,
+                                  const int32_t* expert_offsets, const int32_t* perm_slot,
+                                  const void* w1, const void* w3, const float* s1,
+                                  const float* s3, const void* w1s, const void* w3s,
+                                  const float* s1s, const float* s3s, void* h, void* hs,
+                                  void* ws, hipStream_t s) {
+  const int E = c.num_experts, T = c.num_tokens, SI = c.num_shared * c.shared_inter;
+  const int64_t TK = static_cast<int64_t>(T) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
+  int32_t* sched = static_cast<int32_t*>(ws);
+  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb1, sched, s);
+  if (err != hipSuccess) return err;
+  GemmArgs a{};
+  int64_t tiles = routed_max_tiles(c, b.bm, b.nb1);
+  if (c.num_shared > 0) {
+    const Blocking bs = blocking(c, SI, T);   // its nb1 (the token tile stays b.bm)
+    a.s[a.nsets++] = shared_gate_up(c, bs, x, w1s, w3s, s1s, s3s, hs);
+    tiles += ((T + b.bm - 1) / b.bm) * bs.nb1;
+  }
+  a.s[a.nsets++] = routed_gate_up(c, b, x, perm_slot, expert_offsets, sched, w1, w3, s1, s3, h);
+  return run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a, tiles, s);
+}
+
+hipError_t launch_experts_down(const moe_config& c, const void* h, const void* hs,
+                               const int32_t* expert_offsets, const int32_t* perm_slot,
+                               const float* topk_gate, const void* w2, const float* s2,
+                               const void* w2s, const float* s2s, void* out_slots,
+                               void* y_shared, void* ws, hipStream_t s) {
+  const int E = c.num_experts, T = c.num_tokens, SI = c.num_shared * c.shared_inter;
+  const int64_t TK = static_cast<int64_t>(T) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
+  int32_t* sched = static_cast<int32_t*>(ws);
+  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb2, sched, s);
+  if (err != hipSuccess) return err;
+  GemmArgs a{};
+  int64_t tiles = routed_max_tiles(c, b.bm, b.nb2);
+  if (c.num_shared > 0) {
+    const Blocking bs = blocking(c, SI, T);
+    a.s[a.nsets++] = shared_down(c, bs, hs, w2s, s2s, y_shared);
+    tiles += ((T + b.bm - 1) / b.bm) * bs.nb2;
+  }
+  a.s[a.nsets++] = routed_down(c, b, h, expert_offsets, sched, perm_slot, topk_gate, w2, s2,
+                               out_slots);
+  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a, tiles, s);
+}
+
+hipError_t launch_experts(const moe_config& c, const void* x, const int32_t* expert_offsets,
+                          const int32_t* perm_slot, const float* topk_gate, const void* w1,
+                          const void* w3, const void* w2, const float* s1, const float* s3,
+                          const float* s2, const void* w1s, const void* w3s, const void* w2s,
+                          const float* s1s, const float* s3s, const float* s2s, void* out_slots,
+                          void* y_shared, void* ws, hipStream_t s) {
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  void* h = wsb;
+  void* hs = c.num_shared > 0 ? wsb + h_bytes(c) : nullptr;
+  void* sched = wsb + h_bytes(c) + (c.num_shared > 0 ? shared_ws_bytes(c) : 0);
+  hipError_t err = launch_experts_gate_up(c, x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s,
+                                          w3s, s1s, s3s, h, hs, sched, s);
+  if (err != hipSuccess) return err;
+  return launch_experts_down(c, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w2s, s2s,
+                             out_slots, y_shared, sched, s);
 }
 
 hipError_t launch_pack(int which, int64_t groups, int rows, int cols, int wbytes,

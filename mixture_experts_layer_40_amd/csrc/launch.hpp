@@ -42,6 +42,24 @@ hipError_t launch_expert_ffn(const moe_config& c, const void* x_perm,
                              const float* topk_gate, const void* w1, const void* w3,
                              const void* w2, const float* s1, const float* s3, const float* s2,
                              void* out_slots, void* ws, hipStream_t s);
+size_t experts_ws_bytes(const moe_config& c);
+hipError_t launch_experts_gate_up(const moe_config& c, const void* x,
+                                  const int32_t* expert_offsets, const int32_t* perm_slot,
+                                  const void* w1, const void* w3, const float* s1,
+                                  const float* s3, const void* w1s, const void* w3s,
+                                  const float* s1s, const float* s3s, void* h, void* hs,
+                                  void* ws, hipStream_t s);
+hipError_t launch_experts_down(const moe_config& c, const void* h, const void* hs,
+                               const int32_t* expert_offsets, const int32_t* perm_slot,
+                               const float* topk_gate, const void* w2, const float* s2,
+                               const void* w2s, const float* s2s, void* out_slots,
+                               void* y_shared, void* ws, hipStream_t s);
+hipError_t launch_experts(const moe_config& c, const void* x, const int32_t* expert_offsets,
+                          const int32_t* perm_slot, const float* topk_gate, const void* w1,
+                          const void* w3, const void* w2, const float* s1, const float* s3,
+                          const float* s2, const void* w1s, const void* w3s, const void* w2s,
+                          const float* s1s, const float* s3s, const float* s2s, void* out_slots,
+                          void* y_shared, void* ws, hipStream_t s);
 hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s,
                              const void* w3s, const void* w2s, const float* s1s,
                              const float* s3s, const float* s2s, void* y_shared, void* ws,

@@ -179,6 +179,7 @@ hipError_t launch_permute(const moe_config& c, const int32_t* topk_idx, const vo
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(perm_rank, dim3(nblk), dim3(256), 0, s, topk_idx, TK, E, hist, perm_slot);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (!x_perm) return hipSuccess;   // the caller reads x through perm_slot itself
   const int elem = c.act_dtype == MOE_DTYPE_F32 ? 4 : 2;
   const int row_bytes = c.hidden * elem;
   hipLaunchKernelGGL(perm_gather, dim3(static_cast<unsigned>((TK + 3) / 4)), dim3(256), 0, s,

@@ -5,14 +5,16 @@ their stored formats) and allocates every intermediate buffer once, sized
 for `max_tokens`. With layout="tiled" (the default for bf16 / fp8 weights)
 it relocates the expert weights once into the tiled layout of
 moe_pack_weights and keeps only that copy's references for the calls.
-forward() enqueues
+forward() enqueues, on the current stream,
 
-    moe_shared_ffn (second stream)  ||  moe_route -> moe_permute -> moe_expert_ffn
-    -> join -> moe_combine
+    fused (default with bf16 activations):
+        moe_route -> moe_permute (no row gather) -> moe_experts -> moe_combine
+    otherwise:
+        moe_shared_ffn (second stream)  ||  moe_route -> moe_permute -> moe_expert_ffn
+        -> join -> moe_combine
 
-on the current stream and returns y (plus the routing results it kept). The
-per-batch bias step is `bias_update()`. Nothing here computes: every step is
-a libmoe kernel.
+and returns y (plus the routing results it kept). The per-batch bias step is
+`bias_update()`. Nothing here computes: every step is a libmoe kernel.
 """
 
 from __future__ import annotations
@@ -28,7 +30,8 @@ _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 class MoELayer:
     def __init__(self, spec, weights: dict, max_tokens: Optional[int] = None,
-                 shared_stream: bool = True, device=None, layout: Optional[str] = None):
+                 shared_stream: bool = True, device=None, layout: Optional[str] = None,
+                 fused: Optional[bool] = None):
         self.spec = spec
         self.device = torch.device(device) if device is not None else weights["wr"].device
         self.max_tokens = spec.T if max_tokens is None else max_tokens
@@ -36,6 +39,7 @@ class MoELayer:
         if layout is None:
             layout = "rows" if spec.weight_dtype == "f32" else "tiled"
         self.layout = layout
+        self.fused = spec.act_dtype == "bf16" if fused is None else fused
         self.w = dict(weights)
         if layout == "tiled":
             wd = spec.weight_dtype
@@ -69,7 +73,9 @@ class MoELayer:
         self.ws_perm = ws(L.MOE_WS_PERMUTE)
         self.ws_ffn = ws(L.MOE_WS_FFN)
         self.ws_shared = ws(L.MOE_WS_SHARED)
-        self.side = torch.cuda.Stream(device=dev) if (shared_stream and spec.S > 0) else None
+        self.ws_experts = ws(L.MOE_WS_EXPERTS) if self.fused else None
+        self.side = (torch.cuda.Stream(device=dev)
+                     if (shared_stream and spec.S > 0 and not self.fused) else None)
 
     def _cfg(self, T):
         if T > self.max_tokens:
@@ -83,10 +89,19 @@ class MoELayer:
                     ws=self.ws_route)
         return cfg
 
-    def permute(self, cfg, x):
+    def permute(self, cfg, x, gather=True):
         T = cfg.num_tokens
-        L.moe_permute(cfg, self.topk_idx[:T], x, self.expert_offsets,
-                      self.perm_slot[:T * cfg.top_k], self.x_perm[:T * cfg.top_k], ws=self.ws_perm)
+        L.moe_permute(cfg, self.topk_idx[:T], x if gather else None, self.expert_offsets,
+                      self.perm_slot[:T * cfg.top_k],
+                      self.x_perm[:T * cfg.top_k] if gather else None, ws=self.ws_perm)
+
+    def experts_fused(self, cfg, x):
+        T, w = cfg.num_tokens, self.w
+        L.moe_experts(cfg, x, self.expert_offsets, self.perm_slot[:T * cfg.top_k],
+                      self.topk_gate[:T], w["w1"], w["w3"], w["w2"], w.get("s1"), w.get("s3"),
+                      w.get("s2"), w.get("w1s"), w.get("w3s"), w.get("w2s"), w.get("s1s"),
+                      w.get("s3s"), w.get("s2s"), self.out_slots[:T * cfg.top_k],
+                      None if self.y_shared is None else self.y_shared[:T], ws=self.ws_experts)
 
     def experts(self, cfg):
         T, w = cfg.num_tokens, self.w
@@ -111,6 +126,12 @@ class MoELayer:
         if cfg.num_tokens == 0:
             L.moe_route(cfg, x, self.w["wr"], bias, None, None, self.load, ws=self.ws_route)
             return self.y[:0]
+        if self.fused:
+            self.route(x, bias)
+            self.permute(cfg, x, gather=False)
+            self.experts_fused(cfg, x)
+            self.combine(cfg)
+            return self.y[:cfg.num_tokens]
         cur = torch.cuda.current_stream(self.device)
         if self.side is not None:
             self.side.wait_stream(cur)

@@ -50,11 +50,12 @@ def bank_of(inp, spec):
     return oracle.ExpertBank(fetch=fetch, shared=shared, S=spec.S)
 
 
-def run_steps(spec, inp, bias=None, x=None, layer=None, side_stream=False):
+def run_steps(spec, inp, bias=None, x=None, layer=None, side_stream=False, fused=None):
     """One layer call through the C ABI, step by step; returns host copies."""
     x = inp["x"] if x is None else x
     if layer is None:
-        layer = moe.MoELayer(spec, inp, max_tokens=x.shape[0], shared_stream=side_stream)
+        layer = moe.MoELayer(spec, inp, max_tokens=x.shape[0], shared_stream=side_stream,
+                             fused=fused)
     y = layer.forward(x, bias)
     torch.cuda.synchronize()
     T, K = x.shape[0], spec.K

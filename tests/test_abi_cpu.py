@@ -109,16 +109,16 @@ def test_entry_points_reject_before_any_device_call():
     need = moe.moe_workspace_size(c, moe.MOE_WS_ROUTE)
     assert lib.moe_route(by(c), fake, fake, None, fake, fake, fake, P(0x1000), need - 1, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_route(by(c), fake, fake, None, fake, fake, fake, P(0x1010), need, None) == L.MOE_ERR_WORKSPACE  # misaligned
-    assert lib.moe_permute(by(c), None, fake, fake, fake, fake, fake, 1 << 20, None) == L.MOE_ERR_NULL
+    assert lib.moe_permute(by(c), None, fake, fake, fake, fake, None, 0, None) == L.MOE_ERR_NULL
     assert lib.moe_permute(by(c), fake, fake, fake, fake, fake, None, 0, None) == L.MOE_ERR_WORKSPACE
     # fp8 needs scales; other weight types must not get any
     f8 = _cfg(act_dtype="bf16", weight_dtype="fp8")
     args = [fake] * 8
-    assert lib.moe_expert_ffn(by(f8), *args[:7], None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_NULL
-    assert lib.moe_expert_ffn(by(c), *args[:7], fake, fake, fake, fake, fake, 1 << 30, None) == L.MOE_ERR_DTYPE
-    assert lib.moe_expert_gate_up(by(f8), fake, fake, fake, fake, None, None, fake, fake, 1 << 20, None) == L.MOE_ERR_NULL
-    assert lib.moe_expert_down(by(c), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == L.MOE_ERR_DTYPE
-    assert lib.moe_shared_ffn(by(_cfg(S=0)), fake, fake, fake, fake, None, None, None, fake, fake, 1 << 20, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_expert_ffn(by(f8), *args[:7], None, None, None, fake, None, 0, None) == L.MOE_ERR_NULL
+    assert lib.moe_expert_ffn(by(c), *args[:7], fake, fake, fake, fake, None, 0, None) == L.MOE_ERR_DTYPE
+    assert lib.moe_expert_gate_up(by(f8), fake, fake, fake, fake, None, None, fake, None, 0, None) == L.MOE_ERR_NULL
+    assert lib.moe_expert_down(by(c), fake, fake, fake, fake, fake, fake, fake, None, 0, None) == L.MOE_ERR_DTYPE
+    assert lib.moe_shared_ffn(by(_cfg(S=0)), fake, fake, fake, fake, None, None, None, fake, None, 0, None) == L.MOE_ERR_SHAPE
     assert lib.moe_combine(by(c), None, None, fake, None) == L.MOE_ERR_NULL
     assert lib.moe_bias_update(0, fake, ctypes.c_float(1e-3), fake, None) == L.MOE_ERR_SHAPE
     assert lib.moe_bias_update(257, fake, ctypes.c_float(1e-3), fake, None) == L.MOE_ERR_SHAPE
@@ -137,11 +137,11 @@ def test_tiled_layout_and_pack_validation():
     t = _cfg(act_dtype="bf16", weight_dtype="bf16", weight_layout="tiled")
     r = _cfg(act_dtype="bf16", weight_dtype="bf16")
     # the tiled layout takes the gate/up tensor in w1 and no w3; the rows layout needs w3
-    assert lib.moe_expert_ffn(by(t), *[fake] * 5, fake, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_SHAPE
-    assert lib.moe_expert_ffn(by(r), *[fake] * 5, None, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_NULL
-    assert lib.moe_expert_gate_up(by(t), fake, fake, fake, fake, None, None, fake, fake, 1 << 20, None) == L.MOE_ERR_SHAPE
-    assert lib.moe_shared_ffn(by(t), fake, fake, fake, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_SHAPE
-    assert lib.moe_shared_ffn(by(r), fake, fake, None, fake, None, None, None, fake, fake, 1 << 30, None) == L.MOE_ERR_NULL
+    assert lib.moe_expert_ffn(by(t), *[fake] * 5, fake, fake, None, None, None, fake, None, 0, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_expert_ffn(by(r), *[fake] * 5, None, fake, None, None, None, fake, None, 0, None) == L.MOE_ERR_NULL
+    assert lib.moe_expert_gate_up(by(t), fake, fake, fake, fake, None, None, fake, None, 0, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_shared_ffn(by(t), fake, fake, fake, fake, None, None, None, fake, None, 0, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_shared_ffn(by(r), fake, fake, None, fake, None, None, None, fake, None, 0, None) == L.MOE_ERR_NULL
     pk = lib.moe_pack_weights
     G, UP, DN = L.MOE_PACK_GATE_UP, L.MOE_PACK_GATE_UP, L.MOE_PACK_DOWN
     assert pk(2, 1, 32, 64, L.MOE_DTYPE_BF16, fake, None, fake, None) == L.MOE_ERR_SHAPE
@@ -166,3 +166,34 @@ def test_zero_tokens_is_a_noop_without_device_work():
     assert lib.moe_shared_ffn(by(z), None, None, None, None, None, None, None, None, None, 0, None) == L.MOE_OK
     assert lib.moe_expert_gate_up(by(z), None, None, None, None, None, None, None, None, 0, None) == L.MOE_OK
     del fake
+
+
+def test_fused_entry_points_validate_on_host():
+    lib = moe.load_library()
+    by = ctypes.byref
+    fake = ctypes.c_void_p(0x1000)
+    f32 = _cfg()
+    b16 = _cfg(act_dtype="bf16", weight_dtype="bf16", weight_layout="tiled")
+    nos = _cfg(act_dtype="bf16", weight_dtype="bf16", S=0, Is=0)
+    args18 = [fake] * 18
+    # bf16 activations only
+    assert lib.moe_experts(by(f32), *args18, None, 0, None) == L.MOE_ERR_DTYPE
+    # tiled layout: w3 and w3s must be NULL
+    ok = [fake, fake, fake, fake, fake, None, fake, None, None, None, fake, None, fake, None,
+          None, None, fake, fake]
+    assert lib.moe_experts(by(b16), *ok, None, 0, None) == L.MOE_ERR_WORKSPACE   # stops before any launch
+    bad = list(ok)
+    bad[5] = fake                       # w3 given with the tiled layout
+    assert lib.moe_experts(by(b16), *bad, None, 0, None) == L.MOE_ERR_SHAPE
+    # no shared experts: shared pointers must be NULL
+    rows = [fake, fake, fake, fake, fake, fake, fake, None, None, None, None, None, None, None,
+            None, None, fake, None]
+    assert lib.moe_experts(by(nos), *rows, None, 0, None) == L.MOE_ERR_WORKSPACE
+    rows_bad = list(rows)
+    rows_bad[17] = fake                 # y_shared without shared experts
+    assert lib.moe_experts(by(nos), *rows_bad, None, 0, None) == L.MOE_ERR_SHAPE
+    assert moe.moe_workspace_size(b16, moe.MOE_WS_EXPERTS) >= moe.moe_workspace_size(b16, moe.MOE_WS_FFN)
+    # moe_permute without the row gather needs neither x nor x_perm
+    c = _cfg(act_dtype="bf16", weight_dtype="bf16")
+    assert lib.moe_permute(by(c), fake, None, fake, fake, None, None, 0, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(by(c), fake, None, fake, fake, fake, None, 0, None) == L.MOE_ERR_NULL

@@ -44,6 +44,7 @@ def test_fullsize_layer(name, n_rows):
     r, _ = oracle_route(spec, inp["x"], inp["wr"], inp["bias"])
     n_near = check_route(spec, r, res["idx"], res["gate"], res["load"])
     check_permutation(spec, res["idx"], res["offsets"], res["perm"])
+    layer.permute(layer._cfg(spec.T), inp["x"])      # the row gather, checked on its own
     perm = torch.as_tensor(res["perm"], device="cuda")
     assert torch.equal(layer.x_perm[:spec.T * spec.K], inp["x"][perm // spec.K])
     rows = _sample_rows(spec.T, n_rows, r["near_tie"])

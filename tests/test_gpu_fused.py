@@ -1,0 +1,73 @@
+"""moe_experts (shared and routed experts in one pair of grouped launches,
+routed rows read from x through perm_slot) against the separate calls
+moe_permute (with the row gather) + moe_expert_ffn + moe_shared_ffn: the
+same arithmetic on the same rows, so every output must match bit for bit.
+Also moe_experts_gate_up + moe_experts_down == moe_experts, and the
+argument checks that need a device-free call."""
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_40_amd as moe
+import synth
+from gpu_parity import run_steps, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(base, **kw):
+    name = base + "_" + "_".join(f"{k}{v}" for k, v in sorted(kw.items()))
+    return synth.scaled_config(base, name=name, **kw)
+
+
+CASES = {
+    "v3_gemm": _cfg("v3_prefill_bf16", T=1000, d=1024, E=32, K=4, I=384, Is=256),
+    "dsmoe_small": _cfg("dsmoe2024_bf16", T=300, d=256, E=64, K=6, I=192, Is=128),
+    "fp8_multi": _cfg("v3_decode_fp8", T=700, d=256, E=16, K=4, I=192, S=2, Is=64),
+    "fp8_small": _cfg("v3_decode_fp8", T=64, d=512, E=64, K=8, I=256, Is=256),
+    "bm256": _cfg("v3_prefill_bf16", T=2000, d=256, E=16, K=4, I=256, Is=128),
+    "no_shared": _cfg("v3_prefill_bf16", T=33, d=64, E=1, K=1, I=64, S=0, Is=0),
+    "k_eq_e": _cfg("v3_prefill_bf16", T=50, d=64, E=7, K=7, I=64, Is=64),
+    "one_token": _cfg("v3_prefill_bf16", T=1, d=128, E=256, K=8, I=64, Is=64),
+}
+
+
+@pytest.mark.parametrize("layout", ["tiled", "rows"])
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_matches_separate_calls(name, layout):
+    spec = CASES[name]
+    say(f"[fused] {name} {layout}")
+    inp = synth.make_inputs(spec, "cuda")
+    sep = moe.MoELayer(spec, inp, layout=layout, fused=False, shared_stream=False)
+    fus = moe.MoELayer(spec, inp, layout=layout, fused=True)
+    _, a = run_steps(spec, inp, bias=inp["bias"], layer=sep)
+    _, b = run_steps(spec, inp, bias=inp["bias"], layer=fus)
+    for k in ("idx", "gate", "load", "offsets", "perm"):
+        assert np.array_equal(a[k], b[k]), k
+    TK = spec.T * spec.K
+    assert torch.equal(sep.out_slots[:TK], fus.out_slots[:TK])
+    if spec.S > 0:
+        assert torch.equal(sep.y_shared, fus.y_shared)
+    assert torch.equal(a["y"], b["y"])
+
+
+def test_split_fused_entry_points_equal_moe_experts():
+    spec = CASES["fp8_multi"]
+    inp = synth.make_inputs(spec, "cuda")
+    layer = moe.MoELayer(spec, inp, fused=True)
+    run_steps(spec, inp, bias=inp["bias"], layer=layer)
+    cfg, w = layer._cfg(spec.T), layer.w
+    T, TK, SI = spec.T, spec.T * spec.K, spec.S * spec.Is
+    h = torch.empty((TK, spec.I), dtype=torch.bfloat16, device="cuda")
+    hs = torch.empty((T, SI), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((TK, spec.d), dtype=torch.bfloat16, device="cuda")
+    ysh = torch.empty((T, spec.d), dtype=torch.float32, device="cuda")
+    moe.moe_experts_gate_up(cfg, inp["x"], layer.expert_offsets, layer.perm_slot[:TK], w["w1"],
+                            w["w3"], w.get("s1"), w.get("s3"), w["w1s"], w["w3s"], w.get("s1s"),
+                            w.get("s3s"), h, hs)
+    moe.moe_experts_down(cfg, h, hs, layer.expert_offsets, layer.perm_slot[:TK], layer.topk_gate,
+                         w["w2"], w.get("s2"), w["w2s"], w.get("s2s"), out, ysh)
+    torch.cuda.synchronize()
+    assert torch.equal(out, layer.out_slots[:TK])
+    assert torch.equal(ysh, layer.y_shared)

@@ -62,24 +62,31 @@ def test_layer_parity(name):
     r, _ = oracle_route(spec, inp["x"], inp["wr"], inp["bias"])
     n_near = check_route(spec, r, res["idx"], res["gate"], res["load"])
     check_permutation(spec, res["idx"], res["offsets"], res["perm"])
-    # gathered rows are exact copies
+    # the row gather of moe_permute (the fused forward reads x through
+    # perm_slot instead): gathered rows are exact copies
     K = spec.K
+    layer.permute(layer._cfg(spec.T), inp["x"])
     perm = torch.as_tensor(res["perm"], device="cuda")
     assert torch.equal(layer.x_perm[:spec.T * K], inp["x"][perm // K])
     out = check_outputs(spec, layer, inp, res, r)
     say(f"[parity] {name}: near-ties={n_near} y_err/rms={out['y_err']:.3e}")
 
 
-def test_side_stream_matches_single_stream_and_is_deterministic():
+def test_call_sequences_agree_bit_for_bit_and_are_deterministic():
+    """Separate expert calls on one stream, the shared expert on a second
+    stream, and the fused moe_experts path: identical bits, twice over."""
     spec = CASES["v3_gemm"]
     inp = synth.make_inputs(spec, "cuda")
-    _, a = run_steps(spec, inp, bias=inp["bias"], side_stream=False)
-    ya = a["y"].clone()
-    _, b = run_steps(spec, inp, bias=inp["bias"], side_stream=True)
-    _, c = run_steps(spec, inp, bias=inp["bias"], side_stream=True)
-    for k in ("idx", "gate", "load", "offsets", "perm"):
-        assert np.array_equal(a[k], b[k]) and np.array_equal(b[k], c[k]), k
-    assert torch.equal(ya, b["y"]) and torch.equal(b["y"], c["y"])
+    runs = [run_steps(spec, inp, bias=inp["bias"], side_stream=side, fused=fused)[1]
+            for side, fused in ((False, False), (True, False), (True, False), (False, True),
+                                (False, True))]
+    runs = [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in r.items()}
+            for r in runs]
+    a = runs[0]
+    for b in runs[1:]:
+        for k in ("idx", "gate", "load", "offsets", "perm"):
+            assert np.array_equal(a[k], b[k]), k
+        assert torch.equal(a["y"], b["y"])
 
 
 def test_split_entry_points_equal_expert_ffn():
@@ -88,6 +95,7 @@ def test_split_entry_points_equal_expert_ffn():
     layer, res = run_steps(spec, inp, bias=inp["bias"])
     cfg = moe.config_of(spec)
     TK = spec.T * spec.K
+    layer.permute(layer._cfg(spec.T), inp["x"])        # fill x_perm
     h = torch.empty((TK, spec.I), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((TK, spec.d), dtype=torch.bfloat16, device="cuda")
     moe.moe_expert_gate_up(cfg, layer.x_perm[:TK], layer.expert_offsets, inp["w1"], inp["w3"], None, None, h)
