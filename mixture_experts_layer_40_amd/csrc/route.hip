@@ -16,6 +16,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "gemm_core.hpp"
 #include "launch.hpp"
 
 namespace moe {
@@ -107,106 +108,45 @@ __device__ void topk_token(const float (&lg)[4], int t, int E, int K, int score_
 }
 
 // ---------------------------------------------------------------------------
-// Fused path (bf16, many tokens): one block = 32 tokens x all E experts.
-// Token rows are staged in LDS (double buffered, 16-byte chunks XOR-swizzled
-// by row pair, so the 16 rows one ds_read_b128 serves hit 16 distinct bank groups); each wave streams its own router rows straight from global memory
-// into MFMA operands, so LDS only carries the operand all waves share.
-// Within a 64-wide K stage, lane group g consumes K-elements 16g .. 16g+15
-// (two MFMA steps of 8); both operands use the same assignment.
+// Fused path (bf16, many tokens): one block = 32 tokens x all E (<= 256)
+// experts, in the shape of the expert GEMMs' K loop: 8 waves, wave w streams
+// router rows 32w .. 32w+31 into MFMA operands, the 32-token tile is shared
+// through LDS. The logits stay in LDS; each wave then runs the top-K of 4
+// tokens. Rows past E (E < 256) are computed on a repeated row and dropped.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_fused_bf16(
+__global__ __launch_bounds__(kThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int T, int d, int E, int K, int score_fn, int norm,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ load) {
   constexpr int BT = kFusedTokens;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs0[BT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs1[BT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs2[BT * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs3[MOE_TOKEN_STAGES > 3 ? BT * 64 : 8];
   __shared__ float lgs[BT][257];
   __shared__ int hist[256];
 
-  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
   const int t0 = blockIdx.x * BT;
-  const int nEF = (E + 15) >> 4;
-  hist[tid] = 0;
+  const int mvalid = min(BT, T - t0);
+  if (tid < 256) hist[tid] = 0;
 
-  // router rows of this lane for its (up to) 4 expert fragments
-  const uint16_t* arow[4];
-  bool fvalid[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int f = w + 4 * i;
-    fvalid[i] = f < nEF;
-    int row = 16 * f + r16;
-    row = row < E ? row : E - 1;
-    arow[i] = wr + static_cast<size_t>(row) * d + 16 * g;
-  }
-  // token chunk this thread stages
-  const int brow = tid >> 3, bch = tid & 7;
-  const int btok = t0 + brow;
-  const uint16_t* bsrc = x + static_cast<size_t>(btok < T ? btok : T - 1) * d + bch * 8;
-  const int bdst = brow * 64 + ((bch ^ ((brow >> 1) & 7)) * 8);
-
-  f32x4 acc[4][2];
+  const int row = min(32 * w + r32, E - 1);
+  const uint8_t* aptr = reinterpret_cast<const uint8_t*>(wr + static_cast<size_t>(row) * d + 32 * g);
+  f32x16 acc[1] = {f32x16{}};
+  MainLoop<false, 3, BT>::template run<1>(aptr, x, t0, nullptr, 1, mvalid, d, 64 * 2, 16, bs0, bs1,
+                                          bs2, bs3, acc);
+  // acc[0][4i + j] = logit of expert 32w + 8i + 4g + j for token t0 + r32
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = d / 64;
-  u32x4 a0[4][2], a1[4][2], bst;
-
-  auto load_a = [&](u32x4 (&a)[4][2], int ks) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (fvalid[i]) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(arow[i] + ks * 64);
-        a[i][0] = p[0];
-        a[i][1] = p[1];
-      }
-  };
-  auto load_b = [&](int ks) { bst = *reinterpret_cast<const u32x4*>(bsrc + ks * 64); };
-  auto store_b = [&](int buf) { *reinterpret_cast<u32x4*>(&xs[buf][bdst]) = bst; };
-  auto compute = [&](const u32x4 (&a)[4][2], int buf) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int tf = 0; tf < 2; ++tf) {
-        const int tok = 16 * tf + r16, ch = 2 * g + s;
-        const u32x4 b = *reinterpret_cast<const u32x4*>(&xs[buf][tok * 64 + ((ch ^ ((tok >> 1) & 7)) * 8)]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (fvalid[i]) acc[i][tf] = mfma_16x16x32(a[i][s], b, acc[i][tf]);
-      }
-  };
-
-  load_a(a0, 0);
-  load_b(0);
-  store_b(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ks += 2) {
-    if (ks + 1 < nk) { load_a(a1, ks + 1); load_b(ks + 1); }
-    compute(a0, 0);
-    if (ks + 1 < nk) store_b(1);
-    __syncthreads();
-    if (ks + 1 >= nk) break;
-    if (ks + 2 < nk) { load_a(a0, ks + 2); load_b(ks + 2); }
-    compute(a1, 1);
-    if (ks + 2 < nk) store_b(0);
-    __syncthreads();
-  }
-
-  // logits -> LDS [token][expert]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!fvalid[i]) continue;
-    const int f = w + 4 * i;
-#pragma unroll
-    for (int tf = 0; tf < 2; ++tf)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) lgs[16 * tf + r16][16 * f + 4 * g + q] = acc[i][tf][q];
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int e = 32 * w + 8 * i + 4 * g + j;
+      if (e < E) lgs[r32][e] = acc[0][4 * i + j];
+    }
   __syncthreads();
 
-  for (int tt = w; tt < BT; tt += 4) {
+  for (int tt = w; tt < BT; tt += kThreads / kWave) {
     const int t = t0 + tt;
     if (t >= T) break;
     float lg[4];
@@ -335,7 +275,7 @@ hipError_t launch_route(const moe_config& c, const void* x, const void* wr, cons
   if (err != hipSuccess || c.num_tokens == 0) return err;
   const int T = c.num_tokens, d = c.hidden, E = c.num_experts, K = c.top_k;
   if (route_uses_fused(c)) {
-    hipLaunchKernelGGL(route_fused_bf16, dim3((T + kFusedTokens - 1) / kFusedTokens), dim3(256),
+    hipLaunchKernelGGL(route_fused_bf16, dim3((T + kFusedTokens - 1) / kFusedTokens), dim3(kThreads),
                        0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
                        bias, T, d, E, K, c.score_fn, c.norm, topk_idx, topk_gate, load);
     return hipGetLastError();
