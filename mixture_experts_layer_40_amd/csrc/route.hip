@@ -230,14 +230,25 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
   __syncthreads();
   const int t = blockIdx.x * 4 + wave_id();
   if (t < T) {
-    float lg[4];
+    // the splits are summed in order; the loads of 8 splits are issued
+    // together (a split-serial loop would wait one memory latency per split)
+    float lg[4] = {0.f, 0.f, 0.f, 0.f};
+    const size_t zs = static_cast<size_t>(T) * E;
+    const float* base = part + static_cast<size_t>(t) * E;
+    for (int z0 = 0; z0 < splits; z0 += 8) {
+      float v[8][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = l + 64 * j;
-      float v = 0.f;
-      if (e < E)
-        for (int z = 0; z < splits; ++z) v += part[(static_cast<size_t>(z) * T + t) * E + e];
-      lg[j] = v;
+      for (int z = 0; z < 8; ++z)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = l + 64 * j;
+          v[z][j] = (z0 + z < splits && e < E) ? base[(z0 + z) * zs + e] : 0.f;
+        }
+#pragma unroll
+      for (int z = 0; z < 8; ++z)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (z0 + z < splits) lg[j] += v[z][j];
     }
     topk_token(lg, t, E, K, score_fn, norm, bias, topk_idx, topk_gate, hist);
   }
