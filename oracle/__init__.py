@@ -33,6 +33,7 @@ from .moe import (  # noqa: F401
     router_logits,
     scores,
     select_topk,
+    select_groups,
     gate_values,
     expert_loads,
     permutation,

@@ -88,6 +88,35 @@ def select_topk(keys: np.ndarray, K: int):
     return sel.astype(np.int64), gap
 
 
+def select_groups(s: np.ndarray, G: int, M: int):
+    """Node-limited routing ("DeepSeekMoE架构解析" section 2.3): the E routed
+    experts form G groups of E/G consecutive experts (group g holds experts
+    g*E/G .. (g+1)*E/G - 1, the experts one node hosts); a group's affinity is
+    the sum of its experts' affinity scores s; each token keeps the M groups
+    of largest affinity (lower group index first among equal sums) and its
+    top-K is then taken only among the experts of those groups.
+
+    Returns (allowed [T, E] bool, group_scores [T, G], group_gap [T]) where
+    group_gap is the M-th largest group affinity minus the (M+1)-th (+inf
+    when M == G)."""
+    s = np.asarray(s, dtype=np.float64)
+    T, E = s.shape
+    if G < 1 or E % G != 0 or not (1 <= M <= G):
+        raise ValueError("need E % G == 0 and 1 <= M <= G")
+    n = E // G
+    gs = s.reshape(T, G, n).sum(axis=2)
+    order = np.argsort(-gs, axis=1, kind="stable")
+    keep = np.zeros((T, G), dtype=bool)
+    np.put_along_axis(keep, order[:, :M], True, axis=1)
+    if M < G:
+        mth = np.take_along_axis(gs, order[:, M - 1:M], axis=1)[:, 0]
+        nxt = np.take_along_axis(gs, order[:, M:M + 1], axis=1)[:, 0]
+        ggap = mth - nxt
+    else:
+        ggap = np.full(T, np.inf)
+    return np.repeat(keep, n, axis=1), gs, ggap
+
+
 def gate_values(s: np.ndarray, sel: np.ndarray, norm: str) -> np.ndarray:
     """g_{i,t} for the selected experts. "selected": eq. (13), each selected
     score divided by the sum of the selected scores (so the K gates sum to 1).
@@ -136,16 +165,34 @@ def swiglu_expert(v: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray)
 
 
 def route(x: np.ndarray, wr: np.ndarray, bias: Optional[np.ndarray], K: int,
-          score_fn: str, norm: str) -> dict:
+          score_fn: str, norm: str, groups: Optional[tuple] = None) -> dict:
     """Gating of section 2.1/2.2 for every token: scores, biased top-K,
-    gates from the unbiased scores, loads and the near-tie gap."""
+    gates from the unbiased scores, loads and the near-tie gap.
+
+    groups = (G, M): node-limited routing of section 2.3 (select_groups) before
+    the top-K; the group choice uses the affinity scores themselves (the bias
+    of section 2.2 enters the expert choice only). A token is a near-tie when
+    either its K-th and (K+1)-th allowed keys or its M-th and (M+1)-th group
+    affinities differ by less than NEAR_TIE_GAP."""
     s = scores(router_logits(x, wr), score_fn)
     keys = s if bias is None else s + np.asarray(bias, dtype=np.float64)[None, :]
-    sel, gap = select_topk(keys, K)
+    out = {}
+    near = np.zeros(s.shape[0], dtype=bool)
+    cand = keys
+    if groups is not None and groups[0] > 1:
+        G, M = groups
+        allowed, gs, ggap = select_groups(s, G, M)
+        if M * (s.shape[1] // G) < K:
+            raise ValueError("the kept groups hold fewer than K experts")
+        cand = np.where(allowed, keys, -np.inf)
+        near |= ggap < NEAR_TIE_GAP
+        out.update({"allowed": allowed, "group_scores": gs, "group_gap": ggap})
+    sel, gap = select_topk(cand, K)
+    near |= gap < NEAR_TIE_GAP
     g = gate_values(s, sel, norm)
-    return {"scores": s, "keys": keys, "sel": sel, "gate": g,
-            "load": expert_loads(sel, s.shape[1]), "gap": gap,
-            "near_tie": gap < NEAR_TIE_GAP}
+    out.update({"scores": s, "keys": keys, "sel": sel, "gate": g,
+                "load": expert_loads(sel, s.shape[1]), "gap": gap, "near_tie": near})
+    return out
 
 
 @dataclass

@@ -418,3 +418,95 @@ def test_near_tie_flag_threshold():
     keys = np.array([[1.0, 0.5, 0.5 - 2e-5, 0.0], [1.0, 0.5, 0.5 - 5e-6, 0.0]])
     sel, gap = oracle.select_topk(keys, 2)
     assert (gap < oracle.NEAR_TIE_GAP).tolist() == [False, True]
+
+
+# ---- node-limited (group-limited) routing ("DeepSeekMoE架构解析" section 2.3) ----
+
+def _rand_route_inputs(rng, T, E, d=16):
+    return rng.standard_normal((T, d)), rng.standard_normal((E, d)) * 0.5
+
+
+def test_groups_all_kept_is_plain_topk():
+    rng = np.random.default_rng(11)
+    x, wr = _rand_route_inputs(rng, 50, 32)
+    b = rng.uniform(-0.05, 0.05, 32)
+    a = oracle.route(x, wr, b, 6, "sigmoid", "selected")
+    for groups in ((8, 8), (1, 1)):
+        g = oracle.route(x, wr, b, 6, "sigmoid", "selected", groups=groups)
+        assert np.array_equal(a["sel"], g["sel"]) and np.array_equal(a["gate"], g["gate"])
+
+
+def test_groups_containing_global_topk_change_nothing():
+    """When the kept groups hold the plain top-K, the group limit is moot."""
+    rng = np.random.default_rng(12)
+    x, wr = _rand_route_inputs(rng, 400, 64)
+    b = rng.uniform(-0.05, 0.05, 64)
+    plain = oracle.route(x, wr, b, 8, "sigmoid", "selected")
+    grp = oracle.route(x, wr, b, 8, "sigmoid", "selected", groups=(8, 4))
+    inside = np.all(np.take_along_axis(grp["allowed"], plain["sel"], axis=1), axis=1)
+    assert 0 < inside.sum() < len(inside)          # both kinds of token occur
+    assert np.array_equal(plain["sel"][inside], grp["sel"][inside])
+    assert not np.array_equal(plain["sel"][~inside], grp["sel"][~inside])
+    # every selected expert lies in a kept group, at most M groups are used
+    assert np.all(np.take_along_axis(grp["allowed"], grp["sel"], axis=1))
+    assert max(len(set((grp["sel"][t] // 8).tolist())) for t in range(400)) <= 4
+
+
+def test_groups_against_pairwise_count_definition():
+    """Brute force with ties: a group is kept iff fewer than M groups beat it
+    (larger sum, or equal sum and lower index); an expert is chosen iff it is
+    allowed and fewer than K allowed experts beat it the same way."""
+    rng = np.random.default_rng(13)
+    E, G, M, K = 12, 4, 2, 3
+    n = E // G
+    for _ in range(300):
+        s = rng.integers(0, 4, size=(1, E)) / 8.0          # coarse values: many ties
+        keys = s + rng.integers(0, 3, size=(1, E)) / 16.0
+        allowed, gs, _ = oracle.select_groups(s, G, M)
+        kept = [g for g in range(G)
+                if sum(gs[0, h] > gs[0, g] or (gs[0, h] == gs[0, g] and h < g) for h in range(G)) < M]
+        want_allowed = np.array([e // n in kept for e in range(E)])
+        assert np.array_equal(allowed[0], want_allowed)
+        cand = np.where(allowed, keys, -np.inf)
+        sel, _ = oracle.select_topk(cand, K)
+        chosen = [e for e in range(E) if want_allowed[e] and sum(
+            want_allowed[f] and (keys[0, f] > keys[0, e] or (keys[0, f] == keys[0, e] and f < e))
+            for f in range(E)) < K]
+        assert sorted(sel[0].tolist()) == chosen
+
+
+def test_groups_hand_example_sum_not_max_and_bias_outside():
+    """E = 8 in G = 4 groups of 2, M = 2, K = 2. Group sums 1.0, 0.95, 0.96,
+    0.5: groups 0 and 2 are kept (by the sum; the maxima 0.9, 0.5, 0.48, 0.3
+    would keep 0 and 1). Plain top-2 is {0, 2}; group-limited top-2 is {0, 4}
+    (experts 4 and 5 tie at 0.48: the lower index wins). A bias on expert 2
+    (group 1, not kept) cannot bring it back: the bias is not part of the
+    group affinity."""
+    s = np.array([[0.9, 0.1, 0.5, 0.45, 0.48, 0.48, 0.2, 0.3]])
+    allowed, gs, ggap = oracle.select_groups(s, 4, 2)
+    assert np.allclose(gs[0], [1.0, 0.95, 0.96, 0.5])
+    assert allowed[0].tolist() == [True, True, False, False, True, True, False, False]
+    assert abs(ggap[0] - 0.01) < 1e-12
+    x1 = np.log(s / (1.0 - s))               # one token whose logits (x1 @ I) give s
+    r = oracle.route(x1, np.eye(8), None, 2, "sigmoid", "selected", groups=(4, 2))
+    assert sorted(r["sel"][0].tolist()) == [0, 4]
+    assert np.allclose(r["gate"][0], np.array([0.9, 0.48]) / 1.38)
+    plain = oracle.route(x1, np.eye(8), None, 2, "sigmoid", "selected")
+    assert sorted(plain["sel"][0].tolist()) == [0, 2]
+    bias = np.zeros(8)
+    bias[2] = 5.0
+    rb = oracle.route(x1, np.eye(8), bias, 2, "sigmoid", "selected", groups=(4, 2))
+    assert sorted(rb["sel"][0].tolist()) == [0, 4]
+    assert sorted(oracle.route(x1, np.eye(8), bias, 2, "sigmoid", "selected")["sel"][0].tolist()) == [0, 2]
+
+
+def test_groups_near_tie_flag_and_capacity_check():
+    s_eq = np.array([[0.5, 0.5, 0.25, 0.75, 0.1, 0.2]])      # groups of 2: sums 1.0, 1.0, 0.3
+    _, _, ggap = oracle.select_groups(s_eq, 3, 1)
+    assert ggap[0] == 0.0
+    logits = np.log(s_eq / (1.0 - s_eq))
+    r = oracle.route(logits, np.eye(6), None, 2, "sigmoid", "selected", groups=(3, 1))
+    assert r["near_tie"][0]
+    assert sorted(r["sel"][0].tolist()) == [0, 1]     # group 0 wins the tie (lower index)
+    with pytest.raises(ValueError):
+        oracle.route(logits, np.eye(6), None, 3, "sigmoid", "selected", groups=(3, 1))
