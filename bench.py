@@ -13,8 +13,9 @@ expert weights relocated once into the tiled layout before timing.
 
 Printed: one JSON line with tokens/s, the roofline of the dominant kernel
 (the grouped gate/up GEMM, timed live with HIP events on its stream), the
-decode workload's fraction of HBM peak, and the fp64 oracle timed on a
-bounded sample on the host's cores.
+decode workload's fraction of HBM peak, the same prefill layer with
+node-limited routing (8 groups, top-4 groups), and the fp64 oracle timed on
+a bounded sample on the host's cores.
 """
 
 from __future__ import annotations
@@ -39,6 +40,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 WORKLOAD = "v3_prefill_bf16"
 DECODE = "v3_decode_fp8"
+GROUPED = "v3_grouped_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
                   for f in ("ffn.hip", "common.hpp")]
@@ -213,6 +215,32 @@ def decode_measure(steps, warmup):
     return out
 
 
+def route_ms(layer, x, bias, iters=20) -> float:
+    layer.route(x, bias)
+    torch.cuda.synchronize()
+    t = Timed()
+    for _ in range(iters):
+        with t:
+            layer.route(x, bias)
+    torch.cuda.synchronize()
+    return t.mean_ms()
+
+
+def grouped_measure(steps, warmup, plain_route_ms):
+    """The V3 prefill layer with node-limited routing (8 groups of 32 experts,
+    top-4 groups): layer throughput and the router's own time."""
+    spec = synth.get_config(GROUPED)
+    inp, layer, bufs = setup(spec)
+    x, bias = inp["x"], inp["bias"]
+    sec = time_steps(layer, x, bias, bufs, steps, warmup)
+    out = {"workload": GROUPED, "groups": spec.n_groups, "topk_groups": spec.topk_groups,
+           "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
+           "route_ms": route_ms(layer, x, bias), "route_ms_without_groups": plain_route_ms}
+    del inp, layer, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +249,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before timing, run one 1 GiB read + 1 GiB write elementwise kernel, "
                          "the known-size reference for HBM byte counters")
@@ -285,6 +314,8 @@ def main():
                      "mfma_TFLOPs": achieved, "mfma_peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac": achieved / MFMA_BF16_PEAK_TFLOPS},
     }
+    plain_route = route_ms(layer, x, bias)
+    result["route_ms"] = plain_route
     if not args.no_cpu_baseline:
         log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(spec, inp, layer, args.cpu_tokens)
@@ -293,6 +324,9 @@ def main():
     if not args.no_decode:
         log(f"[bench] decode workload {DECODE}")
         result["decode"] = decode_measure(args.steps, args.warmup)
+    if not args.no_grouped:
+        log(f"[bench] node-limited routing workload {GROUPED}")
+        result["grouped"] = grouped_measure(args.steps, args.warmup, plain_route)
     print(json.dumps(result), flush=True)
 
 

@@ -117,6 +117,11 @@ typedef struct moe_config {
                             unchanged. Same results bit for bit; each weight load
                             then reads whole 1 KB stripes, which HBM serves faster
                             than the rows layout's 64-byte pieces of 32 rows. */
+  int32_t num_groups;    /* G: node-limited routing ([DSMoE] section 2.3) when > 1: the
+                            E experts form G groups of E/G consecutive experts; 0 or 1
+                            = no group limit. Requires E % G == 0 and G <= 64.       */
+  int32_t topk_groups;   /* M: groups kept per token (1..G, with M * E/G >= K); used
+                            only when num_groups > 1.                                */
 } moe_config;
 
 /* Validate a configuration without touching the GPU. Returns a status code. */
@@ -161,7 +166,12 @@ int moe_pack_weights(int which, int32_t groups, int32_t rows, int32_t cols, int3
  *   s[t,i]      = sigmoid(logits) or softmax_i(logits)  (cfg->score_fn)
  *   key[t,i]    = s[t,i] + bias[i]   (bias == NULL: key = s)
  *   topk_idx[t] = the K experts with the largest key, in key-descending
- *                 order, the lower expert index first among equal keys
+ *                 order, the lower expert index first among equal keys;
+ *                 with num_groups = G > 1 ([DSMoE] section 2.3): group g =
+ *                 experts g*E/G .. (g+1)*E/G - 1 has affinity sum_{i in g}
+ *                 s[t,i] (scores, without the bias), the topk_groups groups
+ *                 of largest affinity are kept (lower group index first
+ *                 among equal sums) and the K experts are taken among theirs
  *   topk_gate[t,k] = s[t, topk_idx[t,k]] / sum_k' s[t, topk_idx[t,k']]
  *                 (MOE_NORM_SELECTED) or s[t, topk_idx[t,k]] (MOE_NORM_NONE);
  *                 the bias never enters the gate values

@@ -63,7 +63,8 @@ class moe_config(ctypes.Structure):
                 ("shared_inter", ctypes.c_int32), ("score_fn", ctypes.c_int32),
                 ("norm", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("num_groups", ctypes.c_int32),
+                ("topk_groups", ctypes.c_int32)]
 
 
 _DT = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3}
@@ -73,20 +74,24 @@ _LA = {"rows": MOE_LAYOUT_ROWS, "tiled": MOE_LAYOUT_TILED}
 
 
 def make_config(T, d, E, K, I, S=0, Is=0, score="sigmoid", norm="selected", act_dtype="bf16",
-                weight_dtype="bf16", out_dtype="f32", weight_layout="rows") -> moe_config:
+                weight_dtype="bf16", out_dtype="f32", weight_layout="rows", n_groups=0,
+                topk_groups=0) -> moe_config:
     return moe_config(int(T), int(d), int(E), int(K), int(I), int(S), int(Is),
                       _SC.get(score, score), _NO.get(norm, norm),
                       _DT.get(act_dtype, act_dtype), _DT.get(weight_dtype, weight_dtype),
-                      _DT.get(out_dtype, out_dtype), _LA.get(weight_layout, weight_layout))
+                      _DT.get(out_dtype, out_dtype), _LA.get(weight_layout, weight_layout),
+                      int(n_groups), int(topk_groups))
 
 
 def config_of(spec, T: Optional[int] = None, weight_layout: str = "rows") -> moe_config:
     """moe_config from any object with the fields T, d, E, K, I, S, Is, score,
-    norm, act_dtype, weight_dtype (and optionally out_dtype, default fp32),
-    e.g. a workload description."""
+    norm, act_dtype, weight_dtype (and optionally out_dtype, default fp32, and
+    n_groups / topk_groups, default no group limit), e.g. a workload
+    description."""
     return make_config(spec.T if T is None else T, spec.d, spec.E, spec.K, spec.I, spec.S,
                        spec.Is, spec.score, spec.norm, spec.act_dtype, spec.weight_dtype,
-                       getattr(spec, "out_dtype", "f32"), weight_layout)
+                       getattr(spec, "out_dtype", "f32"), weight_layout,
+                       getattr(spec, "n_groups", 0), getattr(spec, "topk_groups", 0))
 
 
 _lib = None

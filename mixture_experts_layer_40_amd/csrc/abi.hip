@@ -73,6 +73,13 @@ int moe_validate(const moe_config* c) {
   }
   const int64_t tk = static_cast<int64_t>(c->num_tokens) * c->top_k;
   if (tk >= (1LL << 30)) return MOE_ERR_SHAPE;
+  if (c->num_groups < 0) return MOE_ERR_SHAPE;
+  if (c->num_groups > 1) {
+    const int G = c->num_groups, M = c->topk_groups;
+    if (G > 64 || c->num_experts % G != 0) return MOE_ERR_SHAPE;
+    if (M < 1 || M > G || static_cast<int64_t>(M) * (c->num_experts / G) < c->top_k)
+      return MOE_ERR_SHAPE;
+  }
   return MOE_OK;
 }
 

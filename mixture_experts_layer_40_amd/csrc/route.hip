@@ -35,10 +35,13 @@ __device__ __forceinline__ float pick4(const float (&v)[4], int j) {
 }
 
 // Scores, top-K, gates for one token on one wave. lg[j] is the logit of
-// expert (lane + 64 j); entries with expert >= E are ignored.
-__device__ void topk_token(const float (&lg)[4], int t, int E, int K, int score_fn, int norm,
-                           const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
-                           float* __restrict__ topk_gate, int* hist) {
+// expert (lane + 64 j); entries with expert >= E are ignored. G > 1: only the
+// experts of the M groups with the largest score sums take part
+// ("DeepSeekMoE架构解析" section 2.3, node-limited routing).
+__device__ void topk_token(const float (&lg)[4], int t, int E, int K, int G, int M, int score_fn,
+                           int norm, const float* __restrict__ bias,
+                           int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+                           int* hist) {
   const int l = lane_id();
   float s[4], key[4];
   if (score_fn == MOE_SCORE_SIGMOID) {
@@ -64,6 +67,38 @@ __device__ void topk_token(const float (&lg)[4], int t, int E, int K, int score_
   for (int j = 0; j < 4; ++j) {
     const int e = l + 64 * j;
     key[j] = e < E ? (bias ? s[j] + bias[e] : s[j]) : -INFINITY;
+  }
+  if (G > 1) {
+    // group affinity = sum of its experts' scores; lane g ends with group g's
+    const int n = E / G;
+    int grp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) grp[j] = (l + 64 * j) < E ? (l + 64 * j) / n : -1;
+    float gsum = -INFINITY;
+    for (int gi = 0; gi < G; ++gi) {
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part += grp[j] == gi ? s[j] : 0.f;
+      const float tot = wave_sum(part);
+      if (l == gi) gsum = tot;
+    }
+    // keep the M largest (ties: lower group index)
+    uint64_t keep = 0;
+    for (int r = 0; r < M; ++r) {
+      float bv = gsum;
+      int bi = l;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (key_better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      keep |= 1ull << bi;
+      if (l == bi) gsum = -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (grp[j] >= 0 && !((keep >> grp[j]) & 1ull)) key[j] = -INFINITY;
   }
 
   int rec_idx[4] = {0, 0, 0, 0};
@@ -116,8 +151,9 @@ __device__ void topk_token(const float (&lg)[4], int t, int E, int K, int score_
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void route_fused_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, int K, int score_fn, int norm,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ load) {
+    const float* __restrict__ bias, int T, int d, int E, int K, int G, int M, int score_fn,
+    int norm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    int32_t* __restrict__ load) {
   constexpr int BT = kFusedTokens;
   __shared__ __attribute__((aligned(16))) uint16_t bs0[BT * 64];
   __shared__ __attribute__((aligned(16))) uint16_t bs1[BT * 64];
@@ -155,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void route_fused_bf16(
       const int e = l + 64 * j;
       lg[j] = e < E ? lgs[tt][e] : 0.f;
     }
-    topk_token(lg, t, E, K, score_fn, norm, bias, topk_idx, topk_gate, hist);
+    topk_token(lg, t, E, K, G, M, score_fn, norm, bias, topk_idx, topk_gate, hist);
   }
   __syncthreads();
   if (tid < E && hist[tid] > 0) atomicAdd(&load[tid], hist[tid]);
@@ -220,7 +256,7 @@ __global__ __launch_bounds__(256) void route_logits_f32(const float* __restrict_
 // (one wave per token) and the block's load histogram.
 __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part, int splits,
                                                   const float* __restrict__ bias, int T, int E,
-                                                  int K, int score_fn, int norm,
+                                                  int K, int G, int M, int score_fn, int norm,
                                                   int32_t* __restrict__ topk_idx,
                                                   float* __restrict__ topk_gate,
                                                   int32_t* __restrict__ load) {
@@ -250,7 +286,7 @@ __global__ __launch_bounds__(256) void route_topk(const float* __restrict__ part
         for (int j = 0; j < 4; ++j)
           if (z0 + z < splits) lg[j] += v[z][j];
     }
-    topk_token(lg, t, E, K, score_fn, norm, bias, topk_idx, topk_gate, hist);
+    topk_token(lg, t, E, K, G, M, score_fn, norm, bias, topk_idx, topk_gate, hist);
   }
   __syncthreads();
   if (tid < E && hist[tid] > 0) atomicAdd(&load[tid], hist[tid]);
@@ -285,10 +321,12 @@ hipError_t launch_route(const moe_config& c, const void* x, const void* wr, cons
   hipError_t err = launch_fill_i32(load, 0, c.num_experts, s);
   if (err != hipSuccess || c.num_tokens == 0) return err;
   const int T = c.num_tokens, d = c.hidden, E = c.num_experts, K = c.top_k;
+  const int G = c.num_groups > 1 ? c.num_groups : 1;
+  const int M = G > 1 ? c.topk_groups : 1;
   if (route_uses_fused(c)) {
     hipLaunchKernelGGL(route_fused_bf16, dim3((T + kFusedTokens - 1) / kFusedTokens), dim3(kThreads),
                        0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                       bias, T, d, E, K, c.score_fn, c.norm, topk_idx, topk_gate, load);
+                       bias, T, d, E, K, G, M, c.score_fn, c.norm, topk_idx, topk_gate, load);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(ws);
@@ -309,7 +347,7 @@ hipError_t launch_route(const moe_config& c, const void* x, const void* wr, cons
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_topk, dim3((T + 3) / 4), dim3(256), 0, s, part, splits, bias, T, E, K,
-                     c.score_fn, c.norm, topk_idx, topk_gate, load);
+                     G, M, c.score_fn, c.norm, topk_idx, topk_gate, load);
   return hipGetLastError();
 }
 

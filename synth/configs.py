@@ -45,6 +45,10 @@ class MoEConfig:
     zipf_A: Optional[float] = None
     batches: int = 1
     gamma: float = 1e-3
+    # node-limited routing ("DeepSeekMoE" explainer, section 2.3): experts in
+    # n_groups groups of E/n_groups, topk_groups groups kept per token (0 = off)
+    n_groups: int = 0
+    topk_groups: int = 0
     description: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -111,6 +115,12 @@ CONFIGS = {
         bias_range=None, x_std=1.0, w_std=0.02, seed=_BASE + 5,
         zipf_s=1.1, zipf_A=2.3828, batches=20, gamma=1e-3,   # A: oracle/calibrate_zipf.py
         description="Zipf(1.1) expert popularity (hottest ~10x mean load), 20 batches + bias update",
+    ),
+    "v3_grouped_bf16": MoEConfig(
+        name="v3_grouped_bf16", T=8192, d=7168, E=256, K=8, I=2048, S=1, Is=2048,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="bf16",
+        bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 6, n_groups=8, topk_groups=4,
+        description="V3-shape prefill with node-limited routing: 8 groups of 32 experts, top-4 groups",
     ),
 }
 

@@ -69,10 +69,16 @@ def run_steps(spec, inp, bias=None, x=None, layer=None, side_stream=False, fused
     }
 
 
+def groups_of(spec):
+    G = getattr(spec, "n_groups", 0)
+    return (G, spec.topk_groups) if G > 1 else None
+
+
 def oracle_route(spec, x, wr, bias, rows=None):
     x64 = f64(x) if rows is None else f64(x[rows])
     b64 = None if bias is None else bias.detach().cpu().numpy().astype(np.float64)
-    return oracle.route(x64, f64(wr), b64, spec.K, spec.score, spec.norm), x64
+    return oracle.route(x64, f64(wr), b64, spec.K, spec.score, spec.norm,
+                        groups=groups_of(spec)), x64
 
 
 def check_route(spec, r, idx, gate, load=None, rows=None):
@@ -96,8 +102,24 @@ def check_route(spec, r, idx, gate, load=None, rows=None):
     keys = r["keys"]
     kth = np.take_along_axis(keys, r["sel"][:, K - 1:K], axis=1)[:, 0]
     chosen = np.take_along_axis(keys, idx_r, axis=1)
-    if near.any():
+    grp = groups_of(spec)
+    if near.any() and grp is None:
         assert np.all(chosen[near] >= kth[near, None] - oracle.NEAR_TIE_GAP), "invalid near-tie selection"
+    elif near.any():
+        # node-limited: the GPU's experts come from at most M groups, each of
+        # them within the tolerance of the M-th group affinity, and they are
+        # the top K (within the tolerance) of the experts of the groups used
+        G, M = grp
+        n = E // G
+        gs = r["group_scores"]
+        mth = -np.sort(-gs, axis=1)[:, M - 1]
+        for t in np.flatnonzero(near):
+            used = np.unique(idx_r[t] // n)
+            assert len(used) <= M, "more than M groups used"
+            assert np.all(gs[t, used] >= mth[t] - oracle.NEAR_TIE_GAP), "invalid near-tie group"
+            pool = np.concatenate([np.arange(g * n, (g + 1) * n) for g in used])
+            kth_pool = np.sort(keys[t, pool])[::-1][K - 1]
+            assert np.all(keys[t, idx_r[t]] >= kth_pool - oracle.NEAR_TIE_GAP), "invalid near-tie selection"
     g_or = oracle.gate_values(r["scores"], idx_r, spec.norm)
     err = np.abs(gate_r - g_or).max()
     assert err <= GATE_ATOL, f"gate error {err}"

@@ -63,10 +63,23 @@ def test_validate_accepts_named_workload_shapes():
     (dict(out_dtype="fp8"), L.MOE_ERR_DTYPE),
     (dict(act_dtype="bf16", weight_dtype="bf16", out_dtype=5), L.MOE_ERR_DTYPE),
     (dict(weight_layout=7), L.MOE_ERR_SHAPE),
+    (dict(n_groups=3, topk_groups=1), L.MOE_ERR_SHAPE),      # E = 16 not a multiple of 3
+    (dict(n_groups=4, topk_groups=0), L.MOE_ERR_SHAPE),
+    (dict(n_groups=4, topk_groups=5), L.MOE_ERR_SHAPE),
+    (dict(n_groups=8, topk_groups=1, K=3), L.MOE_ERR_SHAPE),  # 1 group of 2 experts < K
+    (dict(E=256, K=8, n_groups=128, topk_groups=8), L.MOE_ERR_SHAPE),   # more than 64 groups
+    (dict(n_groups=-1), L.MOE_ERR_SHAPE),
     (dict(weight_layout="tiled"), L.MOE_ERR_DTYPE),   # fp32 weights have no tiled form
 ])
 def test_validate_rejects(kw, status):
     assert moe.moe_validate(_cfg(**kw)) == status
+
+
+def test_validate_accepts_group_limits():
+    for kw in (dict(n_groups=4, topk_groups=2), dict(n_groups=1, topk_groups=0),
+               dict(n_groups=0, topk_groups=9), dict(n_groups=8, topk_groups=1, K=2),
+               dict(E=256, K=8, n_groups=64, topk_groups=2)):
+        assert moe.moe_validate(_cfg(**kw)) == L.MOE_OK, kw
 
 
 def test_validate_null():

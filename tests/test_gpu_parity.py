@@ -50,6 +50,15 @@ CASES = {
     "e20": _cfg("v3_prefill_bf16", T=129, d=64, E=20, K=5, I=64, Is=64),
     "one_token": _cfg("v3_prefill_bf16", T=1, d=128, E=256, K=8, I=64, Is=64),
     "one_expert": _cfg("v3_prefill_bf16", T=33, d=64, E=1, K=1, I=64, S=0, Is=0),
+    # node-limited routing: split-K router, fused router (T >= 4096), softmax
+    # scores, a single kept group
+    "grouped_small": _cfg("v3_prefill_bf16", T=300, d=256, E=64, K=6, I=128, Is=128,
+                          n_groups=8, topk_groups=3),
+    "grouped_fused": _cfg("v3_grouped_bf16", T=4100, d=128, E=256, K=8, I=128, Is=128),
+    "grouped_softmax": _cfg("dsmoe2024_bf16", T=200, d=128, E=64, K=6, I=128, Is=128,
+                            n_groups=4, topk_groups=2),
+    "grouped_m1": _cfg("v3_prefill_bf16", T=150, d=128, E=32, K=4, I=64, Is=64,
+                       n_groups=4, topk_groups=1),
 }
 
 
