@@ -36,6 +36,7 @@ from .moe import (  # noqa: F401
     select_groups,
     gate_values,
     expert_loads,
+    sequence_loads,
     permutation,
     silu,
     swiglu_expert,

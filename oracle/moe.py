@@ -120,13 +120,34 @@ def select_groups(s: np.ndarray, G: int, M: int):
 def gate_values(s: np.ndarray, sel: np.ndarray, norm: str) -> np.ndarray:
     """g_{i,t} for the selected experts. "selected": eq. (13), each selected
     score divided by the sum of the selected scores (so the K gates sum to 1).
-    "none": the 2024 layout, the selected scores themselves."""
+    "none": the 2024 layout, the selected scores themselves. "one_plus": the
+    weighting of "DeepSeek-V3：MoE大模型架构" (section 路由机制 and its Python
+    demo), each selected score divided by 1 + the sum of the selected scores,
+    the 1 standing for the always-on shared expert (so the gates sum to
+    sum/(1 + sum) < 1)."""
     s_sel = np.take_along_axis(np.asarray(s, dtype=np.float64), sel, axis=1)
     if norm == "selected":
         return s_sel / s_sel.sum(axis=1, keepdims=True)
     if norm == "none":
         return s_sel
+    if norm == "one_plus":
+        return s_sel / (1.0 + s_sel.sum(axis=1, keepdims=True))
     raise ValueError(norm)
+
+
+def sequence_loads(sel: np.ndarray, E: int, seq_len: int) -> np.ndarray:
+    """Per-sequence expert loads: the batch's tokens taken as consecutive
+    sequences of seq_len tokens (the last one may be shorter); entry [q, e]
+    counts the (token, slot) pairs of sequence q routed to expert e (the
+    per-sequence counterpart of the batch load, for sequence-wise balance
+    statistics: course notes "省钱第一招", section 五)."""
+    sel = np.asarray(sel)
+    T = sel.shape[0]
+    nq = -(-T // seq_len)
+    out = np.zeros((nq, E), dtype=np.int64)
+    for q in range(nq):
+        out[q] = expert_loads(sel[q * seq_len:(q + 1) * seq_len], E)
+    return out
 
 
 def expert_loads(sel: np.ndarray, E: int) -> np.ndarray:

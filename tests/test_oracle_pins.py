@@ -510,3 +510,39 @@ def test_groups_near_tie_flag_and_capacity_check():
     assert sorted(r["sel"][0].tolist()) == [0, 1]     # group 0 wins the tie (lower index)
     with pytest.raises(ValueError):
         oracle.route(logits, np.eye(6), None, 3, "sigmoid", "selected", groups=(3, 1))
+
+
+# ---- "1 + sum" gate weighting and per-sequence loads ----
+
+def test_one_plus_gates_closed_form():
+    """Scores 1/2, 1/4, 1/4 selected: gates s / (1 + 1) = 1/4, 1/8, 1/8."""
+    s = np.array([[0.5, 0.25, 0.25, 0.1]])
+    sel = np.array([[0, 1, 2]])
+    g = oracle.gate_values(s, sel, "one_plus")
+    assert np.array_equal(g, np.array([[0.25, 0.125, 0.125]]))
+    assert np.array_equal(oracle.gate_values(s, sel, "selected"), np.array([[0.5, 0.25, 0.25]]))
+
+
+def test_one_plus_gates_relations():
+    """g_one_plus = g_selected * S / (1 + S) with S the selected-score sum, so
+    the gates sum to S / (1 + S) < 1; routing is unaffected by the weighting."""
+    rng = np.random.default_rng(21)
+    x, wr = rng.standard_normal((40, 16)), rng.standard_normal((32, 16))
+    a = oracle.route(x, wr, None, 6, "sigmoid", "selected")
+    b = oracle.route(x, wr, None, 6, "sigmoid", "one_plus")
+    assert np.array_equal(a["sel"], b["sel"])
+    S = np.take_along_axis(a["scores"], a["sel"], axis=1).sum(axis=1)
+    assert np.allclose(b["gate"], a["gate"] * (S / (1 + S))[:, None], rtol=1e-14, atol=0)
+    assert np.allclose(b["gate"].sum(axis=1), S / (1 + S), rtol=1e-14, atol=0)
+    assert np.all(b["gate"].sum(axis=1) < 1)
+
+
+def test_sequence_loads_against_bincount():
+    rng = np.random.default_rng(22)
+    sel = np.stack([rng.choice(20, 3, replace=False) for _ in range(53)])
+    q = oracle.sequence_loads(sel, 20, 10)
+    assert q.shape == (6, 20)
+    for i in range(6):
+        assert np.array_equal(q[i], np.bincount(sel[i * 10:(i + 1) * 10].ravel(), minlength=20))
+    assert np.array_equal(q.sum(axis=0), oracle.expert_loads(sel, 20))
+    assert q[5].sum() == 3 * 3                       # the short last sequence
