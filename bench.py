@@ -226,6 +226,21 @@ def route_ms(layer, x, bias, iters=20) -> float:
     return t.mean_ms()
 
 
+def sequence_loads_ms(layer, spec, seq_len, iters=20) -> float:
+    """Per-sequence expert loads of the last routed batch (sequences of seq_len)."""
+    cfg = layer._cfg(spec.T)
+    nq = -(-spec.T // seq_len)
+    out = torch.empty((nq, spec.E), dtype=torch.int32, device="cuda")
+    moe.moe_sequence_loads(cfg, layer.topk_idx[:spec.T], seq_len, out)
+    torch.cuda.synchronize()
+    t = Timed()
+    for _ in range(iters):
+        with t:
+            moe.moe_sequence_loads(cfg, layer.topk_idx[:spec.T], seq_len, out)
+    torch.cuda.synchronize()
+    return t.mean_ms()
+
+
 def grouped_measure(steps, warmup, plain_route_ms):
     """The V3 prefill layer with node-limited routing (8 groups of 32 experts,
     top-4 groups): layer throughput and the router's own time."""
@@ -316,6 +331,7 @@ def main():
     }
     plain_route = route_ms(layer, x, bias)
     result["route_ms"] = plain_route
+    result["sequence_loads_ms"] = sequence_loads_ms(layer, spec, seq_len=4096)
     if not args.no_cpu_baseline:
         log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(spec, inp, layer, args.cpu_tokens)

@@ -9,6 +9,8 @@
  *            normalisation over the selected experts), section 2.2 (eq. 16
  *            and the bias update rule), section 3.1 (layer sketch: router
  *            weights, bias vector, gathered gate values, weighted sum).
+ *   [V3ARCH] "DeepSeek-V3：MoE大模型架构" (aiqz.cc): section 路由机制 and its
+ *            Python demo (selected scores divided by 1 + their sum).
  *   [COURSE] "省钱第一招：把一个大厨换成专家团" (blog.zero43.top): section 三
  *            (2 shared + 64 routed experts, 2+6 active), section 四 (the
  *            2024 gates are not renormalised), section 五 (bias outside the
@@ -73,6 +75,8 @@ extern "C" {
 
 #define MOE_NORM_SELECTED 0  /* g = s / sum of the K selected s ([DSMoE] eq. 13)           */
 #define MOE_NORM_NONE     1  /* g = s of the selected experts ([COURSE] section 四)        */
+#define MOE_NORM_ONE_PLUS_SELECTED 2  /* g = s / (1 + sum of the K selected s) ([V3ARCH]
+                                         section 路由机制 and its demo: the 1 is the shared expert) */
 
 #define MOE_DTYPE_F32      0
 #define MOE_DTYPE_BF16     1
@@ -173,7 +177,9 @@ int moe_pack_weights(int which, int32_t groups, int32_t rows, int32_t cols, int3
  *                 of largest affinity are kept (lower group index first
  *                 among equal sums) and the K experts are taken among theirs
  *   topk_gate[t,k] = s[t, topk_idx[t,k]] / sum_k' s[t, topk_idx[t,k']]
- *                 (MOE_NORM_SELECTED) or s[t, topk_idx[t,k]] (MOE_NORM_NONE);
+ *                 (MOE_NORM_SELECTED), s[t, topk_idx[t,k]] (MOE_NORM_NONE), or
+ *                 s[t, topk_idx[t,k]] / (1 + sum_k' s[t, topk_idx[t,k']])
+ *                 (MOE_NORM_ONE_PLUS_SELECTED);
  *                 the bias never enters the gate values
  *   load[i]     = number of (t, k) with topk_idx[t,k] == i (overwritten;
  *                 sums to T*K: no token is dropped)
@@ -308,6 +314,17 @@ int moe_experts_down(const moe_config* cfg, const void* h, const void* hs,
  * out_slots [T*K, d] act dtype; y_shared [T, d] fp32; y [T, d] out_dtype. */
 int moe_combine(const moe_config* cfg, const void* out_slots, const void* y_shared,
                 void* y, void* stream);
+
+/* ---- moe_sequence_loads ---------------------------------------------------
+ * Per-sequence expert loads, the statistic behind a sequence-wise balance
+ * check ([COURSE] section 五): the T tokens of the batch are taken as
+ * consecutive sequences of seq_len tokens (the last may be shorter) and
+ *   seq_load[q, e] = number of (t, k) with t in sequence q and topk_idx[t,k] == e
+ * (ids outside [0, E) are not counted). topk_idx [T, K] int32 from moe_route;
+ * seq_load [ceil(T / seq_len), E] int32, overwritten. seq_len >= 1.
+ * Integer results are exact. */
+int moe_sequence_loads(const moe_config* cfg, const int32_t* topk_idx, int32_t seq_len,
+                       int32_t* seq_load, void* stream);
 
 /* ---- moe_bias_update ------------------------------------------------------
  * Auxiliary-loss-free balance step of [DSMoE] section 2.2 ([COURSE] section

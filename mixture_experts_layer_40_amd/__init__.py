@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     MOE_LAYOUT_ROWS,
     MOE_LAYOUT_TILED,
     MOE_NORM_NONE,
+    MOE_NORM_ONE_PLUS_SELECTED,
     MOE_NORM_SELECTED,
     MOE_OK,
     MOE_PACK_DOWN,
@@ -50,6 +51,7 @@ from ._lib import (  # noqa: F401
     moe_pack_weights,
     moe_permute,
     moe_route,
+    moe_sequence_loads,
     moe_shared_ffn,
     moe_status_string,
     moe_validate,

@@ -30,6 +30,7 @@ MOE_SCORE_SIGMOID = 0
 MOE_SCORE_SOFTMAX = 1
 MOE_NORM_SELECTED = 0
 MOE_NORM_NONE = 1
+MOE_NORM_ONE_PLUS_SELECTED = 2
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
 MOE_DTYPE_FP8_E4M3 = 2
@@ -47,7 +48,7 @@ MOE_WS_EXPERTS = 5
 EXPORTED = ("moe_validate", "moe_workspace_size", "moe_status_string", "moe_route",
             "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
             "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights",
-            "moe_experts", "moe_experts_gate_up", "moe_experts_down")
+            "moe_experts", "moe_experts_gate_up", "moe_experts_down", "moe_sequence_loads")
 
 
 class MoEError(RuntimeError):
@@ -69,7 +70,7 @@ class moe_config(ctypes.Structure):
 
 _DT = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3}
 _SC = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
-_NO = {"selected": MOE_NORM_SELECTED, "none": MOE_NORM_NONE}
+_NO = {"selected": MOE_NORM_SELECTED, "none": MOE_NORM_NONE, "one_plus": MOE_NORM_ONE_PLUS_SELECTED}
 _LA = {"rows": MOE_LAYOUT_ROWS, "tiled": MOE_LAYOUT_TILED}
 
 
@@ -127,9 +128,11 @@ def load_library(path: str = LIB_PATH):
     lib.moe_experts.argtypes = [CFG] + [P] * 19 + [SZ, P]
     lib.moe_experts_gate_up.argtypes = [CFG] + [P] * 14 + [SZ, P]
     lib.moe_experts_down.argtypes = [CFG] + [P] * 12 + [SZ, P]
+    lib.moe_sequence_loads.argtypes = [CFG, P, I32, P, P]
     for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up",
                "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update",
-               "moe_pack_weights", "moe_experts", "moe_experts_gate_up", "moe_experts_down"):
+               "moe_pack_weights", "moe_experts", "moe_experts_gate_up", "moe_experts_down",
+               "moe_sequence_loads"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -287,3 +290,8 @@ def moe_experts_down(cfg, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w
         ctypes.byref(cfg), _ptr(h), _ptr(hs), _ptr(expert_offsets), _ptr(perm_slot),
         _ptr(topk_gate), _ptr(w2), _ptr(s2), _ptr(w2s), _ptr(s2s), _ptr(out_slots),
         _ptr(y_shared), _ptr(wsb), nbytes, _stream(stream)))
+
+
+def moe_sequence_loads(cfg, topk_idx, seq_len, seq_load, stream=None):
+    _check("moe_sequence_loads", load_library().moe_sequence_loads(
+        ctypes.byref(cfg), _ptr(topk_idx), int(seq_len), _ptr(seq_load), _stream(stream)))

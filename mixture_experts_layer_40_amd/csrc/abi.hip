@@ -60,7 +60,9 @@ int moe_validate(const moe_config* c) {
   if (c->weight_layout == MOE_LAYOUT_TILED && c->weight_dtype == MOE_DTYPE_F32)
     return MOE_ERR_DTYPE;
   if (c->score_fn != MOE_SCORE_SIGMOID && c->score_fn != MOE_SCORE_SOFTMAX) return MOE_ERR_SHAPE;
-  if (c->norm != MOE_NORM_SELECTED && c->norm != MOE_NORM_NONE) return MOE_ERR_SHAPE;
+  if (c->norm != MOE_NORM_SELECTED && c->norm != MOE_NORM_NONE &&
+      c->norm != MOE_NORM_ONE_PLUS_SELECTED)
+    return MOE_ERR_SHAPE;
   if (c->num_tokens < 0) return MOE_ERR_SHAPE;
   if (c->num_experts < 1 || c->num_experts > 256) return MOE_ERR_SHAPE;
   if (c->top_k < 1 || c->top_k > c->num_experts) return MOE_ERR_SHAPE;
@@ -300,6 +302,17 @@ int moe_combine(const moe_config* c, const void* out_slots, const void* y_shared
   if (!out_slots || !y) return MOE_ERR_NULL;
   (void)hipGetLastError();
   return from_hip(launch_combine(*c, out_slots, y_shared, y, as_stream(stream)));
+}
+
+int moe_sequence_loads(const moe_config* c, const int32_t* topk_idx, int32_t seq_len,
+                       int32_t* seq_load, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (seq_len < 1) return MOE_ERR_SHAPE;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!topk_idx || !seq_load) return MOE_ERR_NULL;
+  (void)hipGetLastError();
+  return from_hip(launch_sequence_loads(*c, topk_idx, seq_len, seq_load, as_stream(stream)));
 }
 
 int moe_bias_update(int32_t num_experts, const int32_t* load, float gamma, float* bias,

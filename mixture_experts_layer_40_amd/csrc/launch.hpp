@@ -65,6 +65,9 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
                              const float* s3s, const float* s2s, void* y_shared, void* ws,
                              hipStream_t s);
 
+hipError_t launch_sequence_loads(const moe_config& c, const int32_t* topk_idx, int seq_len,
+                                 int32_t* seq_load, hipStream_t s);
+
 // Rows -> tiled layout of expert weights. which: 0 = gate/up (a = W1, b = W3,
 // each [groups, rows, cols]), 1 = down (a = W2 [groups, rows, cols], b unused).
 hipError_t launch_pack(int which, int64_t groups, int rows, int cols, int wbytes,

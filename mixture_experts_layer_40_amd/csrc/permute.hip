@@ -153,7 +153,36 @@ __global__ __launch_bounds__(256) void perm_gather(const uint8_t* __restrict__ x
   }
 }
 
+// Per-sequence expert histogram: block q counts the ids of tokens
+// q*L .. min(T, (q+1)*L) - 1.
+__global__ __launch_bounds__(256) void seq_hist(const int32_t* __restrict__ idx, int T, int K,
+                                                int E, int L, int32_t* __restrict__ out) {
+  __shared__ int h[256];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int64_t q = blockIdx.x;
+  const int64_t f0 = q * L * K;
+  const int64_t f1 = (q + 1) * L < T ? (q + 1) * L * K : static_cast<int64_t>(T) * K;
+  for (int64_t f = f0 + tid; f < f1; f += 256) {
+    const int e = idx[f];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  if (tid < E) out[q * E + tid] = h[tid];
+}
+
 }  // namespace
+
+hipError_t launch_sequence_loads(const moe_config& c, const int32_t* topk_idx, int seq_len,
+                                 int32_t* seq_load, hipStream_t s) {
+  const int T = c.num_tokens;
+  if (T == 0) return hipSuccess;
+  const int64_t nq = (static_cast<int64_t>(T) + seq_len - 1) / seq_len;
+  hipLaunchKernelGGL(seq_hist, dim3(static_cast<unsigned>(nq)), dim3(256), 0, s, topk_idx, T,
+                     c.top_k, c.num_experts, seq_len, seq_load);
+  return hipGetLastError();
+}
 
 size_t permute_ws_bytes(const moe_config& c) {
   const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;

@@ -136,7 +136,9 @@ __device__ void topk_token(const float (&lg)[4], int t, int E, int K, int G, int
     if (k < K) {
       const size_t o = static_cast<size_t>(t) * K + k;
       topk_idx[o] = rec_idx[j];
-      topk_gate[o] = norm == MOE_NORM_SELECTED ? rec_s[j] / ssum : rec_s[j];
+      topk_gate[o] = norm == MOE_NORM_SELECTED ? rec_s[j] / ssum
+                   : norm == MOE_NORM_ONE_PLUS_SELECTED ? rec_s[j] / (1.0f + ssum)
+                   : rec_s[j];
       atomicAdd(&hist[rec_idx[j]], 1);
     }
   }

@@ -82,6 +82,19 @@ def test_validate_accepts_group_limits():
         assert moe.moe_validate(_cfg(**kw)) == L.MOE_OK, kw
 
 
+def test_one_plus_norm_and_sequence_loads_validate():
+    assert moe.moe_validate(_cfg(norm="one_plus")) == L.MOE_OK
+    assert moe.moe_validate(_cfg(norm=3)) == L.MOE_ERR_SHAPE
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    c = _cfg()
+    assert lib.moe_sequence_loads(ctypes.byref(c), fake, 0, fake, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_sequence_loads(ctypes.byref(c), None, 16, fake, None) == L.MOE_ERR_NULL
+    assert lib.moe_sequence_loads(ctypes.byref(c), fake, 16, None, None) == L.MOE_ERR_NULL
+    assert lib.moe_sequence_loads(ctypes.byref(_cfg(T=0)), None, 16, None, None) == L.MOE_OK
+    assert lib.moe_sequence_loads(ctypes.byref(_cfg(K=99)), fake, 16, fake, None) == L.MOE_ERR_SHAPE
+
+
 def test_validate_null():
     assert L.load_library().moe_validate(None) == L.MOE_ERR_NULL
 

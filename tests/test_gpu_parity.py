@@ -59,6 +59,10 @@ CASES = {
                             n_groups=4, topk_groups=2),
     "grouped_m1": _cfg("v3_prefill_bf16", T=150, d=128, E=32, K=4, I=64, Is=64,
                        n_groups=4, topk_groups=1),
+    # the "1 + sum" gate weighting, split-K and fused (with node-limited) routers
+    "oneplus": _cfg("v3_prefill_bf16", T=400, d=256, E=64, K=6, I=128, Is=128, norm="one_plus"),
+    "oneplus_grouped_fused": _cfg("v3_grouped_bf16", T=4096, d=128, E=256, K=8, I=64, Is=64,
+                                  norm="one_plus"),
 }
 
 
@@ -206,3 +210,24 @@ def test_zipf_trajectory_small():
         ratios.append(load.max() / load.mean())
     say(f"[zipf small] max/mean per batch: {np.round(ratios, 2).tolist()}")
     assert ratios[0] > 3.0            # skewed to begin with
+
+
+@pytest.mark.parametrize("seq_len", [1, 1000, 4099, 5000])
+def test_sequence_loads_match_oracle(seq_len):
+    """moe_sequence_loads against the oracle's per-sequence counts of its own
+    routing: equal on every sequence, up to the (validated) near-tie tokens,
+    each of which can move at most K pairs between experts."""
+    spec = CASES["v3_fused"]
+    inp = synth.make_inputs(spec, "cuda")
+    layer, res = run_steps(spec, inp, bias=inp["bias"])
+    r, _ = oracle_route(spec, inp["x"], inp["wr"], inp["bias"])
+    check_route(spec, r, res["idx"], res["gate"], res["load"])
+    nq = -(-spec.T // seq_len)
+    got = torch.full((nq, spec.E), -7, dtype=torch.int32, device="cuda")
+    moe.moe_sequence_loads(moe.config_of(spec), layer.topk_idx[:spec.T], seq_len, got)
+    got = got.cpu().numpy().astype(np.int64)
+    want = oracle.sequence_loads(r["sel"], spec.E, seq_len)
+    near_per_seq = np.add.reduceat(r["near_tie"].astype(np.int64), np.arange(0, spec.T, seq_len))
+    diff = np.abs(got - want).sum(axis=1)
+    assert np.all(diff <= 2 * spec.K * near_per_seq), (diff.max(), near_per_seq.max())
+    assert np.all(got.sum(axis=1) == np.diff(np.minimum(np.arange(0, nq + 1) * seq_len, spec.T)) * spec.K)
