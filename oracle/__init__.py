@@ -26,10 +26,12 @@ against closed forms, brute force, library routines or invariants; none is
 "parity unpinned".
 """
 
-from .formats import bf16_to_f64, e4m3_to_f64, E4M3_TABLE, decode_stored  # noqa: F401
+from .formats import bf16_to_f64, e4m3_to_f64, E4M3_TABLE, decode_stored, f64_to_bf16_bits  # noqa: F401
 from .moe import (  # noqa: F401
     GAMMA_F32,
     NEAR_TIE_GAP,
+    RMS_EPS,
+    rmsnorm,
     router_logits,
     scores,
     select_topk,

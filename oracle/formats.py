@@ -24,6 +24,24 @@ def bf16_to_f64(u16: np.ndarray) -> np.ndarray:
     return (u16.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (round to nearest, ties to even), in one
+    step from float64: a bf16 number has 8 significant bits and the binary32
+    exponent range, so the spacing at v is 2^(e-8) for |v| in [2^(e-1), 2^e),
+    and never below 2^-133 (the bf16 subnormal spacing). Finite inputs within
+    the binary32 range. Returns the uint16 bit patterns."""
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("finite values only")
+    _, ex = np.frexp(v)
+    q = np.ldexp(1.0, np.maximum(ex - 8, -133))
+    r = np.rint(v / q) * q                     # rint: round half to even
+    r32 = r.astype(np.float32)
+    if not np.array_equal(r32.astype(np.float64), r):
+        raise ValueError("value outside the bf16 range")
+    return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
 def _e4m3_value(code: int) -> float:
     sign = -1.0 if (code >> 7) & 1 else 1.0
     exp = (code >> 3) & 0xF

@@ -44,6 +44,22 @@ GAMMA_F32 = np.float32(1e-3)
 NEAR_TIE_GAP = 1e-5
 
 
+#: RMSNorm epsilon of the MoE layer's norms ("DeepSeekMoE架构解析" section 4.1).
+RMS_EPS = 1e-6
+
+
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float = RMS_EPS) -> np.ndarray:
+    """Pre-MoE RMSNorm ("DeepSeekMoE架构解析" section 4.1 places an RMSNorm
+    before and after the MoE layer, eps 1e-6): u = x / sqrt(mean(x^2) + eps) * w
+    per token, w the per-channel weight. In float64: for bf16 inputs every
+    square is exact and, at the magnitudes used here, so is their sum in any
+    order; the mean, the sum with eps, the square root, the division and the
+    product are each one correctly rounded operation, in this order."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.sum(x * x, axis=-1, keepdims=True) / x.shape[-1]
+    return x / np.sqrt(ms + eps) * np.asarray(w, dtype=np.float64)
+
+
 def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
     """Affinities u_t^T e_i for every token t and routed expert i (eq. 15's
     argument). x: [T, d], wr: [E, d] (one centroid per row) -> [T, E]."""

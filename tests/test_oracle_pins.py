@@ -546,3 +546,55 @@ def test_sequence_loads_against_bincount():
         assert np.array_equal(q[i], np.bincount(sel[i * 10:(i + 1) * 10].ravel(), minlength=20))
     assert np.array_equal(q.sum(axis=0), oracle.expert_loads(sel, 20))
     assert q[5].sum() == 3 * 3                       # the short last sequence
+
+
+# ---- pre-MoE RMSNorm ("DeepSeekMoE架构解析" section 4.1) and fp64 -> bf16 rounding ----
+
+def test_rmsnorm_closed_forms():
+    w = np.array([1.0, 2.0, 0.5, -1.0])
+    u = oracle.rmsnorm(np.full((1, 4), 3.0), w)
+    assert np.allclose(u, 3.0 / np.sqrt(9.0 + 1e-6) * w, rtol=1e-15, atol=0)
+    u0 = oracle.rmsnorm(np.zeros((1, 4)), w)                    # eps keeps it finite
+    assert np.all(u0 == 0.0)
+    us = oracle.rmsnorm(np.full((1, 4), 1e-4), np.ones(4))       # eps dominates
+    assert np.allclose(us, 1e-4 / np.sqrt(1e-8 + 1e-6), rtol=1e-15, atol=0)
+    assert oracle.RMS_EPS == 1e-6
+
+
+def test_rmsnorm_against_torch():
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((20, 96))
+    w = rng.uniform(0.5, 1.5, 96)
+    want = torch.nn.functional.rms_norm(torch.tensor(x), (96,), torch.tensor(w), eps=1e-6).numpy()
+    assert np.allclose(oracle.rmsnorm(x, w), want, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_sum_of_bf16_squares_is_exact():
+    """The premise of computing the mean square in float64: for bf16 inputs of
+    this magnitude the sum of squares has no rounding, whatever the order."""
+    import math
+    rng = np.random.default_rng(32)
+    x = oracle.bf16_to_f64((rng.standard_normal((8, 7168)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    for row in x:
+        sq = row * row
+        assert float(np.sum(sq)) == math.fsum(sq.tolist()) == float(np.sum(sq[::-1]))
+
+
+def test_f64_to_bf16_rounding():
+    rng = np.random.default_rng(33)
+    # fp32-representable inputs: the same as torch's fp32 -> bf16 conversion (round to nearest even)
+    v32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    want = torch.tensor(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_bits(v32.astype(np.float64)), want)
+    # arbitrary doubles: the result is the nearer of the two neighbouring bf16 values
+    v = rng.standard_normal(20000) * np.exp(rng.uniform(-5, 5, 20000))
+    b = oracle.f64_to_bf16_bits(v)
+    r = oracle.bf16_to_f64(b)
+    lo = oracle.bf16_to_f64((b.astype(np.int32) - np.sign(r - v).astype(np.int32) * np.where(v < 0, -1, 1)).astype(np.uint16))
+    assert np.all(np.abs(r - v) <= np.abs(lo - v))
+    # exact midpoints go to the even neighbour (no double rounding through fp32)
+    one = 1.0
+    assert oracle.f64_to_bf16_bits(np.array([one + 2.0 ** -8]))[0] == 0x3F80        # tie -> even (1.0)
+    assert oracle.f64_to_bf16_bits(np.array([one + 3 * 2.0 ** -8]))[0] == 0x3F82    # tie -> even (1 + 2^-6)
+    assert oracle.f64_to_bf16_bits(np.array([one + 2.0 ** -8 + 2.0 ** -40]))[0] == 0x3F81
+    assert oracle.f64_to_bf16_bits(np.array([-(one + 2.0 ** -8)]))[0] == 0xBF80
