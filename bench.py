@@ -115,6 +115,10 @@ def layer_step(layer, x, bias, bufs, gate_timer=None):
     can be bracketed by events on its stream."""
     h, hs, ws_gemm = bufs
     cfg = layer._cfg(x.shape[0])
+    residual = x if layer.residual else None
+    if layer.pre_norm:
+        moe.moe_rmsnorm(cfg, x, layer.w["norm_w"], layer.u[:x.shape[0]])
+        x = layer.u[:x.shape[0]]
     layer.route(x, bias)
     layer.permute(cfg, x, gather=False)
     T, K, w = cfg.num_tokens, cfg.top_k, layer.w
@@ -133,7 +137,7 @@ def layer_step(layer, x, bias, bufs, gate_timer=None):
                          layer.topk_gate[:T], w["w2"], w.get("s2"), w.get("w2s"), w.get("s2s"),
                          layer.out_slots[:TK], layer.y_shared[:T] if spec_has_shared(layer) else None,
                          ws=ws_gemm)
-    layer.combine(cfg)
+    layer.combine(cfg, residual)
 
 
 def spec_has_shared(layer) -> bool:
@@ -215,15 +219,23 @@ def decode_measure(steps, warmup):
     return out
 
 
-def route_ms(layer, x, bias, iters=20) -> float:
-    layer.route(x, bias)
+def per_launch_ms(call, iters=20) -> float:
+    """Mean time of one call, from HIP events around `iters` back-to-back
+    calls on the current stream (a short kernel timed alone would also count
+    the host's launch latency)."""
+    call()
     torch.cuda.synchronize()
-    t = Timed()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
     for _ in range(iters):
-        with t:
-            layer.route(x, bias)
+        call()
+    e.record()
     torch.cuda.synchronize()
-    return t.mean_ms()
+    return s.elapsed_time(e) / iters
+
+
+def route_ms(layer, x, bias, iters=20) -> float:
+    return per_launch_ms(lambda: layer.route(x, bias), iters)
 
 
 def sequence_loads_ms(layer, spec, seq_len, iters=20) -> float:
@@ -231,14 +243,24 @@ def sequence_loads_ms(layer, spec, seq_len, iters=20) -> float:
     cfg = layer._cfg(spec.T)
     nq = -(-spec.T // seq_len)
     out = torch.empty((nq, spec.E), dtype=torch.int32, device="cuda")
-    moe.moe_sequence_loads(cfg, layer.topk_idx[:spec.T], seq_len, out)
-    torch.cuda.synchronize()
-    t = Timed()
-    for _ in range(iters):
-        with t:
-            moe.moe_sequence_loads(cfg, layer.topk_idx[:spec.T], seq_len, out)
-    torch.cuda.synchronize()
-    return t.mean_ms()
+    idx = layer.topk_idx[:spec.T]
+    return per_launch_ms(lambda: moe.moe_sequence_loads(cfg, idx, seq_len, out), iters)
+
+
+def norm_residual_measure(layer, spec, x, bias, bufs, steps, warmup):
+    """The same prefill layer between a pre-MoE RMSNorm and the residual add
+    (section 4.1, eq. 12): tokens/s and the RMSNorm kernel's own time."""
+    layer.pre_norm, layer.residual = True, True
+    layer.u = torch.empty_like(x)
+    sec = time_steps(layer, x, bias, bufs, steps, warmup)
+    cfg = layer._cfg(spec.T)
+    u, w = layer.u, layer.w["norm_w"]
+    ms = per_launch_ms(lambda: moe.moe_rmsnorm(cfg, x, w, u))
+    layer.pre_norm, layer.residual, layer.u = False, False, None
+    # algorithmic bytes: x read and u written once (the weight vector is noise)
+    nbytes = 2.0 * spec.T * spec.d * x.element_size()
+    return {"tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3, "rmsnorm_ms": ms,
+            "rmsnorm_GBs": nbytes / (ms * 1e-3) / 1e9}
 
 
 def grouped_measure(steps, warmup, plain_route_ms):
@@ -332,6 +354,9 @@ def main():
     plain_route = route_ms(layer, x, bias)
     result["route_ms"] = plain_route
     result["sequence_loads_ms"] = sequence_loads_ms(layer, spec, seq_len=4096)
+    log("[bench] prefill layer with pre-norm and residual")
+    result["norm_residual"] = norm_residual_measure(layer, spec, x, bias, bufs, args.steps,
+                                                    args.warmup)
     if not args.no_cpu_baseline:
         log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
         result["cpu_baseline"] = cpu_baseline(spec, inp, layer, args.cpu_tokens)

@@ -31,7 +31,10 @@
  * Conventions shared by every call:
  *   - Every pointer except `cfg` and `status` strings is a DEVICE pointer to
  *     row-major contiguous memory that the caller owns and keeps alive until
- *     the enqueued work has finished. The library allocates nothing, keeps
+ *     the enqueued work has finished. Every device pointer must be 16-byte
+ *     aligned (hipMalloc and torch's allocator give 256): the kernels move
+ *     rows in 16-byte pieces, and a misaligned pointer is rejected with
+ *     MOE_ERR_SHAPE. The library allocates nothing, keeps
  *     no global state between calls and never synchronises the stream.
  *   - Arguments are validated on the host before anything is enqueued; a
  *     call that returns an error has enqueued nothing. MOE_OK means
@@ -314,6 +317,28 @@ int moe_experts_down(const moe_config* cfg, const void* h, const void* hs,
  * out_slots [T*K, d] act dtype; y_shared [T, d] fp32; y [T, d] out_dtype. */
 int moe_combine(const moe_config* cfg, const void* out_slots, const void* y_shared,
                 void* y, void* stream);
+
+/* ---- moe_rmsnorm / moe_combine_residual ------------------------------------
+ * The steps either side of the layer ([DSMoE] section 4.1: an RMSNorm before
+ * (and after) the MoE layer, eps 1e-6; section 2.1's eq. (12) adds the
+ * layer's input to the expert sum). For a pre-norm layer:
+ *   u = moe_rmsnorm(x)  ->  moe_route / moe_permute / moe_experts on u
+ *   y = moe_combine_residual(out_slots, y_shared, x)
+ * moe_rmsnorm: u[t, j] = x[t, j] / sqrt(mean_j' x[t, j']^2 + eps) * weight[j],
+ *   computed in double precision
+ *   (the sum of squares of bf16 inputs is then exact in any order, and every
+ *   further step is one correctly rounded double operation) and rounded once
+ *   to the activation dtype (round to nearest even). x, u [T, d] act dtype
+ *   (u may be x); weight [d] fp32; eps > 0 and finite (the pages use 1e-6);
+ *   d <= 16384 (bf16) or 8192 (fp32), else MOE_ERR_UNSUPPORTED.
+ * moe_combine_residual: y[t] = residual[t] + y_shared[t] + sum_k
+ *   out_slots[t*K + k], summed in fp32 in this order, rounded once to
+ *   cfg->out_dtype. residual [T, d] act dtype; other arguments as for
+ *   moe_combine (y_shared may be NULL). */
+int moe_rmsnorm(const moe_config* cfg, const void* x, const float* weight, double eps, void* u,
+                void* stream);
+int moe_combine_residual(const moe_config* cfg, const void* out_slots, const void* y_shared,
+                         const void* residual, void* y, void* stream);
 
 /* ---- moe_sequence_loads ---------------------------------------------------
  * Per-sequence expert loads, the statistic behind a sequence-wise balance

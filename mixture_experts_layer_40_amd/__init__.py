@@ -41,6 +41,7 @@ from ._lib import (  # noqa: F401
     make_config,
     moe_bias_update,
     moe_combine,
+    moe_combine_residual,
     moe_config,
     moe_expert_down,
     moe_expert_ffn,
@@ -50,6 +51,7 @@ from ._lib import (  # noqa: F401
     moe_experts_gate_up,
     moe_pack_weights,
     moe_permute,
+    moe_rmsnorm,
     moe_route,
     moe_sequence_loads,
     moe_shared_ffn,

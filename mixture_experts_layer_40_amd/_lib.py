@@ -48,7 +48,8 @@ MOE_WS_EXPERTS = 5
 EXPORTED = ("moe_validate", "moe_workspace_size", "moe_status_string", "moe_route",
             "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
             "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights",
-            "moe_experts", "moe_experts_gate_up", "moe_experts_down", "moe_sequence_loads")
+            "moe_experts", "moe_experts_gate_up", "moe_experts_down", "moe_sequence_loads",
+            "moe_rmsnorm", "moe_combine_residual")
 
 
 class MoEError(RuntimeError):
@@ -67,6 +68,8 @@ class moe_config(ctypes.Structure):
                 ("weight_layout", ctypes.c_int32), ("num_groups", ctypes.c_int32),
                 ("topk_groups", ctypes.c_int32)]
 
+
+RMS_EPS = 1e-6
 
 _DT = {"f32": MOE_DTYPE_F32, "bf16": MOE_DTYPE_BF16, "fp8": MOE_DTYPE_FP8_E4M3}
 _SC = {"sigmoid": MOE_SCORE_SIGMOID, "softmax": MOE_SCORE_SOFTMAX}
@@ -129,10 +132,12 @@ def load_library(path: str = LIB_PATH):
     lib.moe_experts_gate_up.argtypes = [CFG] + [P] * 14 + [SZ, P]
     lib.moe_experts_down.argtypes = [CFG] + [P] * 12 + [SZ, P]
     lib.moe_sequence_loads.argtypes = [CFG, P, I32, P, P]
+    lib.moe_rmsnorm.argtypes = [CFG, P, P, ctypes.c_double, P, P]
+    lib.moe_combine_residual.argtypes = [CFG, P, P, P, P, P]
     for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up",
                "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update",
                "moe_pack_weights", "moe_experts", "moe_experts_gate_up", "moe_experts_down",
-               "moe_sequence_loads"):
+               "moe_sequence_loads", "moe_rmsnorm", "moe_combine_residual"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -295,3 +300,14 @@ def moe_experts_down(cfg, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w
 def moe_sequence_loads(cfg, topk_idx, seq_len, seq_load, stream=None):
     _check("moe_sequence_loads", load_library().moe_sequence_loads(
         ctypes.byref(cfg), _ptr(topk_idx), int(seq_len), _ptr(seq_load), _stream(stream)))
+
+
+def moe_rmsnorm(cfg, x, weight, u, eps=RMS_EPS, stream=None):
+    _check("moe_rmsnorm", load_library().moe_rmsnorm(
+        ctypes.byref(cfg), _ptr(x), _ptr(weight), float(eps), _ptr(u), _stream(stream)))
+
+
+def moe_combine_residual(cfg, out_slots, y_shared, residual, y, stream=None):
+    _check("moe_combine_residual", load_library().moe_combine_residual(
+        ctypes.byref(cfg), _ptr(out_slots), _ptr(y_shared), _ptr(residual), _ptr(y),
+        _stream(stream)))

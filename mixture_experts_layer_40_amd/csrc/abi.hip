@@ -15,6 +15,13 @@ constexpr int64_t kInt32Max = 2147483647LL;
 
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
+// Every device pointer the kernels read or write in 16-byte pieces must be
+// 16-byte aligned; NULL (an absent optional argument) passes.
+template <class... P>
+bool aligned16(P... p) {
+  return ((((reinterpret_cast<uintptr_t>(static_cast<const void*>(p)) & 15u) == 0)) && ...);
+}
+
 int check_ws(size_t need, const void* ws, size_t ws_bytes) {
   if (need == 0) return MOE_OK;
   if (!ws || ws_bytes < need || !aligned256(ws)) return MOE_ERR_WORKSPACE;
@@ -120,6 +127,7 @@ int moe_pack_weights(int which, int32_t groups, int32_t rows, int32_t cols, int3
   if (!src_a || !dst) return MOE_ERR_NULL;
   if (which == MOE_PACK_GATE_UP ? !src_b : src_b != nullptr)
     return which == MOE_PACK_GATE_UP ? MOE_ERR_NULL : MOE_ERR_SHAPE;
+  if (!aligned16(src_a, src_b, dst)) return MOE_ERR_SHAPE;
   const int wbytes = weight_dtype == MOE_DTYPE_BF16 ? 2 : 1;
   (void)hipGetLastError();
   return from_hip(launch_pack(which == MOE_PACK_GATE_UP ? 0 : 1, groups, rows, cols, wbytes, src_a,
@@ -133,6 +141,7 @@ int moe_route(const moe_config* c, const void* x, const void* w_router, const fl
   if (st != MOE_OK) return st;
   if (!load) return MOE_ERR_NULL;
   if (c->num_tokens > 0 && (!x || !w_router || !topk_idx || !topk_gate)) return MOE_ERR_NULL;
+  if (!aligned16(x, w_router, bias, topk_idx, topk_gate, load)) return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_ROUTE), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_route(*c, x, w_router, bias, topk_idx, topk_gate, load, ws,
@@ -146,6 +155,7 @@ int moe_permute(const moe_config* c, const int32_t* topk_idx, const void* x,
   if (st != MOE_OK) return st;
   if (!expert_offsets) return MOE_ERR_NULL;
   if (c->num_tokens > 0 && (!topk_idx || !perm_slot || (x_perm && !x))) return MOE_ERR_NULL;
+  if (!aligned16(topk_idx, x, expert_offsets, perm_slot, x_perm)) return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_PERMUTE), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_permute(*c, topk_idx, x, expert_offsets, perm_slot, x_perm, ws,
@@ -163,6 +173,8 @@ int moe_expert_ffn(const moe_config* c, const void* x_perm, const int32_t* exper
   if ((st = check_w3(c, w3)) != MOE_OK) return st;
   if (!x_perm || !expert_offsets || !perm_slot || !topk_gate || !w1 || !w2 || !out_slots)
     return MOE_ERR_NULL;
+  if (!aligned16(x_perm, expert_offsets, perm_slot, topk_gate, w1, w3, w2, s1, s3, s2, out_slots))
+    return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_FFN), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_expert_ffn(*c, x_perm, expert_offsets, perm_slot, topk_gate, w1, w3, w2,
@@ -178,6 +190,7 @@ int moe_expert_gate_up(const moe_config* c, const void* x_perm, const int32_t* e
   if (c->num_tokens == 0) return MOE_OK;
   if ((st = check_w3(c, w3)) != MOE_OK) return st;
   if (!x_perm || !expert_offsets || !w1 || !h) return MOE_ERR_NULL;
+  if (!aligned16(x_perm, expert_offsets, w1, w3, s1, s3, h)) return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_gate_up(*c, x_perm, expert_offsets, w1, w3, s1, s3, h, ws,
@@ -192,6 +205,7 @@ int moe_expert_down(const moe_config* c, const void* h, const int32_t* expert_of
   if ((st = check_scales(c, s2, s2, s2)) != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
   if (!h || !expert_offsets || !perm_slot || !topk_gate || !w2 || !out_slots) return MOE_ERR_NULL;
+  if (!aligned16(h, expert_offsets, perm_slot, topk_gate, w2, s2, out_slots)) return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_down(*c, h, expert_offsets, perm_slot, topk_gate, w2, s2, out_slots, ws,
@@ -208,6 +222,7 @@ int moe_shared_ffn(const moe_config* c, const void* x, const void* w1s, const vo
   if (c->num_tokens == 0) return MOE_OK;
   if ((st = check_w3(c, w3s)) != MOE_OK) return st;
   if (!x || !w1s || !w2s || !y_shared) return MOE_ERR_NULL;
+  if (!aligned16(x, w1s, w3s, w2s, s1s, s3s, s2s, y_shared)) return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_SHARED), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_shared_ffn(*c, x, w1s, w3s, w2s, s1s, s3s, s2s, y_shared, ws,
@@ -237,6 +252,9 @@ int moe_experts(const moe_config* c, const void* x, const int32_t* expert_offset
     if ((st = check_w3(c, w3s)) != MOE_OK) return st;
     if (!w1s || !w2s || !y_shared) return MOE_ERR_NULL;
   }
+  if (!aligned16(x, expert_offsets, perm_slot, topk_gate, w1, w3, w2, s1, s3, s2, w1s, w3s, w2s,
+                 s1s, s3s, s2s, out_slots, y_shared))
+    return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_EXPERTS), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_experts(*c, x, expert_offsets, perm_slot, topk_gate, w1, w3, w2, s1, s3,
@@ -265,6 +283,8 @@ int moe_experts_gate_up(const moe_config* c, const void* x, const int32_t* exper
     if ((st = check_w3(c, w3s)) != MOE_OK) return st;
     if (!w1s || !hs) return MOE_ERR_NULL;
   }
+  if (!aligned16(x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s, w3s, s1s, s3s, h, hs))
+    return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_experts_gate_up(*c, x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s,
@@ -288,6 +308,9 @@ int moe_experts_down(const moe_config* c, const void* h, const void* hs,
   if (c->num_tokens == 0) return MOE_OK;
   if (!h || !expert_offsets || !perm_slot || !topk_gate || !w2 || !out_slots) return MOE_ERR_NULL;
   if (c->num_shared > 0 && (!hs || !w2s || !y_shared)) return MOE_ERR_NULL;
+  if (!aligned16(h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w2s, s2s, out_slots,
+                 y_shared))
+    return MOE_ERR_SHAPE;
   if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
   (void)hipGetLastError();
   return from_hip(launch_experts_down(*c, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2,
@@ -300,8 +323,34 @@ int moe_combine(const moe_config* c, const void* out_slots, const void* y_shared
   if (st != MOE_OK) return st;
   if (c->num_tokens == 0) return MOE_OK;
   if (!out_slots || !y) return MOE_ERR_NULL;
+  if (!aligned16(out_slots, y_shared, y)) return MOE_ERR_SHAPE;
   (void)hipGetLastError();
-  return from_hip(launch_combine(*c, out_slots, y_shared, y, as_stream(stream)));
+  return from_hip(launch_combine(*c, out_slots, y_shared, nullptr, y, as_stream(stream)));
+}
+
+int moe_combine_residual(const moe_config* c, const void* out_slots, const void* y_shared,
+                         const void* residual, void* y, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!out_slots || !residual || !y) return MOE_ERR_NULL;
+  if (!aligned16(out_slots, y_shared, residual, y)) return MOE_ERR_SHAPE;
+  (void)hipGetLastError();
+  return from_hip(launch_combine(*c, out_slots, y_shared, residual, y, as_stream(stream)));
+}
+
+int moe_rmsnorm(const moe_config* c, const void* x, const float* weight, double eps, void* u,
+                void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (!(eps > 0.0) || isinf(eps)) return MOE_ERR_SHAPE;
+  // one block per token keeps its row in registers: at most 16384 elements
+  if (c->hidden > (c->act_dtype == MOE_DTYPE_BF16 ? 16384 : 8192)) return MOE_ERR_UNSUPPORTED;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!x || !weight || !u) return MOE_ERR_NULL;
+  if (!aligned16(x, weight, u)) return MOE_ERR_SHAPE;
+  (void)hipGetLastError();
+  return from_hip(launch_rmsnorm(*c, x, weight, eps, u, as_stream(stream)));
 }
 
 int moe_sequence_loads(const moe_config* c, const int32_t* topk_idx, int32_t seq_len,
@@ -311,6 +360,7 @@ int moe_sequence_loads(const moe_config* c, const int32_t* topk_idx, int32_t seq
   if (seq_len < 1) return MOE_ERR_SHAPE;
   if (c->num_tokens == 0) return MOE_OK;
   if (!topk_idx || !seq_load) return MOE_ERR_NULL;
+  if (!aligned16(topk_idx, seq_load)) return MOE_ERR_SHAPE;
   (void)hipGetLastError();
   return from_hip(launch_sequence_loads(*c, topk_idx, seq_len, seq_load, as_stream(stream)));
 }
@@ -319,6 +369,7 @@ int moe_bias_update(int32_t num_experts, const int32_t* load, float gamma, float
                     void* stream) {
   if (num_experts < 1 || num_experts > 256) return MOE_ERR_SHAPE;
   if (!load || !bias) return MOE_ERR_NULL;
+  if (!aligned16(load, bias)) return MOE_ERR_SHAPE;
   if (!(gamma >= 0.0f) || isinf(gamma)) return MOE_ERR_SHAPE;
   (void)hipGetLastError();
   return from_hip(launch_bias_update(num_experts, load, gamma, bias, as_stream(stream)));

@@ -75,7 +75,9 @@ hipError_t launch_pack(int which, int64_t groups, int rows, int cols, int wbytes
 
 // ---- combine / bias ----------------------------------------------------------
 hipError_t launch_combine(const moe_config& c, const void* out_slots, const void* y_shared,
-                          void* y, hipStream_t s);
+                          const void* residual, void* y, hipStream_t s);
+hipError_t launch_rmsnorm(const moe_config& c, const void* x, const float* weight, double eps,
+                          void* u, hipStream_t s);
 hipError_t launch_bias_update(int32_t E, const int32_t* load, float gamma, float* bias,
                               hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);

@@ -31,7 +31,7 @@ _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 class MoELayer:
     def __init__(self, spec, weights: dict, max_tokens: Optional[int] = None,
                  shared_stream: bool = True, device=None, layout: Optional[str] = None,
-                 fused: Optional[bool] = None):
+                 fused: Optional[bool] = None, pre_norm: bool = False, residual: bool = False):
         self.spec = spec
         self.device = torch.device(device) if device is not None else weights["wr"].device
         self.max_tokens = spec.T if max_tokens is None else max_tokens
@@ -40,6 +40,7 @@ class MoELayer:
             layout = "rows" if spec.weight_dtype == "f32" else "tiled"
         self.layout = layout
         self.fused = spec.act_dtype == "bf16" if fused is None else fused
+        self.pre_norm, self.residual = pre_norm, residual
         self.w = dict(weights)
         if layout == "tiled":
             wd = spec.weight_dtype
@@ -65,6 +66,7 @@ class MoELayer:
         self.out_slots = torch.empty((T * K, d), dtype=self.act, device=dev)
         self.y_shared = torch.empty((T, d), dtype=torch.float32, device=dev) if spec.S > 0 else None
         self.y = torch.empty((T, d), dtype=_TORCH_DT[getattr(spec, "out_dtype", "f32")], device=dev)
+        self.u = torch.empty((T, d), dtype=self.act, device=dev) if pre_norm else None
 
         def ws(which):
             n = L.moe_workspace_size(self.cfg_max, which)
@@ -115,22 +117,31 @@ class MoELayer:
         L.moe_shared_ffn(cfg, x, w["w1s"], w["w3s"], w["w2s"], w.get("s1s"), w.get("s3s"),
                          w.get("s2s"), self.y_shared[:T], ws=self.ws_shared, stream=stream)
 
-    def combine(self, cfg):
+    def combine(self, cfg, residual=None):
         T = cfg.num_tokens
-        L.moe_combine(cfg, self.out_slots[:T * cfg.top_k],
-                      None if self.y_shared is None else self.y_shared[:T], self.y[:T])
+        ysh = None if self.y_shared is None else self.y_shared[:T]
+        if residual is None:
+            L.moe_combine(cfg, self.out_slots[:T * cfg.top_k], ysh, self.y[:T])
+        else:
+            L.moe_combine_residual(cfg, self.out_slots[:T * cfg.top_k], ysh, residual, self.y[:T])
 
     def forward(self, x, bias=None):
-        """Enqueue one layer call on the current stream; returns y [T, d]."""
+        """Enqueue one layer call on the current stream; returns y [T, d].
+        With pre_norm the experts and the router see u = RMSNorm(x) (weight
+        weights["norm_w"], eps 1e-6); with residual, y = x + the expert sum."""
         cfg = self._cfg(x.shape[0])
         if cfg.num_tokens == 0:
             L.moe_route(cfg, x, self.w["wr"], bias, None, None, self.load, ws=self.ws_route)
             return self.y[:0]
+        res = x if self.residual else None
+        if self.pre_norm:
+            L.moe_rmsnorm(cfg, x, self.w["norm_w"], self.u[:cfg.num_tokens])
+            x = self.u[:cfg.num_tokens]
         if self.fused:
             self.route(x, bias)
             self.permute(cfg, x, gather=False)
             self.experts_fused(cfg, x)
-            self.combine(cfg)
+            self.combine(cfg, res)
             return self.y[:cfg.num_tokens]
         cur = torch.cuda.current_stream(self.device)
         if self.side is not None:
@@ -144,7 +155,7 @@ class MoELayer:
         self.experts(cfg)
         if self.side is not None:
             cur.wait_stream(self.side)
-        self.combine(cfg)
+        self.combine(cfg, res)
         return self.y[:cfg.num_tokens]
 
     def bias_update(self, bias, gamma=None):

@@ -18,6 +18,7 @@ Layouts (row-major, contiguous):
   s1, s3 [E, I], s2 [E, d]      fp32 per-output-row scales (fp8 only)
   w1s, w3s [S*Is, d], w2s [d, S*Is]  shared experts concatenated
   s1s, s3s [S*Is], s2s [d]           fp32 scales (fp8 only)
+  norm_w [d]                          fp32 RMSNorm weight for the optional pre-norm
 """
 
 from __future__ import annotations
@@ -33,7 +34,7 @@ from .configs import MoEConfig
 E4M3_MAX = 448.0
 
 _TAGS = {"x": 1, "wr": 2, "bias": 3, "w1": 4, "w3": 5, "w2": 6,
-         "w1s": 7, "w3s": 8, "w2s": 9, "perm": 10}
+         "w1s": 7, "w3s": 8, "w2s": 9, "perm": 10, "norm_w": 11}
 
 
 def _seed(base: int, tag: str, idx: int = 0) -> int:
@@ -103,6 +104,9 @@ def make_inputs(cfg: MoEConfig, device="cpu", batch: int = 0,
     if cfg.zipf_s is not None:
         wr[:, 0] = zipf_offsets(cfg, dev)
     out["wr"] = _store_act(wr, cfg.act_dtype)
+
+    # RMSNorm weight of the optional pre-norm: 1 + N(0, 0.1^2) per channel, fp32
+    out["norm_w"] = (1.0 + _normal((cfg.d,), 0.1, dev, cfg.seed, "norm_w")).float().contiguous()
 
     if cfg.bias_range is not None:
         g = _gen(dev, cfg.seed, "bias")

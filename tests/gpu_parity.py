@@ -137,7 +137,7 @@ def rel_err(got, want):
     return float(np.abs(got - want).max()) / max(rms, 1e-300), rms
 
 
-def check_outputs(spec, layer, inp, res, r, x=None, rows=None):
+def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
     """Layer output (and its shared and routed parts) on `rows` against the
     oracle. `r` is the oracle routing of all tokens of the batch. The oracle
     uses its own selected set, except on near-tie tokens, where any set
@@ -155,6 +155,10 @@ def check_outputs(spec, layer, inp, res, r, x=None, rows=None):
     y_or, ysh_or, routed_or = oracle.layer_rows(x64, sel, g_or, bank_of(inp, spec))
     tol = OUT_TOL[spec.act_dtype]
     y = oracle.decode_stored(host(res["y"][trow].contiguous()))
+    if residual is not None:
+        # y = residual + expert sum: the error is measured against the
+        # expert sum's own RMS (the residual itself enters exactly)
+        y = y - residual[rows]
     e_y, rms = rel_err(y, y_or)
     assert e_y <= tol, f"y: max err / RMS = {e_y:.3e} > {tol}"
     if spec.S > 0:

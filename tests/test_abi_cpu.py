@@ -223,3 +223,34 @@ def test_fused_entry_points_validate_on_host():
     c = _cfg(act_dtype="bf16", weight_dtype="bf16")
     assert lib.moe_permute(by(c), fake, None, fake, fake, None, None, 0, None) == L.MOE_ERR_WORKSPACE
     assert lib.moe_permute(by(c), fake, None, fake, fake, fake, None, 0, None) == L.MOE_ERR_NULL
+
+
+def test_norm_residual_and_alignment_validate_on_host():
+    lib = moe.load_library()
+    by = ctypes.byref
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)   # odd: 8-byte aligned only
+    c = _cfg(act_dtype="bf16", weight_dtype="bf16")
+    rms = lib.moe_rmsnorm
+    for eps in (0.0, -1e-6, float("inf"), float("nan")):
+        assert rms(by(c), fake, fake, eps, fake, None) == L.MOE_ERR_SHAPE
+    assert rms(by(c), None, fake, 1e-6, fake, None) == L.MOE_ERR_NULL
+    assert rms(by(c), fake, None, 1e-6, fake, None) == L.MOE_ERR_NULL
+    assert rms(by(c), fake, fake, 1e-6, None, None) == L.MOE_ERR_NULL
+    assert rms(by(c), odd, fake, 1e-6, fake, None) == L.MOE_ERR_SHAPE
+    assert rms(by(c), fake, fake, 1e-6, odd, None) == L.MOE_ERR_SHAPE
+    # one block per token keeps its row in registers
+    assert rms(by(_cfg(act_dtype="bf16", weight_dtype="bf16", d=16448)), fake, fake, 1e-6, fake, None) == L.MOE_ERR_UNSUPPORTED
+    assert rms(by(_cfg(d=8256)), fake, fake, 1e-6, fake, None) == L.MOE_ERR_UNSUPPORTED
+    assert rms(by(_cfg(T=0)), None, None, 1e-6, None, None) == L.MOE_OK
+    cr = lib.moe_combine_residual
+    assert cr(by(c), fake, None, None, fake, None) == L.MOE_ERR_NULL
+    assert cr(by(c), fake, fake, odd, fake, None) == L.MOE_ERR_SHAPE
+    assert cr(by(_cfg(T=0)), None, None, None, None, None) == L.MOE_OK
+    # misaligned device pointers are refused by every call, before any launch
+    assert lib.moe_combine(by(c), odd, None, fake, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_route(by(c), odd, fake, None, fake, fake, fake, None, 0, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_permute(by(c), fake, fake, fake, odd, None, None, 0, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_sequence_loads(by(c), odd, 16, fake, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_bias_update(8, fake, ctypes.c_float(1e-3), odd, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_pack_weights(L.MOE_PACK_DOWN, 1, 32, 64, L.MOE_DTYPE_BF16, odd, None, fake, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_expert_down(by(c), fake, fake, fake, fake, odd, None, fake, None, 0, None) == L.MOE_ERR_SHAPE
