@@ -15,6 +15,7 @@ Sources (the web pages this library is built from):
            "路由机制".
   [COURSE] "省钱第一招：把一个大厨换成专家团" (blog.zero43.top, DeepSeek paper
            course 07), sections 三 to 六.
+  The fine-grained FP8 path (fp8block.py) follows [DSMoE] section 4.3.
 
 Every function is the plain definition written out in float64 (the bias
 update is the one step done in fp32, because the bias is an fp32 state
@@ -46,4 +47,16 @@ from .moe import (  # noqa: F401
     ExpertBank,
     layer_rows,
     bias_update,
+)
+from .fp8block import (  # noqa: F401
+    E4M3_MAX,
+    TILE,
+    e4m3_encode,
+    quantize_tiles,
+    dequantize_tiles,
+    dequantize_blocks,
+    swiglu_expert_fp8,
+    BlockExpertBank,
+    quantize_x,
+    layer_rows_fp8,
 )

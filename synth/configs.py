@@ -49,6 +49,11 @@ class MoEConfig:
     # n_groups groups of E/n_groups, topk_groups groups kept per token (0 = off)
     n_groups: int = 0
     topk_groups: int = 0
+    # fp8 weight scales: "row" = one fp32 scale per output row (bf16
+    # activations); "block" = one per 128 x 128 block, with the activations
+    # quantised to fp8 in 1 x 128 tiles on the fly ("DeepSeekMoE" explainer,
+    # section 4.3)
+    fp8_scaling: str = "row"
     description: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -68,14 +73,16 @@ class MoEConfig:
         wb = {"f32": 4, "bf16": 2, "fp8": 1}[self.weight_dtype]
         b = 3 * self.d * self.I * wb
         if self.weight_dtype == "fp8":
-            b += 4 * (2 * self.I + self.d)
+            b += 4 * (3 * (self.I // 128) * (self.d // 128) if self.fp8_scaling == "block"
+                      else 2 * self.I + self.d)
         return b
 
     def shared_weight_bytes(self) -> int:
         wb = {"f32": 4, "bf16": 2, "fp8": 1}[self.weight_dtype]
         b = 3 * self.d * self.Is * self.S * wb
         if self.weight_dtype == "fp8":
-            b += 4 * (2 * self.Is * self.S + self.d)
+            b += 4 * (3 * (self.Is * self.S // 128) * (self.d // 128) if self.fp8_scaling == "block"
+                      else 2 * self.Is * self.S + self.d)
         return b
 
     def act_bytes(self) -> int:
@@ -121,6 +128,12 @@ CONFIGS = {
         score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="bf16",
         bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 6, n_groups=8, topk_groups=4,
         description="V3-shape prefill with node-limited routing: 8 groups of 32 experts, top-4 groups",
+    ),
+    "v3_prefill_fp8b": MoEConfig(
+        name="v3_prefill_fp8b", T=8192, d=7168, E=256, K=8, I=2048, S=1, Is=2048,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="fp8",
+        fp8_scaling="block", bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 7,
+        description="V3-shape prefill in fine-grained fp8: 128x128 weight blocks, 1x128 activation tiles",
     ),
 }
 

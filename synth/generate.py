@@ -15,9 +15,11 @@ Layouts (row-major, contiguous):
   bias[E]               fp32 (or None)
   w1, w3 [E, I, d]      weight dtype (gate / up projections)
   w2     [E, d, I]      weight dtype (down projection)
-  s1, s3 [E, I], s2 [E, d]      fp32 per-output-row scales (fp8 only)
+  s1, s3 [E, I], s2 [E, d]      fp32 per-output-row scales (fp8 only), or with
+                                fp8_scaling "block": s1, s3 [E, I/128, d/128],
+                                s2 [E, d/128, I/128], one per 128 x 128 block
   w1s, w3s [S*Is, d], w2s [d, S*Is]  shared experts concatenated
-  s1s, s3s [S*Is], s2s [d]           fp32 scales (fp8 only)
+  s1s, s3s [S*Is], s2s [d]           fp32 scales (fp8 only; block: [S*Is/128, d/128], [d/128, S*Is/128])
   norm_w [d]                          fp32 RMSNorm weight for the optional pre-norm
 """
 
@@ -69,9 +71,20 @@ def _quant_fp8_rows(w: torch.Tensor):
     return q.view(torch.uint8), scale.squeeze(-1).to(torch.float32).contiguous()
 
 
-def _store_weight(v: torch.Tensor, dtype: str):
+def _quant_fp8_blocks(w: torch.Tensor, block: int = 128):
+    """128 x 128 block fp8-e4m3 quantisation of a [R, C] matrix: one scale
+    amax/448 per block (1 for an all-zero block), code = RNE(w/scale)."""
+    R, C = w.shape
+    t = w.reshape(R // block, block, C // block, block)
+    amax = t.abs().amax(dim=(1, 3), keepdim=True)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = (t / scale).clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).reshape(R, C)
+    return q.view(torch.uint8), scale.reshape(R // block, C // block).to(torch.float32).contiguous()
+
+
+def _store_weight(v: torch.Tensor, dtype: str, scaling: str = "row"):
     if dtype == "fp8":
-        return _quant_fp8_rows(v)
+        return _quant_fp8_blocks(v) if scaling == "block" else _quant_fp8_rows(v)
     return _store_act(v, dtype), None
 
 
@@ -121,12 +134,14 @@ def make_inputs(cfg: MoEConfig, device="cpu", batch: int = 0,
     wdt = cfg.weight_dtype
     stored_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wdt]
     E, I, d = cfg.E, cfg.I, cfg.d
+    block = wdt == "fp8" and cfg.fp8_scaling == "block"
     for name, shape in (("w1", (I, d)), ("w3", (I, d)), ("w2", (d, I))):
         buf = torch.empty((E,) + shape, dtype=stored_dt, device=dev)
-        sc = torch.empty((E, shape[0]), dtype=torch.float32, device=dev) if wdt == "fp8" else None
+        sshape = (E, shape[0] // 128, shape[1] // 128) if block else (E, shape[0])
+        sc = torch.empty(sshape, dtype=torch.float32, device=dev) if wdt == "fp8" else None
         for e in range(E):
             v = _normal(shape, cfg.w_std, dev, cfg.seed, name, e)
-            q, s = _store_weight(v, wdt)
+            q, s = _store_weight(v, wdt, cfg.fp8_scaling)
             buf[e].copy_(q)
             if sc is not None:
                 sc[e].copy_(s)
@@ -138,7 +153,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", batch: int = 0,
         SI = cfg.S * cfg.Is
         for name, shape in (("w1s", (SI, d)), ("w3s", (SI, d)), ("w2s", (d, SI))):
             v = _normal(shape, cfg.w_std, dev, cfg.seed, name)
-            q, s = _store_weight(v, wdt)
+            q, s = _store_weight(v, wdt, cfg.fp8_scaling)
             out[name] = q
             out["s" + name[1] + "s"] = s
     else:

@@ -598,3 +598,204 @@ def test_f64_to_bf16_rounding():
     assert oracle.f64_to_bf16_bits(np.array([one + 3 * 2.0 ** -8]))[0] == 0x3F82    # tie -> even (1 + 2^-6)
     assert oracle.f64_to_bf16_bits(np.array([one + 2.0 ** -8 + 2.0 ** -40]))[0] == 0x3F81
     assert oracle.f64_to_bf16_bits(np.array([-(one + 2.0 ** -8)]))[0] == 0xBF80
+
+
+# ---- fine-grained FP8 ("DeepSeekMoE架构解析" section 4.3): 1x128 tiles, 128x128 blocks ----
+
+def _e4m3_midpoints():
+    pos = oracle.E4M3_TABLE[:0x7F]
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mid.astype(np.float64), (pos[:-1] + pos[1:]) / 2)   # exact in fp32
+    return np.concatenate([mid, -mid])
+
+
+def test_e4m3_encode_against_torch():
+    """The nearest-value encoder against torch's own fp32 -> float8_e4m3fn
+    cast (round to nearest even), on random values of every binade, on the
+    subnormals and on every exact midpoint between neighbouring codes."""
+    rng = np.random.default_rng(41)
+    v = (rng.standard_normal(50000) * np.exp(rng.uniform(-14, 6, 50000))).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    for arr in (v, _e4m3_midpoints(), np.float32([0.0, -0.0, 2.0 ** -10, -(2.0 ** -10), 2.0 ** -9 * 1.5, 448.0, -448.0])):
+        want = torch.tensor(arr).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(oracle.e4m3_encode(arr), want)
+    # decoding what was encoded gives the nearest representable value
+    d = oracle.E4M3_TABLE[oracle.e4m3_encode(v)]
+    pos = oracle.E4M3_TABLE[:0x7F]
+    near = np.min(np.abs(np.abs(v.astype(np.float64))[:, None] - pos[None, :]), axis=1)
+    assert np.array_equal(np.abs(d - v), near)
+
+
+def test_quantize_tiles_closed_forms():
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((3, 512)).astype(np.float32)
+    x[1, 128:256] = 0.0                                      # an all-zero tile
+    codes, s = oracle.quantize_tiles(x)
+    assert codes.shape == (3, 512) and s.shape == (3, 4) and s.dtype == np.float32
+    t = np.abs(x.reshape(3, 4, 128))
+    amax = t.max(axis=2)
+    assert s[1, 1] == 1.0 and np.all(codes[1, 128:256] & 0x7F == 0)
+    nz = amax > 0
+    assert np.array_equal(s[nz], (amax[nz] / np.float32(448)).astype(np.float32))
+    # the largest element of each tile maps to +-448 (code magnitude 0x7E)
+    arg = t.argmax(axis=2)
+    for r in range(3):
+        for j in range(4):
+            if nz[r, j]:
+                assert codes[r, 128 * j + arg[r, j]] & 0x7F == 0x7E
+    # orientation: tile j of row r has amax 448 * 2^(j - r) -> scale 2^(j - r) exactly
+    y = np.ones((3, 512), np.float32)
+    for r in range(3):
+        for j in range(4):
+            y[r, 128 * j] = np.float32(448.0 * 2.0 ** (j - r))
+    cy, sy = oracle.quantize_tiles(y)
+    assert np.array_equal(sy, np.float32([[2.0 ** (j - r) for j in range(4)] for r in range(3)]))
+    # powers of two commute with the quantisation: same codes, scales times 2^p
+    c8, s8 = oracle.quantize_tiles((x * np.float32(8.0)).astype(np.float32))
+    assert np.array_equal(c8, codes)
+    assert np.array_equal(s8, np.where(nz, s * np.float32(8.0), np.float32(1.0)))
+    # values already on the grid (code value times a power-of-two scale) round-trip exactly
+    g = oracle.E4M3_TABLE[rng.integers(0, 0x7F, (2, 256))] * (2.0 ** -5)
+    g[:, 0] = 448.0 * 2.0 ** -5
+    g[:, 128] = 448.0 * 2.0 ** -5
+    cg, sg = oracle.quantize_tiles(g.astype(np.float32))
+    assert np.array_equal(oracle.dequantize_tiles(cg, sg), g)
+
+
+def test_quantize_tiles_error_bound():
+    """|x - dequantised| <= 2^-4 |x| where x/s is in the normal E4M3 range (3
+    mantissa bits: half a step), and <= s * 2^-10 below it (subnormal step
+    2^-9 times the scale)."""
+    rng = np.random.default_rng(43)
+    x = (rng.standard_normal((16, 1024)) * np.exp(rng.uniform(-8, 3, (16, 1024)))).astype(np.float32)
+    codes, s = oracle.quantize_tiles(x)
+    err = np.abs(oracle.dequantize_tiles(codes, s) - x.astype(np.float64))
+    sf = np.repeat(s.astype(np.float64), 128, axis=1)
+    q = np.abs(x.astype(np.float64)) / sf
+    normal = q >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(x[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= sf[~normal] * 2.0 ** -10 * (1 + 1e-6))
+
+
+def test_dequantize_blocks_layout():
+    """Block (i, j) of the scale matrix scales rows 128i.. and columns 128j..:
+    brute force over every element, with a different scale per block."""
+    rng = np.random.default_rng(44)
+    codes = rng.integers(0, 0x7F, (256, 384)).astype(np.uint8)
+    codes |= (rng.integers(0, 2, codes.shape) << 7).astype(np.uint8)
+    sc = np.float32([[1 + i * 10 + j for j in range(3)] for i in range(2)])
+    deq = oracle.dequantize_blocks(codes, sc)
+    for r in range(0, 256, 37):
+        for c in range(0, 384, 29):
+            assert deq[r, c] == oracle.E4M3_TABLE[codes[r, c]] * float(sc[r // 128, c // 128])
+    with pytest.raises(ValueError):
+        oracle.dequantize_blocks(codes, sc.T)
+
+
+def _fp8_weights(rng, rows, cols):
+    codes = oracle.e4m3_encode(np.clip(rng.standard_normal((rows, cols)) * 100, -448, 448).astype(np.float32))
+    sc = rng.uniform(1e-4, 3e-4, (rows // 128, cols // 128)).astype(np.float32)
+    return codes, sc
+
+
+def test_fp8_expert_within_the_h_quantisation_bound():
+    """The fp8 expert against the plain SwiGLU expert on the dequantised x and
+    weights: they differ only by the quantisation of h, so
+    |difference| <= |W2| (2^-4 |h32| + 2^-10 s_h + |h - h32|) elementwise.
+    A wrong tile or block scale, or a transposed operand, is far outside it."""
+    rng = np.random.default_rng(45)
+    n, d, I = 5, 256, 384
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    xq, xs = oracle.quantize_tiles(x)
+    (c1, s1), (c3, s3), (c2, s2) = _fp8_weights(rng, I, d), _fp8_weights(rng, I, d), _fp8_weights(rng, d, I)
+    w1, w3, w2 = oracle.dequantize_blocks(c1, s1), oracle.dequantize_blocks(c3, s3), oracle.dequantize_blocks(c2, s2)
+    out, hq, hs = oracle.swiglu_expert_fp8(xq, xs, w1, w3, w2)
+    xd = oracle.dequantize_tiles(xq, xs)
+    h = om.silu(xd @ w1.T) * (xd @ w3.T)
+    plain = h @ w2.T
+    assert np.allclose(plain, oracle.swiglu_expert(xd, w1, w3, w2), rtol=1e-12, atol=0)
+    h32 = h.astype(np.float32).astype(np.float64)
+    dh = 2.0 ** -4 * np.abs(h32) + 2.0 ** -10 * np.repeat(hs.astype(np.float64), 128, axis=1) + np.abs(h - h32)
+    bound = dh @ np.abs(w2).T
+    assert np.all(np.abs(out - plain) <= bound * (1 + 1e-9))
+    assert np.max(np.abs(out - plain)) > 0                     # h really was quantised
+
+
+def _e4m3_codes_torch(v):
+    return torch.tensor(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_fp8_expert_exact_case():
+    """A case where every quantisation is exact, so the fp8 expert must give
+    the exact SwiGLU result of the real values it was built from: x tiles
+    with amax 448 * 2^p (power-of-two scales), weights that are code values
+    times power-of-two block scales (encoded by torch's own cast), gate
+    pre-activations g = 56 or 112 (SiLU(g) == g in float64, and 1.75 * 2^m
+    keeps h on the E4M3 grid of its tile), and up values +-2^k. The expected
+    output is summed in exact rationals from the real values. A wrong tile,
+    block or row/column orientation of any scale changes the result."""
+    rng = np.random.default_rng(47)
+    n, d, I = 2, 256, 256
+    x = np.zeros((n, d))
+    for t in range(n):
+        x[t, 0], x[t, 1] = 448 * 2.0 ** -3, 2.0 ** -3 * (t + 1)
+        x[t, 128], x[t, 129] = 448 * 2.0 ** -1, 2.0 ** -1
+    W1 = np.zeros((I, d))
+    W1[:128, 0], W1[:128, 128] = 2.0 ** -1, 2.0 ** -3      # g = 28 + 28 = 56
+    W1[128:, 0], W1[128:, 128] = 1.0, 2.0 ** -2            # g = 56 + 56 = 112
+    s1 = np.float32([[2.0 ** -4, 2.0 ** -5], [2.0 ** -6, 2.0 ** -7]])
+    v = (2.0 ** rng.integers(-3, 2, I)) * rng.choice([-1.0, 1.0], I)
+    W3 = np.zeros((I, d))
+    W3[:, 1] = v * 2.0 ** 3                                  # u = (t + 1) v
+    s3 = np.float32([[2.0 ** -2, 1.0], [2.0 ** -3, 1.0]])
+    W2 = np.where(rng.random((d, I)) < 0.3, (2.0 ** rng.integers(-6, -2, (d, I))) * rng.choice([-1.0, 1.0], (d, I)), 0.0)
+    s2 = np.float32([[2.0 ** -9, 2.0 ** -8], [2.0 ** -10, 2.0 ** -7]])
+
+    def codes(w, sc):
+        return _e4m3_codes_torch(w / np.repeat(np.repeat(sc.astype(np.float64), 128, 0), 128, 1))
+
+    c1, c3, c2 = codes(W1, s1), codes(W3, s3), codes(W2, s2)
+    for c, w, sc in ((c1, W1, s1), (c3, W3, s3), (c2, W2, s2)):
+        assert np.array_equal(oracle.dequantize_blocks(c, sc), w)        # exact construction
+    xq, xs = oracle.quantize_tiles(x.astype(np.float32))
+    assert np.array_equal(xs, np.float32([[2.0 ** -3, 2.0 ** -1]] * n))
+    out, hq, hs = oracle.swiglu_expert_fp8(xq, xs, oracle.dequantize_blocks(c1, s1),
+                                           oracle.dequantize_blocks(c3, s3), oracle.dequantize_blocks(c2, s2))
+    g = np.where(np.arange(I) < 128, 56, 112)
+    for t in range(n):
+        h = [Fraction(int(g[i])) * (t + 1) * Fraction(v[i]) for i in range(I)]
+        for j in range(0, d, 7):
+            want = sum(Fraction(W2[j, i]) * h[i] for i in range(I) if W2[j, i] != 0)
+            assert Fraction(out[t, j]) == want
+
+
+def test_fp8_layer_identical_experts_and_shared_concat():
+    """With every routed expert identical the routed sum is (sum of gates) x
+    one expert; two shared experts passed concatenated equal the sum of the
+    two computed apart (the 1 x 128 tiles of h never straddle them)."""
+    rng = np.random.default_rng(46)
+    n, d, I, E, K = 6, 128, 256, 4, 2
+    xb = (rng.standard_normal((n, d)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    c1, s1 = _fp8_weights(rng, I, d)
+    c3, s3 = _fp8_weights(rng, I, d)
+    c2, s2 = _fp8_weights(rng, d, I)
+    sel = np.array([[0, 1], [2, 3], [1, 2], [3, 0], [0, 2], [1, 3]])
+    gate = rng.uniform(0.1, 0.9, (n, K))
+    bank = oracle.BlockExpertBank(fetch=lambda e: (c1, c3, c2, s1, s3, s2))
+    y, y_sh, routed = oracle.layer_rows_fp8(xb, sel, gate, bank)
+    xq, xs = oracle.quantize_x(xb)
+    one = oracle.swiglu_expert_fp8(xq, xs, *bank.expert(0))[0]
+    assert np.allclose(y, gate.sum(axis=1)[:, None] * one, rtol=1e-12, atol=1e-15)
+    assert np.all(y_sh == 0)
+    # shared: two experts of width I concatenated
+    d1, e1 = _fp8_weights(rng, 2 * I, d)
+    d3, e3 = _fp8_weights(rng, 2 * I, d)
+    d2, e2 = _fp8_weights(rng, d, 2 * I)
+    sh = oracle.BlockExpertBank(fetch=lambda e: (c1, c3, c2, s1, s3, s2),
+                                shared=(d1, d3, d2, e1, e3, e2), S=2)
+    _, ysh2, _ = oracle.layer_rows_fp8(xb, sel, gate, sh)
+    W1, W3, W2 = (oracle.dequantize_blocks(d1, e1), oracle.dequantize_blocks(d3, e3),
+                  oracle.dequantize_blocks(d2, e2))
+    apart = sum(oracle.swiglu_expert_fp8(xq, xs, W1[m * I:(m + 1) * I], W3[m * I:(m + 1) * I],
+                                         W2[:, m * I:(m + 1) * I])[0] for m in range(2))
+    assert np.allclose(ysh2, apart, rtol=1e-12, atol=1e-15)
