@@ -97,6 +97,7 @@ extern "C" {
 #define MOE_WS_SHARED  3
 #define MOE_WS_GEMM    4  /* moe_expert_gate_up / moe_expert_down */
 #define MOE_WS_EXPERTS 5  /* moe_experts */
+#define MOE_WS_EXPERTS_FP8 6  /* moe_experts_fp8 */
 
 /* Layer shape and options. Limits (checked by moe_validate): num_tokens >= 0
  * with num_tokens * top_k < 2^30; 1 <= num_experts <=
@@ -307,6 +308,64 @@ int moe_experts_down(const moe_config* cfg, const void* h, const void* hs,
                      const float* topk_gate, const void* w2, const float* s2, const void* w2s,
                      const float* s2s, void* out_slots, void* y_shared,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---- fine-grained fp8 experts ----------------------------------------------
+ * The FP8 scheme of [DSMoE] section 4.3: weights quantised to OCP E4M3FN in
+ * 128 x 128 blocks and activations in 1 x 128 tiles (one fp32 scale per
+ * block / tile), products accumulated in fp32 with each 128-wide block of
+ * the reduction multiplied by its two scales. Call sequence:
+ *   moe_route (bf16 x) -> moe_permute (x_perm = NULL) -> moe_quantize_act
+ *   -> moe_experts_fp8 (= moe_experts_fp8_gate_up + moe_experts_fp8_down)
+ *   -> moe_combine
+ * Requirements (else the status in brackets): bf16 activations and fp8
+ * weights [MOE_ERR_DTYPE]; weight_layout MOE_LAYOUT_TILED, hidden, inter
+ * and num_shared * shared_inter multiples of 128 [MOE_ERR_SHAPE], each at
+ * most 8192 [MOE_ERR_UNSUPPORTED].
+ *
+ * moe_quantize_act: for each token t and tile j (channels 128j .. 128j+127):
+ *   xs[t, j] = amax / 448 with amax = max |x[t, tile]| (fp32, rounded once;
+ *   1 when amax = 0), xq[t, c] = the E4M3 code nearest to x[t, c] / xs[t, j]
+ *   (fp32 division rounded once; ties to the even code; negative values
+ *   that round to zero give the code 0x80). x [T, d] bf16, xq [T, d] codes
+ *   (uint8), xs [T, d/128] fp32. Needs only act_dtype bf16 and d % 128 == 0.
+ *
+ * moe_experts_fp8: the routed and shared experts on the quantised tokens,
+ * with the routed rows read through perm_slot like moe_experts:
+ *   g = W1 x, u = W3 x (each 128-wide block of the reduction scaled by its
+ *   weight-block and token-tile scales), h = SiLU(g) * u in fp32, h
+ *   quantised in 1 x 128 tiles exactly as moe_quantize_act does, then
+ *   W2 h the same way; routed rows times their gate go to out_slots [T*K, d]
+ *   (bf16), the shared experts' sum to y_shared [T, d] (fp32).
+ *   w13 / w13s: the MOE_PACK_GATE_UP tensors of W1, W3 (groups E / 1);
+ *   w2 / w2s: the MOE_PACK_DOWN tensors; codes in both. Block scales (fp32):
+ *   s1, s3 [E, I/128, d/128] of W1, W3 (block (i, j) covers rows 128i.. and
+ *   columns 128j..), s2 [E, d/128, I/128] of W2; s1s, s3s [S*Is/128, d/128],
+ *   s2s [d/128, S*Is/128] (all shared pointers NULL when num_shared == 0).
+ *   Workspace: MOE_WS_EXPERTS_FP8 bytes (holds the quantised h).
+ * moe_experts_fp8_gate_up / moe_experts_fp8_down: its two launches, with the
+ *   quantised intermediate held by the caller: hq [T*K, I] codes and hs
+ *   [T*K, I/128] fp32 (routed rows in expert order), hsq [T, S*Is] codes and
+ *   hss [T, S*Is/128] (shared; NULL when num_shared == 0). Workspace:
+ *   MOE_WS_GEMM bytes each. */
+int moe_quantize_act(const moe_config* cfg, const void* x, void* xq, float* xs, void* stream);
+int moe_experts_fp8(const moe_config* cfg, const void* xq, const float* xs,
+                    const int32_t* expert_offsets, const int32_t* perm_slot,
+                    const float* topk_gate, const void* w13, const void* w2,
+                    const float* s1, const float* s3, const float* s2,
+                    const void* w13s, const void* w2s, const float* s1s, const float* s3s,
+                    const float* s2s, void* out_slots, void* y_shared,
+                    void* ws, size_t ws_bytes, void* stream);
+int moe_experts_fp8_gate_up(const moe_config* cfg, const void* xq, const float* xs,
+                            const int32_t* expert_offsets, const int32_t* perm_slot,
+                            const void* w13, const float* s1, const float* s3,
+                            const void* w13s, const float* s1s, const float* s3s,
+                            void* hq, float* hs, void* hsq, float* hss,
+                            void* ws, size_t ws_bytes, void* stream);
+int moe_experts_fp8_down(const moe_config* cfg, const void* hq, const float* hs,
+                         const void* hsq, const float* hss, const int32_t* expert_offsets,
+                         const int32_t* perm_slot, const float* topk_gate, const void* w2,
+                         const float* s2, const void* w2s, const float* s2s, void* out_slots,
+                         void* y_shared, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- moe_combine ----------------------------------------------------------
  * The layer output: shared experts plus the gate-weighted routed experts

@@ -44,12 +44,14 @@ MOE_WS_FFN = 2
 MOE_WS_SHARED = 3
 MOE_WS_GEMM = 4
 MOE_WS_EXPERTS = 5
+MOE_WS_EXPERTS_FP8 = 6
 
 EXPORTED = ("moe_validate", "moe_workspace_size", "moe_status_string", "moe_route",
             "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
             "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights",
             "moe_experts", "moe_experts_gate_up", "moe_experts_down", "moe_sequence_loads",
-            "moe_rmsnorm", "moe_combine_residual")
+            "moe_rmsnorm", "moe_combine_residual", "moe_quantize_act", "moe_experts_fp8",
+            "moe_experts_fp8_gate_up", "moe_experts_fp8_down")
 
 
 class MoEError(RuntimeError):
@@ -134,10 +136,15 @@ def load_library(path: str = LIB_PATH):
     lib.moe_sequence_loads.argtypes = [CFG, P, I32, P, P]
     lib.moe_rmsnorm.argtypes = [CFG, P, P, ctypes.c_double, P, P]
     lib.moe_combine_residual.argtypes = [CFG, P, P, P, P, P]
+    lib.moe_quantize_act.argtypes = [CFG, P, P, P, P]
+    lib.moe_experts_fp8.argtypes = [CFG] + [P] * 18 + [SZ, P]
+    lib.moe_experts_fp8_gate_up.argtypes = [CFG] + [P] * 15 + [SZ, P]
+    lib.moe_experts_fp8_down.argtypes = [CFG] + [P] * 14 + [SZ, P]
     for fn in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up",
                "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update",
                "moe_pack_weights", "moe_experts", "moe_experts_gate_up", "moe_experts_down",
-               "moe_sequence_loads", "moe_rmsnorm", "moe_combine_residual"):
+               "moe_sequence_loads", "moe_rmsnorm", "moe_combine_residual", "moe_quantize_act",
+               "moe_experts_fp8", "moe_experts_fp8_gate_up", "moe_experts_fp8_down"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -311,3 +318,36 @@ def moe_combine_residual(cfg, out_slots, y_shared, residual, y, stream=None):
     _check("moe_combine_residual", load_library().moe_combine_residual(
         ctypes.byref(cfg), _ptr(out_slots), _ptr(y_shared), _ptr(residual), _ptr(y),
         _stream(stream)))
+
+
+def moe_quantize_act(cfg, x, xq, xs, stream=None):
+    _check("moe_quantize_act", load_library().moe_quantize_act(
+        ctypes.byref(cfg), _ptr(x), _ptr(xq), _ptr(xs), _stream(stream)))
+
+
+def moe_experts_fp8(cfg, xq, xs, expert_offsets, perm_slot, topk_gate, w13, w2, s1, s3, s2,
+                    w13s, w2s, s1s, s3s, s2s, out_slots, y_shared, ws=None, stream=None):
+    wsb, nbytes = _ws(cfg, MOE_WS_EXPERTS_FP8, ws, out_slots)
+    _check("moe_experts_fp8", load_library().moe_experts_fp8(
+        ctypes.byref(cfg), _ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(perm_slot),
+        _ptr(topk_gate), _ptr(w13), _ptr(w2), _ptr(s1), _ptr(s3), _ptr(s2), _ptr(w13s),
+        _ptr(w2s), _ptr(s1s), _ptr(s3s), _ptr(s2s), _ptr(out_slots), _ptr(y_shared), _ptr(wsb),
+        nbytes, _stream(stream)))
+
+
+def moe_experts_fp8_gate_up(cfg, xq, xs, expert_offsets, perm_slot, w13, s1, s3, w13s, s1s,
+                            s3s, hq, hs, hsq, hss, ws=None, stream=None):
+    wsb, nbytes = _ws(cfg, MOE_WS_GEMM, ws, hq)
+    _check("moe_experts_fp8_gate_up", load_library().moe_experts_fp8_gate_up(
+        ctypes.byref(cfg), _ptr(xq), _ptr(xs), _ptr(expert_offsets), _ptr(perm_slot), _ptr(w13),
+        _ptr(s1), _ptr(s3), _ptr(w13s), _ptr(s1s), _ptr(s3s), _ptr(hq), _ptr(hs), _ptr(hsq),
+        _ptr(hss), _ptr(wsb), nbytes, _stream(stream)))
+
+
+def moe_experts_fp8_down(cfg, hq, hs, hsq, hss, expert_offsets, perm_slot, topk_gate, w2, s2,
+                         w2s, s2s, out_slots, y_shared, ws=None, stream=None):
+    wsb, nbytes = _ws(cfg, MOE_WS_GEMM, ws, out_slots)
+    _check("moe_experts_fp8_down", load_library().moe_experts_fp8_down(
+        ctypes.byref(cfg), _ptr(hq), _ptr(hs), _ptr(hsq), _ptr(hss), _ptr(expert_offsets),
+        _ptr(perm_slot), _ptr(topk_gate), _ptr(w2), _ptr(s2), _ptr(w2s), _ptr(s2s),
+        _ptr(out_slots), _ptr(y_shared), _ptr(wsb), nbytes, _stream(stream)))

@@ -49,6 +49,19 @@ int check_scales(const moe_config* c, const float* a, const float* b, const floa
   return (!a && !b && !d) ? MOE_OK : MOE_ERR_DTYPE;
 }
 
+// The fine-grained fp8 experts: bf16 activations quantised in 1 x 128 tiles,
+// fp8 weights in the tiled layout with 128 x 128 block scales; every
+// reduction length and weight-row count a multiple of 128, at most 8192.
+int check_fp8_block(const moe_config* c) {
+  if (c->act_dtype != MOE_DTYPE_BF16 || c->weight_dtype != MOE_DTYPE_FP8_E4M3) return MOE_ERR_DTYPE;
+  if (c->weight_layout != MOE_LAYOUT_TILED) return MOE_ERR_SHAPE;
+  const int64_t si = static_cast<int64_t>(c->num_shared) * c->shared_inter;
+  if (c->hidden % 128 != 0 || c->inter % 128 != 0 || (c->num_shared > 0 && si % 128 != 0))
+    return MOE_ERR_SHAPE;
+  if (c->hidden > 8192 || c->inter > 8192 || si > 8192) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +114,8 @@ size_t moe_workspace_size(const moe_config* c, int which) {
     case MOE_WS_SHARED: return (c->num_tokens == 0 || c->num_shared == 0) ? 0 : shared_ws_bytes(*c);
     case MOE_WS_GEMM: return c->num_tokens == 0 ? 0 : sched_ws_bytes(*c);
     case MOE_WS_EXPERTS: return c->num_tokens == 0 ? 0 : experts_ws_bytes(*c);
+    case MOE_WS_EXPERTS_FP8:
+      return (c->num_tokens == 0 || check_fp8_block(c) != MOE_OK) ? 0 : experts_fp8_ws_bytes(*c);
     default: return 0;
   }
 }
@@ -315,6 +330,88 @@ int moe_experts_down(const moe_config* c, const void* h, const void* hs,
   (void)hipGetLastError();
   return from_hip(launch_experts_down(*c, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2,
                                       w2s, s2s, out_slots, y_shared, ws, as_stream(stream)));
+}
+
+int moe_quantize_act(const moe_config* c, const void* x, void* xq, float* xs, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if (c->act_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (c->hidden % 128 != 0) return MOE_ERR_SHAPE;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!x || !xq || !xs) return MOE_ERR_NULL;
+  if (!aligned16(x, xq, xs)) return MOE_ERR_SHAPE;
+  (void)hipGetLastError();
+  return from_hip(launch_quantize_act(*c, x, xq, xs, as_stream(stream)));
+}
+
+int moe_experts_fp8(const moe_config* c, const void* xq, const float* xs,
+                    const int32_t* expert_offsets, const int32_t* perm_slot,
+                    const float* topk_gate, const void* w13, const void* w2, const float* s1,
+                    const float* s3, const float* s2, const void* w13s, const void* w2s,
+                    const float* s1s, const float* s3s, const float* s2s, void* out_slots,
+                    void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_fp8_block(c)) != MOE_OK) return st;
+  if (c->num_shared == 0 && (w13s || w2s || s1s || s3s || s2s || y_shared)) return MOE_ERR_SHAPE;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!xq || !xs || !expert_offsets || !perm_slot || !topk_gate || !w13 || !w2 || !s1 || !s3 ||
+      !s2 || !out_slots)
+    return MOE_ERR_NULL;
+  if (c->num_shared > 0 && (!w13s || !w2s || !s1s || !s3s || !s2s || !y_shared)) return MOE_ERR_NULL;
+  if (!aligned16(xq, xs, expert_offsets, perm_slot, topk_gate, w13, w2, s1, s3, s2, w13s, w2s, s1s,
+                 s3s, s2s, out_slots, y_shared))
+    return MOE_ERR_SHAPE;
+  if ((st = check_ws(moe_workspace_size(c, MOE_WS_EXPERTS_FP8), ws, ws_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return from_hip(launch_experts_fp8(*c, xq, xs, expert_offsets, perm_slot, topk_gate, w13, w2, s1,
+                                     s3, s2, w13s, w2s, s1s, s3s, s2s, out_slots, y_shared, ws,
+                                     as_stream(stream)));
+}
+
+int moe_experts_fp8_gate_up(const moe_config* c, const void* xq, const float* xs,
+                            const int32_t* expert_offsets, const int32_t* perm_slot,
+                            const void* w13, const float* s1, const float* s3, const void* w13s,
+                            const float* s1s, const float* s3s, void* hq, float* hs, void* hsq,
+                            float* hss, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_fp8_block(c)) != MOE_OK) return st;
+  if (c->num_shared == 0 && (w13s || s1s || s3s || hsq || hss)) return MOE_ERR_SHAPE;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!xq || !xs || !expert_offsets || !perm_slot || !w13 || !s1 || !s3 || !hq || !hs)
+    return MOE_ERR_NULL;
+  if (c->num_shared > 0 && (!w13s || !s1s || !s3s || !hsq || !hss)) return MOE_ERR_NULL;
+  if (!aligned16(xq, xs, expert_offsets, perm_slot, w13, s1, s3, w13s, s1s, s3s, hq, hs, hsq, hss))
+    return MOE_ERR_SHAPE;
+  if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return from_hip(launch_experts_fp8_gate_up(*c, xq, xs, expert_offsets, perm_slot, w13, s1, s3,
+                                             w13s, s1s, s3s, hq, hs, hsq, hss, ws,
+                                             as_stream(stream)));
+}
+
+int moe_experts_fp8_down(const moe_config* c, const void* hq, const float* hs, const void* hsq,
+                         const float* hss, const int32_t* expert_offsets,
+                         const int32_t* perm_slot, const float* topk_gate, const void* w2,
+                         const float* s2, const void* w2s, const float* s2s, void* out_slots,
+                         void* y_shared, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_validate(c);
+  if (st != MOE_OK) return st;
+  if ((st = check_fp8_block(c)) != MOE_OK) return st;
+  if (c->num_shared == 0 && (hsq || hss || w2s || s2s || y_shared)) return MOE_ERR_SHAPE;
+  if (c->num_tokens == 0) return MOE_OK;
+  if (!hq || !hs || !expert_offsets || !perm_slot || !topk_gate || !w2 || !s2 || !out_slots)
+    return MOE_ERR_NULL;
+  if (c->num_shared > 0 && (!hsq || !hss || !w2s || !s2s || !y_shared)) return MOE_ERR_NULL;
+  if (!aligned16(hq, hs, hsq, hss, expert_offsets, perm_slot, topk_gate, w2, s2, w2s, s2s,
+                 out_slots, y_shared))
+    return MOE_ERR_SHAPE;
+  if ((st = check_ws(moe_workspace_size(c, MOE_WS_GEMM), ws, ws_bytes)) != MOE_OK) return st;
+  (void)hipGetLastError();
+  return from_hip(launch_experts_fp8_down(*c, hq, hs, hsq, hss, expert_offsets, perm_slot,
+                                          topk_gate, w2, s2, w2s, s2s, out_slots, y_shared, ws,
+                                          as_stream(stream)));
 }
 
 int moe_combine(const moe_config* c, const void* out_slots, const void* y_shared, void* y,

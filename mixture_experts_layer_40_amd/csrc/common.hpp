@@ -55,6 +55,49 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(const u32x4& a, const u32x4& b, 
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 codes with unit block scales
+// (E8M0 exponent 127 = 1.0): lane l supplies 32 codes of row (l % 32) of
+// the first operand (a0 = the first 16, a1 the next) and the matching 32 of
+// column (l % 32) of the second; the result layout is that of
+// mfma_32x32x16. The instruction pairs the k-th code a lane supplies for A
+// with the k-th code the lane of the same half supplies for B, so any K
+// order that both operands share gives the same sum.
+__device__ __forceinline__ f32x16 mfma_32x32x64_fp8(const u32x4& a0, const u32x4& a1,
+                                                    const u32x4& b0, const u32x4& b1,
+                                                    const f32x16& c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 a = {static_cast<int>(a0.x), static_cast<int>(a0.y), static_cast<int>(a0.z),
+                   static_cast<int>(a0.w), static_cast<int>(a1.x), static_cast<int>(a1.y),
+                   static_cast<int>(a1.z), static_cast<int>(a1.w)};
+  const i32x8 b = {static_cast<int>(b0.x), static_cast<int>(b0.y), static_cast<int>(b0.z),
+                   static_cast<int>(b0.w), static_cast<int>(b1.x), static_cast<int>(b1.y),
+                   static_cast<int>(b1.z), static_cast<int>(b1.w)};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest even, for finite |v| <= 448
+// (larger magnitudes saturate to 448). Normal range: round the fp32
+// significand to 3 fraction bits (add-and-truncate at bit 20, whose carry
+// into the exponent is the correct result) and rebias the exponent from 127
+// to 7; below 2^-6 the value is a multiple of the subnormal step 2^-9,
+// rounded with rintf (ties to even) after an exact scaling by 2^9.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a >= 0.015625f) {                                  // 2^-6
+    uint32_t m = b & 0x7FFFFFFFu;
+    m += 0x7FFFFu + ((m >> 20) & 1u);
+    const int e = static_cast<int>(m >> 23) - 127 + 7;
+    code = (static_cast<uint32_t>(e) << 3) | ((m >> 20) & 7u);
+    code = e > 15 || code > 0x7Eu ? 0x7Eu : code;
+  } else {
+    code = static_cast<uint32_t>(rintf(a * 512.0f));     // 0 .. 8 (8 = 2^-6, code 0x08)
+  }
+  return sign | code;
+}
+
 // 4 fp8 E4M3 codes (one dword) -> 4 bf16 (two dwords). Every E4M3 value is
 // exactly representable in bf16, so the conversion is lossless.
 __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t q) {

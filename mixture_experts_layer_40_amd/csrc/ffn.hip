@@ -74,6 +74,10 @@ struct GemmSet {
   void* out;                  // down output [slots, n]
   int out_f32;                // down output is fp32 (else the activation dtype)
   int tiled;                  // weights in the tiled layout (wa only; see pack_tiles)
+  // fine-grained fp8 (grouped_gemm_f8b): act holds E4M3 codes; sa / sb are
+  // 128 x 128 block scales [E, n/128, kdim/128] of wa (W1 or W2) / W3
+  const float* ascale;        // token tile scales [act rows, kdim/128]
+  float* hscale;              // gate/up: h tile scales out [rows, n/128]
 };
 
 // A launch covers the tiles of one or two sets (set 0's tiles first), e.g.
@@ -242,6 +246,163 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
           u32x2 v;
           v.x = pack_bf16x2(ov[0], ov[1]);
           v.y = pack_bf16x2(ov[2], ov[3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fine-grained fp8 ("DeepSeekMoE架构解析" section 4.3): E4M3 weights with one
+// fp32 scale per 128 x 128 block and E4M3 tokens with one per 1 x 128 tile,
+// fp8 MFMA with fp32 accumulation. One K stage is one 128-wide block: its
+// partial sum (two MFMAs from zero) is added to the fp32 accumulators by
+// the VALU, times c = (weight block scale) x (token tile scale); the scales
+// of the tile's tokens and of each wave's weight rows are staged in LDS.
+// Gate/up writes h as E4M3 codes with one scale per 1 x 128 tile: a tile of
+// this kernel holds exactly the 128 intermediate columns of one h tile for
+// every token, so the tile's max-abs is a block-wide reduction.
+// ---------------------------------------------------------------------------
+constexpr int kF8MaxKB = 64;      // kdim <= 8192
+
+template <int MODE, int BM, int NSA>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_f8b(GemmArgs args) {
+  constexpr int NTF = BM / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t bs0[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs1[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs2[BM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t bs3[MOE_TOKEN_STAGES > 3 ? BM * 64 : 8];
+  __shared__ float tok_scale[BM][kF8MaxKB + 1];   // +1: the 32 rows of a read hit 32 banks
+  __shared__ float w_scale[kThreads / kWave][2][kF8MaxKB];
+  __shared__ float red[kThreads / kWave][BM];
+
+  Tile tl;
+  if (!decode_tile(args, BM, tl)) return;
+  const GemmSet& a = args.s[tl.set];
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
+  const int ntf = (tl.mvalid + 31) >> 5;
+  const int nkb = a.kdim / 128;
+
+  // this wave's 32-row fragment of the tiled weights (32 x 128 codes per stage)
+  const int rb = tl.nblk * 8 + w;
+  const int nrow0 = MODE == kGateUp ? 16 * rb : 32 * rb;
+  const bool wvalid = nrow0 < a.n;
+  const int rbv = wvalid ? rb : 0;
+  constexpr int astage = 32 * 128, avs = 1024;
+  const uint8_t* aptr = static_cast<const uint8_t*>(a.wa) + static_cast<size_t>(tl.e) * a.wstride +
+                        static_cast<size_t>(rbv) * nkb * astage + 16 * l;
+
+  // token tile scales (rows past the expert's end repeat its last row)
+  for (int i = tid; i < BM * nkb; i += kThreads) {
+    const int row = i / nkb, kb = i - row * nkb;
+    const int p = tl.row0 + (row < tl.mvalid ? row : tl.mvalid - 1);
+    const int src = a.act_rows ? max(a.act_rows[p], 0) / a.act_div : p;
+    tok_scale[row][kb] = a.ascale[static_cast<size_t>(src) * nkb + kb];
+  }
+  // weights: gate/up waves share the tile's W1 and W3 blocks; a down wave's
+  // 32 rows lie in one 128-row block
+  if (l < nkb) {
+    const int nbr = a.n / 128;
+    const int blk = MODE == kGateUp ? tl.nblk : (32 * rbv) / 128;
+    const size_t o = (static_cast<size_t>(tl.e) * nbr + blk) * nkb;
+    const float* s1 = a.sa + o;
+    const float* s3 = MODE == kGateUp ? a.sb + o : s1;
+    w_scale[w][0][l] = s1[l];
+    w_scale[w][1][l] = s3[l];
+  }
+  __syncthreads();
+
+  f32x16 acc[NTF];
+#pragma unroll
+  for (int t = 0; t < NTF; ++t) acc[t] = f32x16{};
+  // acc += block partial x scales; gate/up: elements 0..7 are W1 rows,
+  // 8..15 W3 rows; down: one weight block per wave
+  auto post = [&](auto ntc, int s, auto& blk) {
+    constexpr int NT = decltype(ntc)::value;
+    const float sw1 = w_scale[w][0][s], sw3 = w_scale[w][1][s];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float st = tok_scale[32 * t + r32][s];
+      const float c1 = st * sw1, c3 = st * sw3;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[t][e] = fmaf(blk[t][e], c1, acc[t][e]);
+#pragma unroll
+      for (int e = 8; e < 16; ++e) acc[t][e] = fmaf(blk[t][e], c3, acc[t][e]);
+    }
+  };
+
+  const uint16_t* act = static_cast<const uint16_t*>(a.act);
+  const int kdim16 = a.kdim / 2;                  // a row of codes in 16-bit units
+  using ML = MainLoop<false, NSA, BM, true>;
+  switch (ntf) {
+#define MOE_NT_CASE(n) \
+    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, kdim16, astage, avs, bs0, bs1, bs2, bs3, acc, post); break;
+    MOE_NT_CASE(1) MOE_NT_CASE(2) MOE_NT_CASE(3) MOE_NT_CASE(4)
+#undef MOE_NT_CASE
+    default: break;
+  }
+
+  if (MODE == kGateUp) {
+    // every wave of a gate/up tile is valid (n % 128 == 0) and takes part in
+    // the block-wide max-abs
+    float hv[NTF][8];
+#pragma unroll
+    for (int t = 0; t < NTF; ++t) {
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          hv[t][4 * i + q] = silu(acc[t][4 * i + q]) * acc[t][4 * (i + 2) + q];
+          m = fmaxf(m, fabsf(hv[t][4 * i + q]));
+        }
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      if (g == 0) red[w][32 * t + r32] = m;
+    }
+    __syncthreads();
+    uint8_t* hq = static_cast<uint8_t*>(a.h);
+    const int nts = a.n / 128;
+#pragma unroll
+    for (int t = 0; t < NTF; ++t) {
+      const int tok = 32 * t + r32;
+      if (!(t < ntf && tok < tl.mvalid)) continue;
+      float amax = red[0][tok];
+#pragma unroll
+      for (int ww = 1; ww < kThreads / kWave; ++ww) amax = fmaxf(amax, red[ww][tok]);
+      const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+      const size_t row = static_cast<size_t>(tl.row0 + tok);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) packed |= f32_to_e4m3(__fdiv_rn(hv[t][4 * i + q], sc)) << (8 * q);
+        *reinterpret_cast<uint32_t*>(hq + row * a.n + nrow0 + 8 * i + 4 * g) = packed;
+      }
+      if (w == 0 && g == 0) a.hscale[row * nts + tl.nblk] = sc;
+    }
+  } else {
+    if (!wvalid) return;
+#pragma unroll
+    for (int t = 0; t < NTF; ++t) {
+      const int tok = 32 * t + r32;
+      if (!(t < ntf && tok < tl.mvalid)) continue;
+      const int p = tl.row0 + tok;
+      const int slot = a.perm_slot ? a.perm_slot[p] : p;
+      if (slot < 0) continue;
+      const float gv = a.gate ? a.gate[slot] : 1.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = nrow0 + 8 * i + 4 * g;
+        const size_t o = static_cast<size_t>(slot) * a.n + col;
+        const float o0 = acc[t][4 * i] * gv, o1 = acc[t][4 * i + 1] * gv;
+        const float o2 = acc[t][4 * i + 2] * gv, o3 = acc[t][4 * i + 3] * gv;
+        if (a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{o0, o1, o2, o3};
+        } else {
+          u32x2 v;
+          v.x = pack_bf16x2(o0, o1);
+          v.y = pack_bf16x2(o2, o3);
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = v;
         }
       }
@@ -508,6 +669,60 @@ int64_t routed_max_tiles(const moe_config& c, int bm, int nb) {
   return ((TK + bm - 1) / bm + c.num_experts) * nb;
 }
 
+// ---- fine-grained fp8 (grouped_gemm_f8b) -----------------------------------
+
+template <int MODE>
+void launch_f8b_bm(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
+  switch (bm) {
+    case 32: hipLaunchKernelGGL((grouped_gemm_f8b<MODE, 32, 3>), gd, dim3(kThreads), 0, s, a); break;
+    case 64: hipLaunchKernelGGL((grouped_gemm_f8b<MODE, 64, 3>), gd, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_f8b<MODE, 128, 3>), gd, dim3(kThreads), 0, s, a); break;
+  }
+}
+
+hipError_t run_f8b(int mode, int bm, const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
+  const int64_t grid = grid_for(max_tiles);
+  if (grid <= 0) return hipSuccess;
+  const dim3 gd(static_cast<unsigned>(grid));
+  if (mode == kGateUp) launch_f8b_bm<kGateUp>(bm, gd, s, a);
+  else launch_f8b_bm<kDown>(bm, gd, s, a);
+  return hipGetLastError();
+}
+
+// Token tiles of at most 128 rows (two sets of accumulators do not fit 256).
+Blocking blocking_f8b(const moe_config& c, int n_inter, int64_t rows_per_group) {
+  return {std::min(pick_bm(rows_per_group), 128), n_inter / 128, (c.hidden + kBNDown - 1) / kBNDown};
+}
+
+GemmSet f8b_gate_up(const moe_config& c, const Blocking& b, const void* xq, const float* xs,
+                    const int32_t* act_rows, const int32_t* offsets, const int32_t* sched,
+                    int n, int fixed_m, const void* w13, const float* s1, const float* s3,
+                    void* hq, float* hs) {
+  GemmSet g{};
+  g.act = xq; g.ascale = xs; g.act_rows = act_rows; g.act_div = c.top_k;
+  g.wa = w13; g.sa = s1; g.sb = s3;
+  g.offsets = offsets; g.sched = sched; g.fixed_m = fixed_m; g.E = offsets ? c.num_experts : 1;
+  g.kdim = c.hidden; g.n = n; g.nb = b.nb1; g.h = hq; g.hscale = hs;
+  g.tiled = 1;
+  g.wstride = 2LL * n * c.hidden;                // bytes of one expert's tiled gate/up tensor
+  return g;
+}
+
+GemmSet f8b_down(const moe_config& c, const Blocking& b, const void* hq, const float* hs,
+                 const int32_t* offsets, const int32_t* sched, int kdim, int fixed_m,
+                 const int32_t* perm_slot, const float* gate, const void* w2, const float* s2,
+                 void* out, int out_f32) {
+  GemmSet g{};
+  g.act = hq; g.ascale = hs;
+  g.wa = w2; g.sa = s2;
+  g.offsets = offsets; g.sched = sched; g.fixed_m = fixed_m; g.E = offsets ? c.num_experts : 1;
+  g.kdim = kdim; g.n = c.hidden; g.nb = b.nb2;
+  g.tiled = 1;
+  g.wstride = static_cast<int64_t>(c.hidden) * kdim;
+  g.perm_slot = perm_slot; g.gate = gate; g.out = out; g.out_f32 = out_f32;
+  return g;
+}
+
 }  // namespace
 
 size_t sched_ws_bytes(const moe_config& c) { return align_up(static_cast<size_t>(c.num_experts + 1) * 4, 256); }
@@ -655,6 +870,107 @@ hipError_t launch_experts(const moe_config& c, const void* x, const int32_t* exp
   if (err != hipSuccess) return err;
   return launch_experts_down(c, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w2s, s2s,
                              out_slots, y_shared, sched, s);
+}
+
+// ---- fine-grained fp8 experts ------------------------------------------------
+
+size_t hq_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_tokens) * c.top_k * c.inter, 256);
+}
+size_t hs_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_tokens) * c.top_k * (c.inter / 128) * 4, 256);
+}
+size_t hsq_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_tokens) * c.num_shared * c.shared_inter, 256);
+}
+size_t hss_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_tokens) * (c.num_shared * c.shared_inter / 128) * 4, 256);
+}
+
+size_t experts_fp8_ws_bytes(const moe_config& c) {
+  size_t b = hq_bytes(c) + hs_bytes(c) + sched_ws_bytes(c);
+  if (c.num_shared > 0) b += hsq_bytes(c) + hss_bytes(c);
+  return b;
+}
+
+hipError_t launch_experts_fp8_gate_up(const moe_config& c, const void* xq, const float* xs,
+                                      const int32_t* expert_offsets, const int32_t* perm_slot,
+                                      const void* w13, const float* s1, const float* s3,
+                                      const void* w13s, const float* s1s, const float* s3s,
+                                      void* hq, float* hs, void* hsq, float* hss, void* ws,
+                                      hipStream_t s) {
+  const int E = c.num_experts, T = c.num_tokens, SI = c.num_shared * c.shared_inter;
+  const int64_t TK = static_cast<int64_t>(T) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  const Blocking b = blocking_f8b(c, c.inter, (TK + E - 1) / E);
+  int32_t* sched = static_cast<int32_t*>(ws);
+  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb1, sched, s);
+  if (err != hipSuccess) return err;
+  GemmArgs a{};
+  int64_t tiles = routed_max_tiles(c, b.bm, b.nb1);
+  if (c.num_shared > 0) {
+    const Blocking bs = blocking_f8b(c, SI, T);
+    a.s[a.nsets++] = f8b_gate_up(c, bs, xq, xs, nullptr, nullptr, nullptr, SI, T, w13s, s1s, s3s,
+                                 hsq, hss);
+    tiles += ((T + b.bm - 1) / b.bm) * bs.nb1;
+  }
+  a.s[a.nsets++] = f8b_gate_up(c, b, xq, xs, perm_slot, expert_offsets, sched, c.inter, 0, w13,
+                               s1, s3, hq, hs);
+  return run_f8b(kGateUp, b.bm, a, tiles, s);
+}
+
+hipError_t launch_experts_fp8_down(const moe_config& c, const void* hq, const float* hs,
+                                   const void* hsq, const float* hss,
+                                   const int32_t* expert_offsets, const int32_t* perm_slot,
+                                   const float* topk_gate, const void* w2, const float* s2,
+                                   const void* w2s, const float* s2s, void* out_slots,
+                                   void* y_shared, void* ws, hipStream_t s) {
+  const int E = c.num_experts, T = c.num_tokens, SI = c.num_shared * c.shared_inter;
+  const int64_t TK = static_cast<int64_t>(T) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  const Blocking b = blocking_f8b(c, c.inter, (TK + E - 1) / E);
+  int32_t* sched = static_cast<int32_t*>(ws);
+  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb2, sched, s);
+  if (err != hipSuccess) return err;
+  GemmArgs a{};
+  int64_t tiles = routed_max_tiles(c, b.bm, b.nb2);
+  if (c.num_shared > 0) {
+    const Blocking bs = blocking_f8b(c, SI, T);
+    a.s[a.nsets++] = f8b_down(c, bs, hsq, hss, nullptr, nullptr, SI, T, nullptr, nullptr, w2s, s2s,
+                              y_shared, 1);
+    tiles += ((T + b.bm - 1) / b.bm) * bs.nb2;
+  }
+  a.s[a.nsets++] = f8b_down(c, b, hq, hs, expert_offsets, sched, c.inter, 0, perm_slot, topk_gate,
+                            w2, s2, out_slots, c.act_dtype == MOE_DTYPE_F32);
+  return run_f8b(kDown, b.bm, a, tiles, s);
+}
+
+hipError_t launch_experts_fp8(const moe_config& c, const void* xq, const float* xs,
+                              const int32_t* expert_offsets, const int32_t* perm_slot,
+                              const float* topk_gate, const void* w13, const void* w2,
+                              const float* s1, const float* s3, const float* s2,
+                              const void* w13s, const void* w2s, const float* s1s,
+                              const float* s3s, const float* s2s, void* out_slots,
+                              void* y_shared, void* ws, hipStream_t s) {
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  void* hq = p;
+  p += hq_bytes(c);
+  float* hs = reinterpret_cast<float*>(p);
+  p += hs_bytes(c);
+  void* hsq = nullptr;
+  float* hss = nullptr;
+  if (c.num_shared > 0) {
+    hsq = p;
+    p += hsq_bytes(c);
+    hss = reinterpret_cast<float*>(p);
+    p += hss_bytes(c);
+  }
+  void* sched = p;
+  hipError_t err = launch_experts_fp8_gate_up(c, xq, xs, expert_offsets, perm_slot, w13, s1, s3,
+                                              w13s, s1s, s3s, hq, hs, hsq, hss, sched, s);
+  if (err != hipSuccess) return err;
+  return launch_experts_fp8_down(c, hq, hs, hsq, hss, expert_offsets, perm_slot, topk_gate, w2, s2,
+                                 w2s, s2s, out_slots, y_shared, sched, s);
 }
 
 hipError_t launch_pack(int which, int64_t groups, int rows, int cols, int wbytes,

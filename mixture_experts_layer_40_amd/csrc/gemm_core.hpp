@@ -1,5 +1,6 @@
 // The K loop shared by the grouped expert GEMMs and the router GEMM on
-// gfx950: v_mfma_f32_32x32x16_bf16 with weight rows as the first operand,
+// gfx950: v_mfma_f32_32x32x16_bf16 (or, for fp8 codes on both sides,
+// v_mfma_scale_f32_32x32x64_f8f6f4) with weight rows as the first operand,
 // token rows as the second, tokens staged through LDS by direct loads.
 #pragma once
 
@@ -24,6 +25,20 @@ namespace moe {
 // over its MFMAs. The K loop is specialised on the number NT of 32-token
 // fragments the tile really has: branch-free, and a tile with 3 rows costs
 // one fragment.
+//
+// F8B (fine-grained fp8, "DeepSeekMoE架构解析" section 4.3): weights and
+// tokens are both E4M3 codes and a stage is 128 K-elements -- one block of
+// the 128 x 128 weight scales and of the 1 x 128 token scales, and the same
+// bytes per stage as the bf16 loop (4 KB of a 32-row tiled fragment, 128
+// bytes per token row), so the DMA and the counter waits are unchanged. A
+// stage is two 32x32x64 fp8 MFMAs per token fragment into a block partial
+// that starts from zero; the caller's hook `post(NT, s, blk)` then adds the
+// partials, times their scales, into its fp32 accumulators. The fp8 MFMA
+// aligns its 64 products (and its C input) to the largest before summing,
+// losing bits below about 2^-12 of that sum, so a long accumulation kept
+// inside the MFMA chain would lose accuracy as the sum grows; promoting
+// each 128-wide block to VALU fp32 bounds the loss by the block's own
+// magnitude (the promotion of "DeepSeekMoE架构解析" section 4.3).
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 512;
 #ifndef MOE_TOKEN_STAGES
@@ -59,8 +74,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool FP8, int NSA, int BM>
+struct NoPost {
+  template <class N, class A>
+  __device__ __forceinline__ void operator()(N, int, A&) const {}
+};
+
+template <bool FP8, int NSA, int BM, bool F8B = false>
 struct MainLoop {
+  static_assert(!(FP8 && F8B), "F8B takes fp8 codes on both sides; FP8 widens weights to bf16");
   static constexpr int AW = FP8 ? 2 : 4;       // 16-byte loads per fragment per stage
   static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
   static constexpr int ND = MOE_TOKEN_STAGES;  // LDS token stages (ND-1 in flight)
@@ -72,12 +93,24 @@ struct MainLoop {
   // its last row, prefetches past the last stage re-read the last stage, and
   // when a stage has fewer 16-byte chunks than threads the extra threads
   // repeat a chunk (writing the same bytes to the same place).
+  // kdim counts 16-bit units of a token row (fp8 rows: bytes / 2); one
+  // stage is 64 such units.
   template <int NT>
   __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
                                              const int32_t* act_rows, int act_div, int mvalid,
                                              int kdim, int astage, int avs,
                                              uint16_t* bs0, uint16_t* bs1, uint16_t* bs2,
                                              uint16_t* bs3, f32x16 (&acc)[BM / 32]) {
+    run<NT>(aptr, act, row0, act_rows, act_div, mvalid, kdim, astage, avs, bs0, bs1, bs2, bs3,
+            acc, NoPost{});
+  }
+
+  template <int NT, class Post>
+  __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
+                                             const int32_t* act_rows, int act_div, int mvalid,
+                                             int kdim, int astage, int avs,
+                                             uint16_t* bs0, uint16_t* bs1, uint16_t* bs2,
+                                             uint16_t* bs3, f32x16 (&acc)[BM / 32], Post&& post) {
     constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
     constexpr int BCH = (CH + kThreads - 1) / kThreads; // copies per thread per stage
     const int l = lane_id(), g = l >> 5, r32 = l & 31;
@@ -122,6 +155,36 @@ struct MainLoop {
     // over its 4*NT MFMAs: issued in one burst they queue at the CU's
     // address unit and hold every wave's MFMAs back behind them.
     constexpr int NV = BCH + AW;
+    // F8B: the two 64-wide halves m of a 128-wide stage; lane group g takes
+    // codes 32g .. 32g+31 of each half: weight pieces 2m, 2m+1 and token
+    // chunks 4m+2g, 4m+2g+1 (the same K order on both operands).
+    auto read_b8 = [&](u32x4 (&dst)[2], const uint16_t* b0, int t, int m) {
+      const int tok = 32 * t + r32, c0 = 4 * m + 2 * g, sw = (tok >> 1) & 7;
+      const uint16_t* row = b0 + tok * 64;
+      dst[0] = *reinterpret_cast<const u32x4*>(row + ((c0 ^ sw) * 8));
+      dst[1] = *reinterpret_cast<const u32x4*>(row + (((c0 + 1) ^ sw) * 8));
+    };
+    auto compute8 = [&](const u32x4 (&src)[AW], const uint16_t* b0, f32x16 (&blk)[NT],
+                        auto&& issue) {
+      u32x4 bfr[2][NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) read_b8(bfr[0][t], b0, t, 0);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (m == 0) read_b8(bfr[1][t], b0, t, 1);
+          blk[t] = mfma_32x32x64_fp8(src[2 * m], src[2 * m + 1], bfr[m][t][0], bfr[m][t][1],
+                                     m == 0 ? f32x16{} : blk[t]);
+          const int i = m * NT + t;
+          static_for<NV>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if ((k * 2 * NT) / NV == i) issue(kc);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
     auto compute = [&](const u32x4 (&src)[AW], const uint16_t* b0, auto&& issue) {
       u32x4 bfr[2][NT];
 #pragma unroll
@@ -182,7 +245,13 @@ struct MainLoop {
       };
       // W(s) landed: after its last piece came the requests of NSA-2 stages
       wait_vmcnt<(NSA - 2) * NV>();
-      compute(ra[u % NSA], buf(u % ND), issue);
+      if constexpr (F8B) {
+        f32x16 blk[NT];
+        compute8(ra[u % NSA], buf(u % ND), blk, issue);
+        post(IntC<NT>{}, s, blk);
+      } else {
+        compute(ra[u % NSA], buf(u % ND), issue);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // T(s+1) landed: after it were issued the W of its stage and the
       // T and W of ND-2 stages. A plain barrier: the fence of __syncthreads

@@ -65,6 +65,30 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
                              const float* s3s, const float* s2s, void* y_shared, void* ws,
                              hipStream_t s);
 
+// ---- fine-grained fp8 experts (128 x 128 weight blocks, 1 x 128 token tiles) --
+hipError_t launch_quantize_act(const moe_config& c, const void* x, void* xq, float* xs,
+                               hipStream_t s);
+size_t experts_fp8_ws_bytes(const moe_config& c);
+hipError_t launch_experts_fp8_gate_up(const moe_config& c, const void* xq, const float* xs,
+                                      const int32_t* expert_offsets, const int32_t* perm_slot,
+                                      const void* w13, const float* s1, const float* s3,
+                                      const void* w13s, const float* s1s, const float* s3s,
+                                      void* hq, float* hs, void* hsq, float* hss, void* ws,
+                                      hipStream_t s);
+hipError_t launch_experts_fp8_down(const moe_config& c, const void* hq, const float* hs,
+                                   const void* hsq, const float* hss,
+                                   const int32_t* expert_offsets, const int32_t* perm_slot,
+                                   const float* topk_gate, const void* w2, const float* s2,
+                                   const void* w2s, const float* s2s, void* out_slots,
+                                   void* y_shared, void* ws, hipStream_t s);
+hipError_t launch_experts_fp8(const moe_config& c, const void* xq, const float* xs,
+                              const int32_t* expert_offsets, const int32_t* perm_slot,
+                              const float* topk_gate, const void* w13, const void* w2,
+                              const float* s1, const float* s3, const float* s2,
+                              const void* w13s, const void* w2s, const float* s1s,
+                              const float* s3s, const float* s2s, void* out_slots,
+                              void* y_shared, void* ws, hipStream_t s);
+
 hipError_t launch_sequence_loads(const moe_config& c, const int32_t* topk_idx, int seq_len,
                                  int32_t* seq_load, hipStream_t s);
 

@@ -9,6 +9,9 @@ forward() enqueues, on the current stream,
 
     fused (default with bf16 activations):
         moe_route -> moe_permute (no row gather) -> moe_experts -> moe_combine
+    fine-grained fp8 (weights with 128 x 128 block scales):
+        moe_route -> moe_permute (no row gather) -> moe_quantize_act
+        -> moe_experts_fp8 -> moe_combine
     otherwise:
         moe_shared_ffn (second stream)  ||  moe_route -> moe_permute -> moe_expert_ffn
         -> join -> moe_combine
@@ -40,6 +43,9 @@ class MoELayer:
             layout = "rows" if spec.weight_dtype == "f32" else "tiled"
         self.layout = layout
         self.fused = spec.act_dtype == "bf16" if fused is None else fused
+        self.fp8_block = getattr(spec, "fp8_scaling", "row") == "block"
+        if self.fp8_block and (layout != "tiled" or not self.fused):
+            raise ValueError("block-scaled fp8 experts run fused on the tiled layout")
         self.pre_norm, self.residual = pre_norm, residual
         self.w = dict(weights)
         if layout == "tiled":
@@ -75,7 +81,11 @@ class MoELayer:
         self.ws_perm = ws(L.MOE_WS_PERMUTE)
         self.ws_ffn = ws(L.MOE_WS_FFN)
         self.ws_shared = ws(L.MOE_WS_SHARED)
-        self.ws_experts = ws(L.MOE_WS_EXPERTS) if self.fused else None
+        self.ws_experts = ws(L.MOE_WS_EXPERTS) if self.fused and not self.fp8_block else None
+        if self.fp8_block:
+            self.xq = torch.empty((T, d), dtype=torch.uint8, device=dev)
+            self.xs = torch.empty((T, d // 128), dtype=torch.float32, device=dev)
+            self.ws_experts = ws(L.MOE_WS_EXPERTS_FP8)
         self.side = (torch.cuda.Stream(device=dev)
                      if (shared_stream and spec.S > 0 and not self.fused) else None)
 
@@ -104,6 +114,15 @@ class MoELayer:
                       w.get("s2"), w.get("w1s"), w.get("w3s"), w.get("w2s"), w.get("s1s"),
                       w.get("s3s"), w.get("s2s"), self.out_slots[:T * cfg.top_k],
                       None if self.y_shared is None else self.y_shared[:T], ws=self.ws_experts)
+
+    def experts_fp8(self, cfg, x):
+        T, w = cfg.num_tokens, self.w
+        L.moe_quantize_act(cfg, x, self.xq[:T], self.xs[:T])
+        L.moe_experts_fp8(cfg, self.xq[:T], self.xs[:T], self.expert_offsets,
+                          self.perm_slot[:T * cfg.top_k], self.topk_gate[:T], w["w1"], w["w2"],
+                          w["s1"], w["s3"], w["s2"], w.get("w1s"), w.get("w2s"), w.get("s1s"),
+                          w.get("s3s"), w.get("s2s"), self.out_slots[:T * cfg.top_k],
+                          None if self.y_shared is None else self.y_shared[:T], ws=self.ws_experts)
 
     def experts(self, cfg):
         T, w = cfg.num_tokens, self.w
@@ -140,7 +159,10 @@ class MoELayer:
         if self.fused:
             self.route(x, bias)
             self.permute(cfg, x, gather=False)
-            self.experts_fused(cfg, x)
+            if self.fp8_block:
+                self.experts_fp8(cfg, x)
+            else:
+                self.experts_fused(cfg, x)
             self.combine(cfg, res)
             return self.y[:cfg.num_tokens]
         cur = torch.cuda.current_stream(self.device)

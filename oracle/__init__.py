@@ -55,6 +55,7 @@ from .fp8block import (  # noqa: F401
     quantize_tiles,
     dequantize_tiles,
     dequantize_blocks,
+    expert_h_fp8,
     swiglu_expert_fp8,
     BlockExpertBank,
     quantize_x,

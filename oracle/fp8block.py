@@ -93,14 +93,20 @@ def dequantize_blocks(codes: np.ndarray, scales: np.ndarray, block: int = TILE) 
     return e4m3_to_f64(codes) * full
 
 
-def swiglu_expert_fp8(xq: np.ndarray, xs: np.ndarray, w1, w3, w2) -> np.ndarray:
-    """One SwiGLU expert on quantised rows: xq codes [n, d] with tile scales
-    xs [n, d/128]; w1, w3 [I, d] and w2 [d, I] float64 (dequantised blocks).
-    h = SiLU(W1 x) * (W3 x) in float64, rounded to fp32, quantised in 1 x 128
-    tiles, then W2 h. Returns (out [n, d] float64, hq, hs)."""
+def expert_h_fp8(xq: np.ndarray, xs: np.ndarray, w1, w3) -> np.ndarray:
+    """The intermediate of one SwiGLU expert on quantised rows, h = SiLU(W1 x)
+    * (W3 x) in float64 from the dequantised tokens (xq codes [n, d], tile
+    scales xs [n, d/128]) and weights (w1, w3 [I, d] float64), rounded to the
+    fp32 value that the 1 x 128 quantisation of h starts from."""
     x = dequantize_tiles(xq, xs)
-    h = silu(x @ w1.T) * (x @ w3.T)
-    hq, hs = quantize_tiles(h.astype(np.float32))
+    return (silu(x @ w1.T) * (x @ w3.T)).astype(np.float32)
+
+
+def swiglu_expert_fp8(xq: np.ndarray, xs: np.ndarray, w1, w3, w2) -> np.ndarray:
+    """One SwiGLU expert on quantised rows (w2 [d, I] float64): h from
+    expert_h_fp8, quantised in 1 x 128 tiles, then W2 h.
+    Returns (out [n, d] float64, hq, hs)."""
+    hq, hs = quantize_tiles(expert_h_fp8(xq, xs, w1, w3))
     return dequantize_tiles(hq, hs) @ w2.T, hq, hs
 
 

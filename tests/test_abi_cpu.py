@@ -254,3 +254,41 @@ def test_norm_residual_and_alignment_validate_on_host():
     assert lib.moe_bias_update(8, fake, ctypes.c_float(1e-3), odd, None) == L.MOE_ERR_SHAPE
     assert lib.moe_pack_weights(L.MOE_PACK_DOWN, 1, 32, 64, L.MOE_DTYPE_BF16, odd, None, fake, None) == L.MOE_ERR_SHAPE
     assert lib.moe_expert_down(by(c), fake, fake, fake, fake, odd, None, fake, None, 0, None) == L.MOE_ERR_SHAPE
+
+
+def test_fp8_block_entry_points_validate_on_host():
+    lib = moe.load_library()
+    by = ctypes.byref
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    ok = _cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=256, I=256, Is=256)
+    assert moe.moe_workspace_size(ok, moe.MOE_WS_EXPERTS_FP8) > 0
+    q = lib.moe_quantize_act
+    assert q(by(_cfg()), fake, fake, fake, None) == L.MOE_ERR_DTYPE          # fp32 activations
+    assert q(by(_cfg(act_dtype="bf16", weight_dtype="bf16", d=192)), fake, fake, fake, None) == L.MOE_ERR_SHAPE
+    assert q(by(ok), None, fake, fake, None) == L.MOE_ERR_NULL
+    assert q(by(ok), fake, odd, fake, None) == L.MOE_ERR_SHAPE
+    assert q(by(_cfg(act_dtype="bf16", weight_dtype="bf16", T=0)), None, None, None, None) == L.MOE_OK
+    ex = lib.moe_experts_fp8
+    full = [fake] * 17
+    # dtype, layout and 128-multiple requirements, each before any launch
+    assert ex(by(_cfg(act_dtype="bf16", weight_dtype="bf16", weight_layout="tiled", d=256, I=256, Is=256)), *full, None, 0, None) == L.MOE_ERR_DTYPE
+    assert ex(by(_cfg(act_dtype="bf16", weight_dtype="fp8", d=256, I=256, Is=256)), *full, None, 0, None) == L.MOE_ERR_SHAPE
+    assert ex(by(_cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=192, I=256, Is=256)), *full, None, 0, None) == L.MOE_ERR_SHAPE
+    assert ex(by(_cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=256, I=320, Is=256)), *full, None, 0, None) == L.MOE_ERR_SHAPE
+    assert ex(by(_cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=8320, I=256, Is=256)), *full, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    assert ex(by(ok), *full, None, 0, None) == L.MOE_ERR_WORKSPACE
+    args = list(full)
+    args[7] = None                                                    # s3 missing
+    assert ex(by(ok), *args, None, 0, None) == L.MOE_ERR_NULL
+    args = list(full)
+    args[0] = odd
+    assert ex(by(ok), *args, None, 0, None) == L.MOE_ERR_SHAPE
+    noshared = _cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=256, I=256, S=0, Is=256)
+    assert ex(by(noshared), *full, None, 0, None) == L.MOE_ERR_SHAPE   # shared pointers given
+    gu, dn = lib.moe_experts_fp8_gate_up, lib.moe_experts_fp8_down
+    assert gu(by(ok), *[fake] * 14, None, 0, None) == L.MOE_ERR_WORKSPACE
+    assert dn(by(ok), *[fake] * 13, None, 0, None) == L.MOE_ERR_WORKSPACE
+    assert gu(by(ok), *([fake] * 10 + [None] + [fake] * 3), None, 0, None) == L.MOE_ERR_NULL   # hq
+    assert dn(by(ok), *([None] + [fake] * 12), None, 0, None) == L.MOE_ERR_NULL
+    z = _cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=256, I=256, Is=256, T=0)
+    assert ex(by(z), *([None] * 17), None, 0, None) == L.MOE_OK
