@@ -37,13 +37,15 @@ import mixture_experts_layer_40_amd as moe  # noqa: E402
 import synth  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0      # MI355X dense fp8
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 WORKLOAD = "v3_prefill_bf16"
 DECODE = "v3_decode_fp8"
 GROUPED = "v3_grouped_bf16"
+FP8B = "v3_prefill_fp8b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
-                  for f in ("ffn.hip", "common.hpp")]
+                  for f in ("ffn.hip", "gemm_core.hpp", "common.hpp")]
 
 
 def log(*a):
@@ -278,6 +280,81 @@ def grouped_measure(steps, warmup, plain_route_ms):
     return out
 
 
+def fp8_gate_up_bytes(spec) -> float:
+    """Algorithmic HBM bytes of one fine-grained fp8 gate/up launch: W1 and W3
+    codes of every routed and shared expert once with their 128 x 128 block
+    scales, the quantised x and its tile scales once, h and the shared h
+    written once as codes with their tile scales."""
+    TK, SI, d, I = spec.T * spec.K, spec.S * spec.Is, spec.d, spec.I
+    w = (spec.E * 2 * I + 2 * SI) * d * (1 + 4 / (128 * 128))
+    return float(w + spec.T * d * (1 + 4 / 128) + (TK * I + spec.T * SI) * (1 + 4 / 128))
+
+
+def fp8_measure(steps, warmup):
+    """The V3 prefill layer in fine-grained fp8 (128 x 128 weight blocks,
+    1 x 128 activation tiles; router and combine as in bf16): tokens/s, and
+    the gate/up launch against the HBM and fp8 MFMA rooflines."""
+    spec = synth.get_config(FP8B)
+    inp = synth.make_inputs(spec, "cuda")
+    layer = moe.MoELayer(spec, inp, max_tokens=spec.T)
+    x, bias = inp["x"], inp["bias"]
+    T, K, I, SI = spec.T, spec.K, spec.I, spec.S * spec.Is
+    cfg = layer._cfg(T)
+    hq = torch.empty((T * K, I), dtype=torch.uint8, device="cuda")
+    hs = torch.empty((T * K, I // 128), dtype=torch.float32, device="cuda")
+    hsq = torch.empty((T, SI), dtype=torch.uint8, device="cuda")
+    hss = torch.empty((T, SI // 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(moe.moe_workspace_size(cfg, moe.MOE_WS_GEMM), 256), dtype=torch.uint8,
+                     device="cuda")
+    w = layer.w
+
+    def step(timer=None):
+        layer.route(x, bias)
+        layer.permute(cfg, x, gather=False)
+        moe.moe_quantize_act(cfg, x, layer.xq[:T], layer.xs[:T])
+
+        def gate_up():
+            moe.moe_experts_fp8_gate_up(cfg, layer.xq[:T], layer.xs[:T], layer.expert_offsets,
+                                        layer.perm_slot[:T * K], w["w1"], w["s1"], w["s3"],
+                                        w["w1s"], w["s1s"], w["s3s"], hq, hs, hsq, hss, ws=ws)
+        if timer is not None:
+            with timer:
+                gate_up()
+        else:
+            gate_up()
+        moe.moe_experts_fp8_down(cfg, hq, hs, hsq, hss, layer.expert_offsets,
+                                 layer.perm_slot[:T * K], layer.topk_gate[:T], w["w2"], w["s2"],
+                                 w["w2s"], w["s2s"], layer.out_slots[:T * K], layer.y_shared[:T],
+                                 ws=ws)
+        layer.combine(cfg)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timed()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    gms = timer.mean_ms()
+    flops, nbytes = gate_up_flops(spec), fp8_gate_up_bytes(spec)
+    quant_ms = per_launch_ms(lambda: moe.moe_quantize_act(cfg, x, layer.xq[:T], layer.xs[:T]))
+    out = {"workload": FP8B, "tokens_per_s": T / sec, "ms_per_step": sec * 1e3,
+           "gate_up_ms": gms, "gate_up_algorithmic_bytes": nbytes,
+           "gate_up_GBs": nbytes / (gms * 1e-3) / 1e9,
+           "gate_up_hbm_frac": nbytes / (gms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "gate_up_TFLOPs": flops / (gms * 1e-3) / 1e12,
+           "gate_up_mfma_fp8_frac": flops / (gms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
+           "flop_per_byte": flops / nbytes, "quantize_act_ms": quant_ms,
+           "layer_TFLOPs": spec.flops() / sec / 1e12}
+    log(f"[bench] fp8 prefill: {sec*1e3:.3f} ms/step, {T/sec:.0f} tok/s, gate/up {gms:.3f} ms "
+        f"({out['gate_up_TFLOPs']:.0f} TFLOP/s, {out['gate_up_GBs']:.0f} GB/s algorithmic)")
+    del inp, layer, hq, hs, hsq, hss, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,6 +364,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-grouped", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before timing, run one 1 GiB read + 1 GiB write elementwise kernel, "
                          "the known-size reference for HBM byte counters")
@@ -368,6 +446,9 @@ def main():
     if not args.no_grouped:
         log(f"[bench] node-limited routing workload {GROUPED}")
         result["grouped"] = grouped_measure(args.steps, args.warmup, plain_route)
+    if not args.no_fp8:
+        log(f"[bench] fine-grained fp8 workload {FP8B}")
+        result["fp8_prefill"] = fp8_measure(args.steps, args.warmup)
     print(json.dumps(result), flush=True)
 
 
