@@ -44,6 +44,7 @@ DECODE = "v3_decode_fp8"
 GROUPED = "v3_grouped_bf16"
 FP8B = "v3_prefill_fp8b"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
+TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_fp8_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
                   for f in ("ffn.hip", "gemm_core.hpp", "common.hpp")]
 
@@ -60,13 +61,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(path=TRAFFIC_FILE):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
     if they were taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
@@ -347,6 +348,7 @@ def fp8_measure(steps, warmup):
            "gate_up_TFLOPs": flops / (gms * 1e-3) / 1e12,
            "gate_up_mfma_fp8_frac": flops / (gms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
            "flop_per_byte": flops / nbytes, "quantize_act_ms": quant_ms,
+           "gate_up_traffic": measured_traffic(TRAFFIC_FILE_FP8),
            "layer_TFLOPs": spec.flops() / sec / 1e12}
     log(f"[bench] fp8 prefill: {sec*1e3:.3f} ms/step, {T/sec:.0f} tok/s, gate/up {gms:.3f} ms "
         f"({out['gate_up_TFLOPs']:.0f} TFLOP/s, {out['gate_up_GBs']:.0f} GB/s algorithmic)")
