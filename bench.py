@@ -1,6 +1,7 @@
 """Throughput of the DeepSeekMoE layer forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-decode]
+                    [--no-grouped] [--no-fp8] [--no-stress]
 
 One step = one whole layer call on one batch already resident in HBM:
 router GEMM + sigmoid + biased top-K + gates + loads, the stable permutation,
@@ -12,10 +13,14 @@ score + bias selection) plus 1 shared expert, bf16, synthetic seeded inputs,
 expert weights relocated once into the tiled layout before timing.
 
 Printed: one JSON line with tokens/s, the roofline of the dominant kernel
-(the grouped gate/up GEMM, timed live with HIP events on its stream), the
-decode workload's fraction of HBM peak, the same prefill layer with
-node-limited routing (8 groups, top-4 groups), and the fp64 oracle timed on
-a bounded sample on the host's cores.
+(the grouped gate/up GEMM, timed live with HIP events on its stream, as a
+fraction of the nominal peaks and of measured ones: a streaming copy and the
+vendor BLAS bf16 GEMM), the fp64 oracle timed on a bounded
+sample on the host's cores with the GPU's error on those tokens, and the
+other workloads: the layer with the pre-MoE RMSNorm and residual, the decode
+layer's fraction of HBM peak, node-limited routing (8 groups, top-4), the
+fine-grained fp8 prefill layer, and the skewed-load stress run (20 batches
+with the bias update, max/mean load per batch).
 """
 
 from __future__ import annotations
@@ -43,6 +48,7 @@ WORKLOAD = "v3_prefill_bf16"
 DECODE = "v3_decode_fp8"
 GROUPED = "v3_grouped_bf16"
 FP8B = "v3_prefill_fp8b"
+STRESS = "zipf_stress_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_fp8_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
@@ -170,7 +176,7 @@ def time_steps(layer, x, bias, bufs, steps, warmup, gate_timer=None):
     return (time.perf_counter() - t0) / steps
 
 
-def cpu_baseline(spec, inp, layer, n_tokens):
+def cpu_baseline(spec, inp, layer, bufs, n_tokens):
     """The fp64 oracle on a bounded sample: route n_tokens tokens and compute
     their layer outputs, decoding each touched expert's stored weights."""
     import oracle
@@ -195,12 +201,29 @@ def cpu_baseline(spec, inp, layer, n_tokens):
     x64 = oracle.decode_stored(x)
     r = oracle.route(x64, oracle.decode_stored(wr), bias.astype(np.float64), spec.K, spec.score,
                      spec.norm)
-    oracle.layer_rows(x64, r["sel"], r["gate"], bank)
+    y_or = oracle.layer_rows(x64, r["sel"], r["gate"], bank)[0]
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_tokens} tokens of the {spec.name} batch (routing + shared + "
-                      f"{len(np.unique(r['sel']))} routed experts decoded to fp64), {dt:.1f} s"}
+    baseline = {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{n_tokens} tokens of the {spec.name} batch (routing + shared + "
+                          f"{len(np.unique(r['sel']))} routed experts decoded to fp64), {dt:.1f} s"}
+    # parity of the same tokens (outside the timed region): one plain layer
+    # step, then the GPU's y against the oracle's; a near-tie token (K-th and
+    # (K+1)-th keys within 1e-5) is evaluated on the GPU's selected set
+    layer_step(layer, inp["x"], inp["bias"], bufs)
+    torch.cuda.synchronize()
+    gidx = layer.topk_idx[trow].cpu().numpy().astype(np.int64)
+    near = r["near_tie"]
+    same = np.array([set(a) == set(b) for a, b in zip(gidx, r["sel"])])
+    if near.any():
+        g_near = oracle.gate_values(r["scores"][near], gidx[near], spec.norm)
+        y_or[near] = oracle.layer_rows(x64[near], gidx[near], g_near, bank)[0]
+    y_gpu = layer.y[trow].double().cpu().numpy()
+    rms = float(np.sqrt(np.mean(y_or ** 2)))
+    parity = {"tokens": n_tokens, "sets_equal_outside_near_ties": bool(np.all(same | near)),
+              "near_ties": int(near.sum()),
+              "max_abs_err_over_rms": float(np.abs(y_gpu - y_or).max() / rms), "tolerance": 2e-2}
+    return baseline, parity
 
 
 def decode_measure(steps, warmup):
@@ -357,6 +380,59 @@ def fp8_measure(steps, warmup):
     return out
 
 
+def measured_peaks():
+    """Achievable peaks on this GPU, beside the nominal ones: torch's streaming
+    copy (1 GiB read + 1 GiB written) and the vendor BLAS bf16 GEMM at
+    8192^3. (The decode leg's own weight streaming runs faster than this copy,
+    so the copy is a floor on what HBM delivers, not its ceiling.)"""
+    src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = per_launch_ms(lambda: dst.copy_(src), 10)
+    del src, dst
+    a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    b = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    c = torch.empty((8192, 8192), dtype=torch.bfloat16, device="cuda")
+    gemm_ms = per_launch_ms(lambda: torch.matmul(a, b, out=c), 10)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBs": 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
+            "blas_bf16_TFLOPs": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
+            "copy": "torch copy_ of 2^28 fp32", "blas": "torch.matmul bf16 8192 x 8192 x 8192"}
+
+
+def stress_measure():
+    """The skewed-load workload: 20 batches of 32768 tokens whose router rows
+    give expert popularity Zipf(1.1) (hottest about 10x the mean), each layer
+    call followed by the bias update from zero (gamma 1e-3): tokens/s over the
+    20 (forward + update) and each batch's max/mean load."""
+    spec = synth.get_config(STRESS)
+    inp = synth.make_inputs(spec, "cuda")
+    layer = moe.MoELayer(spec, inp, max_tokens=spec.T)
+    xs = [inp["x"]] + [synth.make_x(spec, "cuda", batch=b) for b in range(1, spec.batches)]
+    bias = torch.zeros(spec.E, dtype=torch.float32, device="cuda")
+    layer.forward(xs[0], bias)              # warm-up; the timed run starts from zero bias
+    torch.cuda.synchronize()
+    bias.zero_()
+    loads = []
+    t0 = time.perf_counter()
+    for x in xs:
+        layer.forward(x, bias)
+        loads.append(layer.load.clone())
+        layer.bias_update(bias)
+    torch.cuda.synchronize()
+    sec = time.perf_counter() - t0
+    ratio = [float(l.max() / l.float().mean()) for l in (t.cpu() for t in loads)]
+    upd_ms = per_launch_ms(lambda: moe.moe_bias_update(spec.E, layer.load, 0.0, bias), 20)
+    out = {"workload": STRESS, "batches": spec.batches, "tokens_per_batch": spec.T,
+           "tokens_per_s": spec.batches * spec.T / sec, "ms_per_batch": sec * 1e3 / spec.batches,
+           "max_over_mean_load": ratio, "max_violation_first_last": [ratio[0] - 1, ratio[-1] - 1],
+           "bias_update_ms": upd_ms}
+    log(f"[bench] stress: {out['ms_per_batch']:.2f} ms/batch, max/mean {ratio[0]:.2f} -> {ratio[-1]:.2f}")
+    del inp, layer, xs, bias
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +443,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-stress", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before timing, run one 1 GiB read + 1 GiB write elementwise kernel, "
                          "the known-size reference for HBM byte counters")
@@ -439,7 +516,8 @@ def main():
                                                     args.warmup)
     if not args.no_cpu_baseline:
         log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
-        result["cpu_baseline"] = cpu_baseline(spec, inp, layer, args.cpu_tokens)
+        result["cpu_baseline"], result["parity_sample"] = cpu_baseline(spec, inp, layer, bufs,
+                                                                       args.cpu_tokens)
     del inp, layer, bufs
     torch.cuda.empty_cache()
     if not args.no_decode:
@@ -451,6 +529,14 @@ def main():
     if not args.no_fp8:
         log(f"[bench] fine-grained fp8 workload {FP8B}")
         result["fp8_prefill"] = fp8_measure(args.steps, args.warmup)
+    if not args.no_stress:
+        log(f"[bench] skewed-load workload {STRESS}")
+        result["stress"] = stress_measure()
+    peaks = measured_peaks()
+    result["measured_peaks"] = peaks
+    rl = result["roofline"]
+    rl["frac_of_measured_copy"] = rl["achieved"] / peaks["copy_GBs"]
+    rl["mfma_frac_of_measured_blas"] = rl["mfma_TFLOPs"] / peaks["blas_bf16_TFLOPs"]
     print(json.dumps(result), flush=True)
 
 
