@@ -19,8 +19,9 @@ vendor BLAS bf16 GEMM), the fp64 oracle timed on a bounded
 sample on the host's cores with the GPU's error on those tokens, and the
 other workloads: the layer with the pre-MoE RMSNorm and residual, the decode
 layer's fraction of HBM peak, node-limited routing (8 groups, top-4), the
-fine-grained fp8 prefill layer, and the skewed-load stress run (20 batches
-with the bias update, max/mean load per batch).
+fine-grained fp8 prefill layer, the skewed-load stress run (20 batches
+with the bias update, max/mean load per batch), and the tiny fp32 and
+2024-layout workloads (tokens/s and TFLOP/s against their peaks).
 """
 
 from __future__ import annotations
@@ -433,6 +434,33 @@ def stress_measure():
     return out
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3    # MI355X fp32 vector
+
+
+def forward_measure(name, steps, warmup):
+    """A named workload through MoELayer.forward (its default path), timed
+    over `steps` layer calls: tokens/s and layer TFLOP/s against the peak of
+    its arithmetic (bf16 MFMA, or fp32 vector for the fp32 layer)."""
+    spec = synth.get_config(name)
+    inp = synth.make_inputs(spec, "cuda")
+    layer = moe.MoELayer(spec, inp, max_tokens=spec.T)
+    x, bias = inp["x"], inp["bias"]
+    for _ in range(warmup):
+        layer.forward(x, bias)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.forward(x, bias)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps
+    tf = spec.flops() / sec / 1e12
+    peak = FP32_VECTOR_PEAK_TFLOPS if spec.act_dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+    del inp, layer
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens": spec.T, "tokens_per_s": spec.T / sec,
+            "ms_per_step": sec * 1e3, "layer_TFLOPs": tf, "peak_TFLOPs": peak, "frac": tf / peak}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -532,6 +560,9 @@ def main():
     if not args.no_stress:
         log(f"[bench] skewed-load workload {STRESS}")
         result["stress"] = stress_measure()
+    log("[bench] the tiny fp32 and the 2024-layout workloads")
+    result["other_configs"] = [forward_measure(n, args.steps, args.warmup)
+                               for n in ("tiny_f32", "dsmoe2024_bf16")]
     peaks = measured_peaks()
     result["measured_peaks"] = peaks
     rl = result["roofline"]
