@@ -2,11 +2,11 @@
 //
 // Conventions used throughout:
 //  * Waves are 64 lanes; blocks are 256 threads (4 waves) unless noted.
-//  * MFMA tiles use v_mfma_f32_16x16x32_bf16. For one instruction, lane l
-//    supplies 8 consecutive K-elements of row (l % 16) of the first operand
-//    and of column (l % 16) of the second; lane group g = l / 16 owns
-//    K-elements 8g .. 8g+7; the 16x16 fp32 result leaves rows 4g .. 4g+3 of
-//    column (l % 16) in lane l.
+//  * MFMA: the expert GEMMs and the fused router use
+//    v_mfma_f32_32x32x16_bf16 (mfma_32x32x16 below), the fine-grained fp8
+//    GEMMs v_mfma_scale_f32_32x32x64_f8f6f4 (mfma_32x32x64_fp8), the split-K
+//    router logits v_mfma_f32_16x16x32_bf16 (mfma_16x16x32); each wrapper
+//    states its lane layout.
 //  * GEMMs are written in the "weights as rows" orientation: the first MFMA
 //    operand is a block of weight rows (output features), the second a block
 //    of token rows, so one lane ends up holding 4 consecutive output features
@@ -41,6 +41,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// v_mfma_f32_16x16x32_bf16: lane l supplies 8 consecutive K-elements of row
+// (l % 16) of the first operand and of column (l % 16) of the second (lane
+// group g = l / 16 owns K-elements 8g .. 8g+7); the 16x16 fp32 result
+// leaves rows 4g .. 4g+3 of column (l % 16) in lane l.
 __device__ __forceinline__ f32x4 mfma_16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
