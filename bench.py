@@ -455,10 +455,16 @@ def forward_measure(name, steps, warmup):
     sec = (time.perf_counter() - t0) / steps
     tf = spec.flops() / sec / 1e12
     peak = FP32_VECTOR_PEAK_TFLOPS if spec.act_dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
-    del inp, layer
+    # the same call recorded once into a HIP graph and replayed (no host
+    # launch work per call)
+    xg = x.clone()
+    graph = layer.capture(xg, bias)
+    gsec = per_launch_ms(graph.replay, steps) * 1e-3
+    del inp, layer, graph, xg
     torch.cuda.empty_cache()
     return {"workload": name, "tokens": spec.T, "tokens_per_s": spec.T / sec,
-            "ms_per_step": sec * 1e3, "layer_TFLOPs": tf, "peak_TFLOPs": peak, "frac": tf / peak}
+            "ms_per_step": sec * 1e3, "layer_TFLOPs": tf, "peak_TFLOPs": peak, "frac": tf / peak,
+            "graph_ms_per_step": gsec * 1e3, "graph_tokens_per_s": spec.T / gsec}
 
 
 def main():

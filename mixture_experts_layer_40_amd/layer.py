@@ -17,7 +17,8 @@ forward() enqueues, on the current stream,
         -> join -> moe_combine
 
 and returns y (plus the routing results it kept). The per-batch bias step is
-`bias_update()`. Nothing here computes: every step is a libmoe kernel.
+`bias_update()`; `capture()` records a call into a HIP graph for replay.
+Nothing here computes: every step is a libmoe kernel.
 """
 
 from __future__ import annotations
@@ -179,6 +180,24 @@ class MoELayer:
             cur.wait_stream(self.side)
         self.combine(cfg, res)
         return self.y[:cfg.num_tokens]
+
+    def capture(self, x, bias=None):
+        """Record one forward(x, bias) into a HIP graph and return it
+        (torch.cuda.CUDAGraph): a launch-bound caller -- few tokens, the fp32
+        layer -- then reruns the whole call sequence with graph.replay(). x,
+        bias and the layer's outputs keep their addresses, so new inputs are
+        written into x before a replay. Every node is a libmoe kernel (no
+        memset nodes), so each replay recomputes everything."""
+        cur = torch.cuda.current_stream(self.device)
+        warm = torch.cuda.Stream(device=self.device)
+        warm.wait_stream(cur)
+        with torch.cuda.stream(warm):
+            self.forward(x, bias)
+        cur.wait_stream(warm)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, bias)
+        return graph
 
     def bias_update(self, bias, gamma=None):
         L.moe_bias_update(self.spec.E, self.load, self.spec.gamma if gamma is None else gamma, bias)
