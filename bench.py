@@ -494,7 +494,7 @@ def main():
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
+        torch.neg(src, out=dst)      # a kernel no other step launches, so counters can select it
         torch.cuda.synchronize()
         del src, dst
         log("[bench] calibration copy: 1 GiB read, 1 GiB written")
