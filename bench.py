@@ -12,16 +12,21 @@ T = 8192 tokens, d = 7168, 256 routed experts of intermediate 2048 (top-8,
 score + bias selection) plus 1 shared expert, bf16, synthetic seeded inputs,
 expert weights relocated once into the tiled layout before timing.
 
-Printed: one JSON line with tokens/s, the roofline of the dominant kernel
-(the grouped gate/up GEMM, timed live with HIP events on its stream, as a
-fraction of the nominal peaks and of measured ones: a streaming copy and the
-vendor BLAS bf16 GEMM), the fp64 oracle timed on a bounded
+Printed: one JSON line with tokens/s (mean over the timed region, and the
+median and minimum of per-step event timings), the roofline of the dominant
+kernel (the grouped gate/up GEMM, timed live with HIP events on its stream,
+as a fraction of the nominal peaks and of measured ones), the fp64 oracle
+timed on a bounded
 sample on the host's cores with the GPU's error on those tokens, and the
 other workloads: the layer with the pre-MoE RMSNorm and residual, the decode
 layer's fraction of HBM peak, node-limited routing (8 groups, top-4), the
 fine-grained fp8 prefill layer, the skewed-load stress run (20 batches
 with the bias update, max/mean load per batch), and the tiny fp32 and
 2024-layout workloads (tokens/s and TFLOP/s against their peaks).
+Measured peaks come from the probes of libmoe_peaks.so (a loop of
+independent MFMAs per instruction form, an fp32 FMA loop, a streaming read
+and copy; plus torch's copy and the vendor BLAS GEMM for reference), and
+every rate in the line is also given as a fraction of them.
 """
 
 from __future__ import annotations
@@ -40,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import mixture_experts_layer_40_amd as moe  # noqa: E402
+from mixture_experts_layer_40_amd import peaks as pk  # noqa: E402
 import synth  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16
@@ -166,15 +172,31 @@ def setup(spec):
     return inp, layer, (h, hs, ws_gemm)
 
 
-def time_steps(layer, x, bias, bufs, steps, warmup, gate_timer=None):
+def time_steps(layer, x, bias, bufs, steps, warmup, gate_timer=None, step_ms=None):
+    """Seconds per step over `steps` timed steps (host clock around the whole
+    timed region, bracketed by synchronisations). With a list `step_ms`, an
+    event pair on the stream also brackets each step and its duration is
+    appended (for the median and minimum)."""
     for _ in range(warmup):
         layer_step(layer, x, bias, bufs)
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if step_ms is not None else None
     t0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps):
+        if ev:
+            ev[i].record()
         layer_step(layer, x, bias, bufs, gate_timer)
+    if ev:
+        ev[steps].record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    sec = (time.perf_counter() - t0) / steps
+    if ev:
+        step_ms.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return sec
+
+
+def spread(step_ms):
+    return {"ms_per_step_median": float(np.median(step_ms)), "ms_per_step_min": float(np.min(step_ms))}
 
 
 def cpu_baseline(spec, inp, layer, bufs, n_tokens):
@@ -231,7 +253,8 @@ def decode_measure(steps, warmup):
     spec = synth.get_config(DECODE)
     inp, layer, bufs = setup(spec)
     x, bias = inp["x"], inp["bias"]
-    sec = time_steps(layer, x, bias, bufs, steps, warmup)
+    step_ms = []
+    sec = time_steps(layer, x, bias, bufs, steps, warmup, step_ms=step_ms)
     load = layer.load.cpu().numpy()
     n_active = int((load > 0).sum())
     bytes_ = ((n_active * spec.weight_bytes_per_expert() + spec.shared_weight_bytes())
@@ -240,7 +263,7 @@ def decode_measure(steps, warmup):
     gbs = bytes_ / sec / 1e9
     out = {"workload": DECODE, "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
            "active_experts": n_active, "algorithmic_bytes": int(bytes_), "achieved_GBs": gbs,
-           "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}
+           "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, **spread(step_ms)}
     del inp, layer, bufs
     torch.cuda.empty_cache()
     return out
@@ -299,6 +322,8 @@ def grouped_measure(steps, warmup, plain_route_ms):
     sec = time_steps(layer, x, bias, bufs, steps, warmup)
     out = {"workload": GROUPED, "groups": spec.n_groups, "topk_groups": spec.topk_groups,
            "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
+           "layer_TFLOPs": spec.flops() / sec / 1e12,
+           "layer_frac_mfma_peak": spec.flops() / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS,
            "route_ms": route_ms(layer, x, bias), "route_ms_without_groups": plain_route_ms}
     del inp, layer, bufs
     torch.cuda.empty_cache()
@@ -373,7 +398,8 @@ def fp8_measure(steps, warmup):
            "gate_up_mfma_fp8_frac": flops / (gms * 1e-3) / 1e12 / MFMA_FP8_PEAK_TFLOPS,
            "flop_per_byte": flops / nbytes, "quantize_act_ms": quant_ms,
            "gate_up_traffic": measured_traffic(TRAFFIC_FILE_FP8),
-           "layer_TFLOPs": spec.flops() / sec / 1e12}
+           "layer_TFLOPs": spec.flops() / sec / 1e12,
+           "layer_frac_mfma_fp8_peak": spec.flops() / sec / 1e12 / MFMA_FP8_PEAK_TFLOPS}
     log(f"[bench] fp8 prefill: {sec*1e3:.3f} ms/step, {T/sec:.0f} tok/s, gate/up {gms:.3f} ms "
         f"({out['gate_up_TFLOPs']:.0f} TFLOP/s, {out['gate_up_GBs']:.0f} GB/s algorithmic)")
     del inp, layer, hq, hs, hsq, hss, ws
@@ -382,10 +408,17 @@ def fp8_measure(steps, warmup):
 
 
 def measured_peaks():
-    """Achievable peaks on this GPU, beside the nominal ones: torch's streaming
-    copy (1 GiB read + 1 GiB written) and the vendor BLAS bf16 GEMM at
-    8192^3. (The decode leg's own weight streaming runs faster than this copy,
-    so the copy is a floor on what HBM delivers, not its ceiling.)"""
+    """Achievable peaks on this GPU, beside the nominal ones. From the probes
+    of libmoe_peaks.so: a loop of independent MFMAs of each instruction form
+    (8 waves per block, 1024 blocks, operands changing from one instruction
+    to the next), an fp32 FMA loop, and a 16-byte-load streaming read and
+    copy of 2 GiB. For reference also torch's copy of 1 GiB and the vendor
+    BLAS bf16 GEMM at 8192^3."""
+    loops = {form: pk.measure_mfma(form, blocks=1024, iters=iters)
+             for form, iters in (("bf16_32x32x16", 4096), ("bf16_16x16x32", 4096),
+                                 ("fp8_32x32x64", 2048), ("fp8_16x16x128", 2048),
+                                 ("f32_fma", 16384))}
+    stream = pk.measure_stream(1 << 31, reps=10)
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     copy_ms = per_launch_ms(lambda: dst.copy_(src), 10)
@@ -396,9 +429,44 @@ def measured_peaks():
     gemm_ms = per_launch_ms(lambda: torch.matmul(a, b, out=c), 10)
     del a, b, c
     torch.cuda.empty_cache()
-    return {"copy_GBs": 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
+    return {"mfma_loop_TFLOPs": loops,
+            "mfma_bf16_TFLOPs": max(loops["bf16_32x32x16"], loops["bf16_16x16x32"]),
+            "mfma_fp8_TFLOPs": max(loops["fp8_32x32x64"], loops["fp8_16x16x128"]),
+            "fma_f32_TFLOPs": loops["f32_fma"],
+            "stream_read_GBs": stream["read_GBs"], "stream_copy_GBs": stream["copy_GBs"],
+            "copy_GBs": 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
             "blas_bf16_TFLOPs": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
             "copy": "torch copy_ of 2^28 fp32", "blas": "torch.matmul bf16 8192 x 8192 x 8192"}
+
+
+def attach_measured_fractions(result, peaks):
+    """Every rate of the run as a fraction of the measured peak of the same
+    resource (best MFMA loop of its dtype, fp32 FMA loop, streaming read),
+    beside the fractions of the published peaks already in the line."""
+    bf16, fp8, f32 = peaks["mfma_bf16_TFLOPs"], peaks["mfma_fp8_TFLOPs"], peaks["fma_f32_TFLOPs"]
+    rd = peaks["stream_read_GBs"]
+    result["layer_frac_measured_mfma"] = result["layer_TFLOPs"] / bf16
+    rl = result["roofline"]
+    rl["frac_of_measured_read"] = rl["achieved"] / rd
+    rl["frac_of_measured_copy"] = rl["achieved"] / peaks["copy_GBs"]
+    rl["mfma_frac_of_measured_loop"] = rl["mfma_TFLOPs"] / bf16
+    rl["mfma_frac_of_own_form_loop"] = rl["mfma_TFLOPs"] / peaks["mfma_loop_TFLOPs"]["bf16_32x32x16"]
+    rl["mfma_frac_of_measured_blas"] = rl["mfma_TFLOPs"] / peaks["blas_bf16_TFLOPs"]
+    if "decode" in result:
+        result["decode"]["frac_of_measured_read"] = result["decode"]["achieved_GBs"] / rd
+    if "fp8_prefill" in result:
+        f = result["fp8_prefill"]
+        f["gate_up_frac_of_measured_read"] = f["gate_up_GBs"] / rd
+        f["gate_up_frac_of_measured_fp8_loop"] = f["gate_up_TFLOPs"] / fp8
+        f["layer_frac_measured_fp8_mfma"] = f["layer_TFLOPs"] / fp8
+    if "grouped" in result:
+        g = result["grouped"]
+        g["layer_frac_measured_mfma"] = g["layer_TFLOPs"] / bf16
+    if "stress" in result:
+        result["stress"]["frac_of_measured"] = result["stress"]["layer_TFLOPs"] / bf16
+    for o in result.get("other_configs", []):
+        o["frac_of_measured"] = o["layer_TFLOPs"] / (f32 if o["peak_TFLOPs"] == FP32_VECTOR_PEAK_TFLOPS
+                                                     else bf16)
 
 
 def stress_measure():
@@ -424,8 +492,11 @@ def stress_measure():
     sec = time.perf_counter() - t0
     ratio = [float(l.max() / l.float().mean()) for l in (t.cpu() for t in loads)]
     upd_ms = per_launch_ms(lambda: moe.moe_bias_update(spec.E, layer.load, 0.0, bias), 20)
+    tf = spec.batches * spec.flops() / sec / 1e12
     out = {"workload": STRESS, "batches": spec.batches, "tokens_per_batch": spec.T,
            "tokens_per_s": spec.batches * spec.T / sec, "ms_per_batch": sec * 1e3 / spec.batches,
+           "layer_TFLOPs": tf, "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+           "frac": tf / MFMA_BF16_PEAK_TFLOPS,
            "max_over_mean_load": ratio, "max_violation_first_last": [ratio[0] - 1, ratio[-1] - 1],
            "bias_update_ms": upd_ms}
     log(f"[bench] stress: {out['ms_per_batch']:.2f} ms/batch, max/mean {ratio[0]:.2f} -> {ratio[-1]:.2f}")
@@ -504,7 +575,8 @@ def main():
     x, bias = inp["x"], inp["bias"]
     gate_timer = Timed()
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
-    sec = time_steps(layer, x, bias, bufs, args.steps, args.warmup, gate_timer)
+    step_ms = []
+    sec = time_steps(layer, x, bias, bufs, args.steps, args.warmup, gate_timer, step_ms)
     tokens_per_s = spec.T / sec
     gate_ms = gate_timer.mean_ms()
     gate_flops = gate_up_flops(spec)
@@ -525,6 +597,7 @@ def main():
                    "top_k": spec.K, "inter": spec.I, "shared_experts": spec.S,
                    "shared_inter": spec.Is, "weights": "bf16", "output": "fp32",
                    "parallelism": "single GPU"},
+        **spread(step_ms),
         "layer_TFLOPs": layer_tflops,
         "layer_frac_mfma_peak": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
         "load_max_over_mean": float(load.max() / load.mean()),
@@ -569,11 +642,10 @@ def main():
     log("[bench] the tiny fp32 and the 2024-layout workloads")
     result["other_configs"] = [forward_measure(n, args.steps, args.warmup)
                                for n in ("tiny_f32", "dsmoe2024_bf16")]
+    log("[bench] measured peaks (MFMA / FMA loops, streaming read and copy)")
     peaks = measured_peaks()
     result["measured_peaks"] = peaks
-    rl = result["roofline"]
-    rl["frac_of_measured_copy"] = rl["achieved"] / peaks["copy_GBs"]
-    rl["mfma_frac_of_measured_blas"] = rl["mfma_TFLOPs"] / peaks["blas_bf16_TFLOPs"]
+    attach_measured_fractions(result, peaks)
     print(json.dumps(result), flush=True)
 
 

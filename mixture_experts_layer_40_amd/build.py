@@ -1,10 +1,11 @@
-"""Build libmoe.so (all HIP sources, gfx950) in-tree next to this file.
+"""Build libmoe.so (all HIP sources, gfx950) in-tree next to this file, and
+libmoe_peaks.so (the achievable-peak probes of include/moe_peaks.h).
 
     python -m mixture_experts_layer_40_amd.build [--verbose]
 
-The library is plain hipcc output: one shared object exporting the C ABI of
-include/libmoe.h. Packed-fp32 instruction selection is disabled for device
-code (-packed-fp32-ops); hipcc's host pass warns that it does not know the
+Each library is plain hipcc output: one shared object exporting a C ABI.
+Packed-fp32 instruction selection is disabled for device code
+(-packed-fp32-ops); hipcc's host pass warns that it does not know the
 feature, which is harmless.
 """
 
@@ -22,6 +23,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmoe.so")
+PEAKS_DIR = os.path.join(PKG_DIR, "probes")
+PEAKS_LIB_PATH = os.path.join(PKG_DIR, "libmoe_peaks.so")
 ARCH = "gfx950"
 
 
@@ -36,23 +39,32 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB_PATH + ".tmp"
+def _compile(srcs, path, verbose, extra_flags):
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-function",
-           f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + sources() + list(extra_flags or [])
+           f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + srcs + list(extra_flags or [])
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "is not a recognized feature for this target" not in l)
     if res.returncode != 0:
-        raise RuntimeError("libmoe build failed:\n" + out)
+        raise RuntimeError(f"{os.path.basename(path)} build failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
+    return path
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    return _compile(sources(), LIB_PATH, verbose, extra_flags)
+
+
+def build_peaks(verbose: bool = False, extra_flags=None) -> str:
+    return _compile(sorted(glob.glob(os.path.join(PEAKS_DIR, "*.hip"))), PEAKS_LIB_PATH, verbose,
+                    extra_flags)
 
 
 def main(argv=None):
@@ -62,8 +74,8 @@ def main(argv=None):
                     help="print per-kernel register/LDS usage from the compiler")
     args = ap.parse_args(argv)
     extra = ["-Rpass-analysis=kernel-resource-usage"] if args.resource_usage else []
-    path = build(verbose=args.verbose or args.resource_usage, extra_flags=extra)
-    print(path)
+    for fn in (build, build_peaks):
+        print(fn(verbose=args.verbose or args.resource_usage, extra_flags=extra))
 
 
 if __name__ == "__main__":
