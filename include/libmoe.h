@@ -103,7 +103,9 @@ extern "C" {
  * with num_tokens * top_k < 2^30; 1 <= num_experts <=
  * 256; 1 <= top_k <= num_experts; hidden and inter are positive multiples
  * of 64; num_shared >= 0 and, when positive, num_shared * shared_inter is a
- * positive multiple of 64 (num_shared == 0 means no shared expert). */
+ * positive multiple of 64 (num_shared == 0 means no shared expert). A shape
+ * whose grouped expert GEMMs would need more than 2^30 tiles in one launch
+ * (tokens x hidden far beyond any one-GPU layer) gives MOE_ERR_UNSUPPORTED. */
 typedef struct moe_config {
   int32_t num_tokens;    /* T: tokens in the batch                               */
   int32_t hidden;        /* d: hidden size                                       */

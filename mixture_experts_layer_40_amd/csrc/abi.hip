@@ -95,6 +95,8 @@ int moe_validate(const moe_config* c) {
   }
   const int64_t tk = static_cast<int64_t>(c->num_tokens) * c->top_k;
   if (tk >= (1LL << 30)) return MOE_ERR_SHAPE;
+  // grouped GEMM tiles are indexed in int and launched as one grid
+  if (grouped_tiles_bound(*c) > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if (c->num_groups < 0) return MOE_ERR_SHAPE;
   if (c->num_groups > 1) {
     const int G = c->num_groups, M = c->topk_groups;

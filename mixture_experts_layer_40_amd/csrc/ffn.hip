@@ -725,6 +725,31 @@ GemmSet f8b_down(const moe_config& c, const Blocking& b, const void* hq, const f
 
 }  // namespace
 
+// The largest tile count (= grid, up to a multiple of 8) of any grouped
+// GEMM launch this configuration can make; tiles are indexed in int.
+int64_t grouped_tiles_bound(const moe_config& c) {
+  const int E = c.num_experts, T = c.num_tokens;
+  const int64_t SI = static_cast<int64_t>(c.num_shared) * c.shared_inter;
+  const int64_t TK = static_cast<int64_t>(T) * c.top_k;
+  if (TK == 0) return 0;
+  int64_t m = 0;
+  for (int f8 = 0; f8 < 2; ++f8) {
+    if (f8 && !(is_fp8(c) && SI <= 8192 && c.hidden % 128 == 0 && c.inter % 128 == 0)) continue;
+    const Blocking b = f8 ? blocking_f8b(c, c.inter, (TK + E - 1) / E) : blocking(c, c.inter, (TK + E - 1) / E);
+    const Blocking bs = f8 ? blocking_f8b(c, static_cast<int>(SI), T)
+                           : blocking(c, static_cast<int>(std::min<int64_t>(SI, 1 << 30)), T);
+    const int64_t mt = (T + b.bm - 1) / b.bm;
+    const int64_t mts = (T + bs.bm - 1) / bs.bm;
+    for (int down = 0; down < 2; ++down) {
+      const int64_t nb = down ? b.nb2 : b.nb1, nbs = down ? bs.nb2 : bs.nb1;
+      int64_t tiles = (TK / b.bm + E + 1) * nb;                 // routed bound (as routed_max_tiles)
+      if (c.num_shared > 0) tiles += std::max(mt * nbs, mts * nbs);
+      m = std::max(m, grid_for(tiles));
+    }
+  }
+  return m;
+}
+
 size_t sched_ws_bytes(const moe_config& c) { return align_up(static_cast<size_t>(c.num_experts + 1) * 4, 256); }
 
 size_t h_bytes(const moe_config& c) {

@@ -30,6 +30,8 @@ hipError_t launch_permute(const moe_config& c, const int32_t* topk_idx, const vo
 // ---- expert FFN (routed and shared) ------------------------------------------
 size_t ffn_ws_bytes(const moe_config& c);
 size_t sched_ws_bytes(const moe_config& c);
+// Largest grid (tile count) of any grouped GEMM launch of this configuration.
+int64_t grouped_tiles_bound(const moe_config& c);
 size_t shared_ws_bytes(const moe_config& c);
 hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t* expert_offsets,
                           const void* w1, const void* w3, const float* s1, const float* s3,

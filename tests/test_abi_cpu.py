@@ -43,6 +43,13 @@ def test_validate_accepts_named_workload_shapes():
         assert moe.moe_validate(moe.config_of(spec)) == moe.MOE_OK, name
 
 
+def test_validate_accepts_large_token_counts():
+    # a million tokens at the V3 shape stays well inside the one-grid tile bound
+    big = _cfg(act_dtype="bf16", weight_dtype="bf16", T=1 << 20, K=8, E=256, d=7168, I=2048,
+               S=1, Is=2048)
+    assert moe.moe_validate(big) == moe.MOE_OK
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(K=17), L.MOE_ERR_SHAPE),              # K > E
     (dict(K=0), L.MOE_ERR_SHAPE),
@@ -70,6 +77,10 @@ def test_validate_accepts_named_workload_shapes():
     (dict(E=256, K=8, n_groups=128, topk_groups=8), L.MOE_ERR_SHAPE),   # more than 64 groups
     (dict(n_groups=-1), L.MOE_ERR_SHAPE),
     (dict(weight_layout="tiled"), L.MOE_ERR_DTYPE),   # fp32 weights have no tiled form
+    # fp32 path: (2^24 token tiles of 32 + E) x 256 column blocks > 2^30 tiles in one grid
+    (dict(T=1 << 26, K=8, E=16, d=8192), L.MOE_ERR_UNSUPPORTED),
+    # bf16: a hidden size so large that the down launch alone needs > 2^30 tiles
+    (dict(act_dtype="bf16", weight_dtype="bf16", T=1 << 20, K=8, d=1 << 24), L.MOE_ERR_UNSUPPORTED),
 ])
 def test_validate_rejects(kw, status):
     assert moe.moe_validate(_cfg(**kw)) == status
