@@ -422,12 +422,15 @@ def measured_peaks():
     (8 waves per block, 1024 blocks, operands changing from one instruction
     to the next), an fp32 FMA loop, and a 16-byte-load streaming read and
     copy of 2 GiB. For reference also torch's copy of 1 GiB and the vendor
-    BLAS bf16 GEMM at 8192^3."""
+    BLAS bf16 GEMM at 8192^3. Also the L2 -> CU read rate (each CU
+    re-reading 64 KB), against which the GEMMs' L2 -> CU operand traffic
+    can be set."""
     loops = {form: pk.measure_mfma(form, blocks=1024, iters=iters)
              for form, iters in (("bf16_32x32x16", 4096), ("bf16_16x16x32", 4096),
                                  ("fp8_32x32x64", 2048), ("fp8_16x16x128", 2048),
                                  ("f32_fma", 16384))}
     stream = pk.measure_stream(1 << 31, reps=10)
+    l2 = pk.measure_l2()
     src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     copy_ms = per_launch_ms(lambda: dst.copy_(src), 10)
@@ -443,6 +446,7 @@ def measured_peaks():
             "mfma_fp8_TFLOPs": max(loops["fp8_32x32x64"], loops["fp8_16x16x128"]),
             "fma_f32_TFLOPs": loops["f32_fma"],
             "stream_read_GBs": stream["read_GBs"], "stream_copy_GBs": stream["copy_GBs"],
+            "l2_read_GBs": l2,
             "copy_GBs": 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
             "blas_bf16_TFLOPs": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
             "copy": "torch copy_ of 2^28 fp32", "blas": "torch.matmul bf16 8192 x 8192 x 8192"}

@@ -55,6 +55,17 @@ double moe_peak_mfma_flops(int kind, int32_t blocks, int32_t iters);
 int moe_peak_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out,
                          void* stream);
 
+/* L2 -> CU read rate: block b re-reads its own region_bytes of src
+ * (src + b * region_bytes; region_bytes a positive multiple of 64 KB, src
+ * 16-byte aligned, blocks * region_bytes bytes readable) `iters` times with
+ * 16-byte loads, 512 threads per block, eight loads in flight per thread.
+ * A region larger than a CU's 32 KB L1 whose blocks' regions, summed per XCD
+ * (blocks are dealt to the 8 XCDs in turn), fit its 4 MB L2 measures the L2
+ * hit rate; thread i writes the XOR of the words it read to out[i] (out has
+ * blocks * 512 entries). Bytes read = blocks * region_bytes * iters. */
+int moe_peak_l2_read(const void* src, size_t region_bytes, int32_t blocks, int32_t iters,
+                     uint32_t* out, void* stream);
+
 /* dst[0 .. bytes) = src[0 .. bytes) with 16-byte loads and stores
  * (bytes % 16 == 0, both 16-byte aligned, no overlap), in the chunks of
  * moe_peak_stream_read. */

@@ -31,7 +31,7 @@ FORMS = {
     "f32_fma": MOE_PEAK_FMA_F32,
 }
 EXPORTED = ("moe_peak_mfma", "moe_peak_mfma_flops", "moe_peak_stream_read",
-            "moe_peak_stream_copy")
+            "moe_peak_l2_read", "moe_peak_stream_copy")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -54,6 +54,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_peak_mfma_flops.restype = ctypes.c_double
     lib.moe_peak_stream_read.argtypes = [P, SZ, I32, P, P]
     lib.moe_peak_stream_read.restype = ctypes.c_int
+    lib.moe_peak_l2_read.argtypes = [P, SZ, I32, I32, P, P]
+    lib.moe_peak_l2_read.restype = ctypes.c_int
     lib.moe_peak_stream_copy.argtypes = [P, P, SZ, I32, P]
     lib.moe_peak_stream_copy.restype = ctypes.c_int
     _lib = lib
@@ -81,6 +83,12 @@ def moe_peak_mfma_flops(kind: int, blocks: int, iters: int) -> float:
 def moe_peak_stream_read(src: torch.Tensor, nbytes: int, blocks: int, out: torch.Tensor):
     _check("moe_peak_stream_read", load_library().moe_peak_stream_read(
         src.data_ptr(), nbytes, blocks, out.data_ptr(), _stream()))
+
+
+def moe_peak_l2_read(src: torch.Tensor, region_bytes: int, blocks: int, iters: int,
+                     out: torch.Tensor):
+    _check("moe_peak_l2_read", load_library().moe_peak_l2_read(
+        src.data_ptr(), region_bytes, blocks, iters, out.data_ptr(), _stream()))
 
 
 def moe_peak_stream_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks: int):
@@ -127,3 +135,15 @@ def measure_stream(nbytes: int = 1 << 31, read_blocks: int = 4096,
     del src, dst, out
     return {"read_GBs": nbytes / (read_ms * 1e-3) / 1e9,
             "copy_GBs": 2.0 * nbytes / (copy_ms * 1e-3) / 1e9}
+
+
+def measure_l2(region_bytes: int = 65536, blocks: int = 256, iters: int = 400,
+               reps: int = 5) -> float:
+    """GB/s of L2 hits into the CUs: each of `blocks` blocks (one per CU by
+    default) re-reads its own 64 KB (over the 32 KB L1; 2 MB per XCD, under
+    its 4 MB L2)."""
+    src = torch.ones(region_bytes * blocks // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
+    ms = _time_ms(lambda: moe_peak_l2_read(src, region_bytes, blocks, iters, out), reps)
+    del src, out
+    return region_bytes * blocks * iters / (ms * 1e-3) / 1e9

@@ -185,6 +185,25 @@ __global__ __launch_bounds__(kStreamThreads) void stream_copy(const u32x4* __res
   }
 }
 
+// L2 probe: block b sweeps its region (region16 words, a multiple of
+// 8 * 512) `iters` times, 512 threads, eight 16-byte loads per thread per step.
+__global__ __launch_bounds__(kLoopThreads) void l2_read(const u32x4* __restrict__ src,
+                                                       size_t region16, int iters,
+                                                       uint32_t* __restrict__ out) {
+  const u32x4* base = src + static_cast<size_t>(blockIdx.x) * region16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int it = 0; it < iters; ++it) {
+    for (size_t i = threadIdx.x; i < region16; i += kUnroll * kLoopThreads) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = base[i + u * kLoopThreads];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
+  }
+  out[static_cast<size_t>(blockIdx.x) * kLoopThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 template <int KIND>
 double flops_of(int32_t blocks, int32_t iters) {
   return static_cast<double>(blocks) * (kLoopThreads / kWave) * iters * Form<KIND>::per_iter *
@@ -235,6 +254,17 @@ int moe_peak_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t
   hipLaunchKernelGGL(stream_read, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                      bytes / 16, out);
+  return status_of(hipGetLastError());
+}
+
+int moe_peak_l2_read(const void* src, size_t region_bytes, int32_t blocks, int32_t iters,
+                     uint32_t* out, void* stream) {
+  if (!src || !out) return MOE_ERR_NULL;
+  if (blocks < 1 || iters < 1 || region_bytes == 0 || region_bytes % 65536 != 0 || !aligned16(src))
+    return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(l2_read, dim3(static_cast<unsigned>(blocks)), dim3(kLoopThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                     region_bytes / 16, iters, out);
   return status_of(hipGetLastError());
 }
 

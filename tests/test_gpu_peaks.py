@@ -1,5 +1,5 @@
-"""The achievable-peak probes on the GPU: the streaming read touches every
-word (its per-thread XORs combine to the XOR of the buffer) and the
+"""The achievable-peak probes on the GPU: the streaming and L2 reads touch
+every word (their per-thread XORs combine to the XOR of the buffer) and the
 streaming copy is exact, on sizes that leave a ragged grid-stride tail; the
 MFMA and FMA loops give finite, non-zero, run-to-run identical results and a
 positive rate."""
@@ -30,6 +30,21 @@ def test_stream_read_and_copy_touch_every_word(n16, blocks):
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert got == want
     assert torch.equal(dst, src)
+
+
+@pytest.mark.parametrize("blocks,region_kb,iters", [(1, 64, 1), (3, 128, 3)])
+def test_l2_read_touches_every_word(blocks, region_kb, iters):
+    say(f"[peaks] l2 read blocks={blocks} region={region_kb} KB iters={iters}")
+    n32 = blocks * region_kb * 1024 // 4
+    gen = torch.Generator(device="cpu").manual_seed(n32)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (n32,), generator=gen, dtype=torch.int64).to(torch.int32)
+    out = torch.empty(blocks * 512, dtype=torch.int32, device="cuda")
+    pk.moe_peak_l2_read(host.cuda(), region_kb * 1024, blocks, iters, out)
+    torch.cuda.synchronize()
+    # every word is read `iters` times (odd), so the XORs combine to the buffer's
+    assert np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)) == \
+        np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert pk.measure_l2(blocks=64, iters=20, reps=2) > 0
 
 
 @pytest.mark.parametrize("form", list(pk.FORMS))

@@ -54,6 +54,14 @@ def test_bad_arguments_are_rejected_on_the_host():
     assert rd(fake, 24, 1, fake, None) == L.MOE_ERR_SHAPE
     assert rd(odd, 16, 1, fake, None) == L.MOE_ERR_SHAPE
     assert rd(fake, 16, 0, fake, None) == L.MOE_ERR_SHAPE
+    l2 = lib.moe_peak_l2_read
+    assert l2(None, 65536, 1, 1, fake, None) == L.MOE_ERR_NULL
+    assert l2(fake, 65536, 1, 1, None, None) == L.MOE_ERR_NULL
+    assert l2(fake, 32768, 1, 1, fake, None) == L.MOE_ERR_SHAPE      # not a multiple of 64 KB
+    assert l2(fake, 0, 1, 1, fake, None) == L.MOE_ERR_SHAPE
+    assert l2(fake, 65536, 0, 1, fake, None) == L.MOE_ERR_SHAPE
+    assert l2(fake, 65536, 1, 0, fake, None) == L.MOE_ERR_SHAPE
+    assert l2(odd, 65536, 1, 1, fake, None) == L.MOE_ERR_SHAPE
     assert cp(None, fake, 16, 1, None) == L.MOE_ERR_NULL
     assert cp(fake, odd, 16, 1, None) == L.MOE_ERR_SHAPE
     assert cp(fake, ctypes.c_void_p(0x1010), 32, 1, None) == L.MOE_ERR_SHAPE   # overlap
