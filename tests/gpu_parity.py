@@ -7,7 +7,9 @@ The bar (the tolerances of the layer's specification):
     those are counted and their GPU set must be valid within 1e-5;
   * permutation and offsets bit-exact (they are defined by the indices);
   * outputs: max |GPU - oracle| <= 2e-2 * RMS(oracle) for bf16/fp8 paths and
-    <= 1e-4 * RMS(oracle) for the fp32 path; near-tie tokens are compared
+    <= 1e-4 * RMS(oracle) for the fp32 path, beyond the rounding that
+    storing each routed slot row once in the activation dtype adds (at most
+    2^-8 of the slot in bf16, elementwise); near-tie tokens are compared
     with the oracle evaluated on the GPU's selected set.
 """
 
@@ -132,9 +134,23 @@ def check_permutation(spec, idx, offsets, perm):
     assert np.array_equal(perm, perm_or), "permutation differs"
 
 
-def rel_err(got, want):
+def rel_err(got, want, allowance=0.0):
+    """max(|got - want| - allowance) / RMS(want), and RMS(want)."""
     rms = float(np.sqrt(np.mean(want ** 2)))
-    return float(np.abs(got - want).max()) / max(rms, 1e-300), rms
+    return float((np.abs(got - want) - allowance).max()) / max(rms, 1e-300), rms
+
+
+# Relative rounding of one value stored in the activation dtype: bf16 keeps 8
+# significant bits (round to nearest: at most 2^-8 of the value), fp32 24.
+STORE_REL = {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}
+
+
+def slot_storage_allowance(act_dtype, slots):
+    """Elementwise error that storing the K routed slot rows [.., K, d] once
+    in the activation dtype contributes to their sum: each is off by at most
+    STORE_REL of itself. (With one slot and no shared expert the output is a
+    single stored slot, so this rounding alone can reach 2^-8 max|y|.)"""
+    return STORE_REL[act_dtype] * np.abs(slots).sum(axis=-2)
 
 
 def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
@@ -159,7 +175,8 @@ def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
         # y = residual + expert sum: the error is measured against the
         # expert sum's own RMS (the residual itself enters exactly)
         y = y - residual[rows]
-    e_y, rms = rel_err(y, y_or)
+    # the arithmetic error, beyond the rounding of the stored slot rows
+    e_y, rms = rel_err(y, y_or, slot_storage_allowance(spec.act_dtype, routed_or))
     assert e_y <= tol, f"y: max err / RMS = {e_y:.3e} > {tol}"
     if spec.S > 0:
         ysh = oracle.decode_stored(host(layer.y_shared[trow].contiguous()))
@@ -174,11 +191,11 @@ def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
     slot_rows = (trow[:, None] * K + torch.arange(K, device=x.device)[None, :]).reshape(-1)
     osl = oracle.decode_stored(host(layer.out_slots[slot_rows].contiguous())).reshape(len(rows), K, d)
     # out_slots is an intermediate held in the activation dtype: each element
-    # also carries its own storage rounding (at most 2^-9 relative in bf16,
+    # also carries its own storage rounding (at most 2^-8 relative in bf16,
     # 2^-24 in fp32) on top of the arithmetic budget of the output tolerance.
     # Each (token, slot) row is one gate-scaled expert output, so its error
     # is measured against that row's own RMS.
-    store = 2.0 ** -9 if spec.act_dtype == "bf16" else 2.0 ** -24
+    store = STORE_REL[spec.act_dtype]
     rms_row = np.sqrt(np.mean(aligned ** 2, axis=2, keepdims=True))
     excess = np.abs(osl - aligned) - store * np.abs(aligned)
     e_o = float((excess / np.maximum(rms_row, 1e-300)).max())
