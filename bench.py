@@ -1,7 +1,7 @@
 """Throughput of the DeepSeekMoE layer forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-decode]
-                    [--no-grouped] [--no-fp8] [--no-stress]
+                    [--no-grouped] [--no-fp8] [--no-stress] [--no-ep8]
 
 One step = one whole layer call on one batch already resident in HBM:
 router GEMM + sigmoid + biased top-K + gates + loads, the stable permutation,
@@ -20,7 +20,8 @@ timed on a bounded
 sample on the host's cores with the GPU's error on those tokens, and the
 other workloads: the layer with the pre-MoE RMSNorm and residual, the decode
 layer's fraction of HBM peak, node-limited routing (8 groups, top-4), the
-fine-grained fp8 prefill layer, the skewed-load stress run (20 batches
+fine-grained fp8 prefill layer, one GPU's share of the layer under 8-way
+expert parallelism (32 local experts, 2048 rows each), the skewed-load stress run (20 batches
 with the bias update, max/mean load per batch), and the tiny fp32 and
 2024-layout workloads (tokens/s and TFLOP/s against their peaks).
 Measured peaks come from the probes of libmoe_peaks.so (a loop of
@@ -55,6 +56,7 @@ WORKLOAD = "v3_prefill_bf16"
 DECODE = "v3_decode_fp8"
 GROUPED = "v3_grouped_bf16"
 FP8B = "v3_prefill_fp8b"
+EP8 = "v3_ep8_shard_bf16"
 STRESS = "zipf_stress_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_fp8_traffic.txt")
@@ -339,6 +341,33 @@ def grouped_measure(steps, warmup, plain_route_ms):
     return out
 
 
+def ep8_measure(steps, warmup):
+    """One GPU's share of the V3 prefill layer under 8-way expert
+    parallelism (32 local experts, 2048 routed rows each; the collectives
+    that would move those rows are not part of it): the same GEMM flops as
+    the single-GPU layer on 1/8 of its weights, so every token tile is full
+    and the launches are MFMA-bound."""
+    spec = synth.get_config(EP8)
+    inp, layer, bufs = setup(spec)
+    x, bias = inp["x"], inp["bias"]
+    timer = Timed()
+    step_ms = []
+    sec = time_steps(layer, x, bias, bufs, steps, warmup, timer, step_ms)
+    gms = timer.mean_ms()
+    tf = spec.flops() / sec / 1e12
+    gtf = gate_up_flops(spec) / (gms * 1e-3) / 1e12
+    out = {"workload": EP8, "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
+           **spread(step_ms), "routed_rows": spec.T * spec.K,
+           "layer_TFLOPs": tf, "layer_frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+           "gate_up_ms": gms, "gate_up_TFLOPs": gtf,
+           "gate_up_mfma_frac": gtf / MFMA_BF16_PEAK_TFLOPS}
+    log(f"[bench] ep8 shard: {sec*1e3:.3f} ms/step, layer {tf:.0f} TFLOP/s, gate/up {gms:.3f} ms "
+        f"({gtf:.0f} TFLOP/s)")
+    del inp, layer, bufs
+    torch.cuda.empty_cache()
+    return out
+
+
 def fp8_gate_up_bytes(spec) -> float:
     """Algorithmic HBM bytes of one fine-grained fp8 gate/up launch: W1 and W3
     codes of every routed and shared expert once with their 128 x 128 block
@@ -476,6 +505,11 @@ def attach_measured_fractions(result, peaks):
     if "grouped" in result:
         g = result["grouped"]
         g["layer_frac_measured_mfma"] = g["layer_TFLOPs"] / bf16
+    if "ep8_shard" in result:
+        e = result["ep8_shard"]
+        e["layer_frac_measured_mfma"] = e["layer_TFLOPs"] / bf16
+        e["gate_up_frac_of_measured_loop"] = e["gate_up_TFLOPs"] / bf16
+        e["gate_up_frac_of_own_form_loop"] = e["gate_up_TFLOPs"] / peaks["mfma_loop_TFLOPs"]["bf16_32x32x16"]
     if "stress" in result:
         result["stress"]["frac_of_measured"] = result["stress"]["layer_TFLOPs"] / bf16
     for o in result.get("other_configs", []):
@@ -563,6 +597,7 @@ def main():
     ap.add_argument("--no-grouped", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-stress", action="store_true")
+    ap.add_argument("--no-ep8", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before timing, run one 1 GiB read + 1 GiB write elementwise kernel, "
                          "the known-size reference for HBM byte counters")
@@ -650,6 +685,9 @@ def main():
     if not args.no_fp8:
         log(f"[bench] fine-grained fp8 workload {FP8B}")
         result["fp8_prefill"] = fp8_measure(args.steps, args.warmup)
+    if not args.no_ep8:
+        log(f"[bench] one GPU's expert-parallel share {EP8}")
+        result["ep8_shard"] = ep8_measure(args.steps, args.warmup)
     if not args.no_stress:
         log(f"[bench] skewed-load workload {STRESS}")
         result["stress"] = stress_measure()

@@ -135,6 +135,14 @@ CONFIGS = {
         fp8_scaling="block", bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 7,
         description="V3-shape prefill in fine-grained fp8: 128x128 weight blocks, 1x128 activation tiles",
     ),
+    "v3_ep8_shard_bf16": MoEConfig(
+        name="v3_ep8_shard_bf16", T=8192, d=7168, E=32, K=8, I=2048, S=1, Is=2048,
+        score=SCORE_SIGMOID, norm=NORM_SELECTED, act_dtype="bf16", weight_dtype="bf16",
+        bias_range=0.05, x_std=1.0, w_std=0.02, seed=_BASE + 8,
+        description="One GPU's share of the V3 prefill layer under 8-way expert parallelism: "
+                    "32 local experts receiving 8 x 8192 x 8 / 256 = 2048 routed rows each, "
+                    "the shared expert on the 8192 local tokens",
+    ),
 }
 
 

@@ -34,7 +34,8 @@ def _sample_rows(T, n, near, seed=0):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("name,n_rows", [("dsmoe2024_bf16", 96), ("v3_prefill_bf16", 12),
-                                         ("v3_decode_fp8", 16), ("v3_grouped_bf16", 12)])
+                                         ("v3_decode_fp8", 16), ("v3_grouped_bf16", 12),
+                                         ("v3_ep8_shard_bf16", 12)])
 def test_fullsize_layer(name, n_rows):
     spec = synth.get_config(name)
     say(f"[full] {name}: generating inputs")
