@@ -557,6 +557,10 @@ int pick_bm(int64_t rows_per_group) {
   return 256;
 }
 
+// Build-time knobs: depth (K stages) of the weight register ring of the
+// 128/256-token kernels (MOE_NS_BIG) and of the 32-token ones
+// (MOE_NS_SMALL); 3 measured best or equal (deeper rings change nothing
+// for decode, and do not fit the registers of the 256-token tiles).
 template <int MODE, bool FP8>
 void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
 #ifndef MOE_NS_BIG
