@@ -60,6 +60,7 @@ EP8 = "v3_ep8_shard_bf16"
 STRESS = "zipf_stress_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_fp8_traffic.txt")
+MFMA_UTIL_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_util.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
                   for f in ("ffn.hip", "gemm_core.hpp", "common.hpp")]
 
@@ -74,6 +75,22 @@ def kernel_source_hash() -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_mfma_util(path=MFMA_UTIL_FILE):
+    """Matrix-core busy percentages of the grouped GEMM launches from the
+    committed rocprofv3 counter run (MfmaUtil), if it was taken on the
+    current kernel source; else an empty dict."""
+    if not os.path.exists(path):
+        return {}
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha") != kernel_source_hash():
+        return {}
+    return {k[len("mfma_util_"):]: float(v) for k, v in kv.items() if k.startswith("mfma_util_")}
 
 
 def measured_traffic(path=TRAFFIC_FILE):
@@ -698,6 +715,11 @@ def main():
     peaks = measured_peaks()
     result["measured_peaks"] = peaks
     attach_measured_fractions(result, peaks)
+    # matrix-core busy share of the GEMM launches, from the committed counter
+    # run (null when the kernels changed since it was taken)
+    util = measured_mfma_util()
+    result["roofline"]["mfma_busy_pct"] = util.get("v3_gate_up")
+    result["mfma_busy_pct_counters"] = util or None
     print(json.dumps(result), flush=True)
 
 
