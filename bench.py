@@ -61,6 +61,7 @@ STRESS = "zipf_stress_bf16"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_fp8_traffic.txt")
 MFMA_UTIL_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_util.txt")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_v3_fp8_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
                   for f in ("ffn.hip", "gemm_core.hpp", "common.hpp")]
 
@@ -94,8 +95,9 @@ def measured_mfma_util(path=MFMA_UTIL_FILE):
 
 
 def measured_traffic(path=TRAFFIC_FILE):
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
-    if they were taken on the current kernel source; else None."""
+    """HBM bytes from a committed rocprofv3 counter summary (per gate/up launch,
+    or per decode layer call for the decode one), if the counters were taken on
+    the current kernel source; else None."""
     if not os.path.exists(path):
         return None
     kv = {}
@@ -106,7 +108,8 @@ def measured_traffic(path=TRAFFIC_FILE):
     if kv.get("kernel_src_sha") != kernel_source_hash():
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["decode_gemm_bytes_per_call"] if "decode_gemm_bytes_per_call" in kv
+                     else kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
@@ -291,7 +294,9 @@ def decode_measure(steps, warmup):
            "active_experts": n_active, "algorithmic_bytes": int(bytes_), "achieved_GBs": gbs,
            "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, **spread(step_ms),
            "graph_ms_per_step": gsec * 1e3, "graph_tokens_per_s": spec.T / gsec,
-           "graph_achieved_GBs": ggbs, "graph_frac": ggbs / HBM_PEAK_GBS}
+           "graph_achieved_GBs": ggbs, "graph_frac": ggbs / HBM_PEAK_GBS,
+           # HBM bytes of its two GEMM launches from the committed counter runs
+           "gemm_traffic": measured_traffic(DECODE_TRAFFIC_FILE)}
     del inp, layer, bufs, graph, xg
     torch.cuda.empty_cache()
     return out
