@@ -62,6 +62,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_traffic.txt")
 TRAFFIC_FILE_FP8 = os.path.join(ROOT, "profiles", "gate_up_v3_prefill_fp8_traffic.txt")
 MFMA_UTIL_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_util.txt")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_v3_fp8_traffic.txt")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
                   for f in ("ffn.hip", "gemm_core.hpp", "common.hpp")]
 
@@ -92,6 +93,30 @@ def measured_mfma_util(path=MFMA_UTIL_FILE):
     if kv.get("kernel_src_sha") != kernel_source_hash():
         return {}
     return {k[len("mfma_util_"):]: float(v) for k, v in kv.items() if k.startswith("mfma_util_")}
+
+
+def measured_clock(path=CLOCK_FILE):
+    """Engine clock (GHz) and matrix-core busy share (%) of the grouped GEMM
+    launches from the committed rocprofv3 counter run (GRBM_GUI_ACTIVE over
+    each dispatch's duration), if it was taken on the current kernel source;
+    with the dense bf16 MFMA rate at that clock. Else an empty dict."""
+    if not os.path.exists(path):
+        return {}
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_src_sha") != kernel_source_hash():
+        return {}
+    out = {}
+    for k, v in kv.items():
+        if k.startswith("clock_ghz_"):
+            name = k[len("clock_ghz_"):]
+            ghz = float(v)
+            out[name] = {"ghz": ghz, "mfma_busy_pct": float(kv.get("mfma_busy_" + name, "nan")),
+                         "bf16_ceiling_TFLOPs": MFMA_BF16_PEAK_TFLOPS * ghz / 2.4}
+    return out
 
 
 def measured_traffic(path=TRAFFIC_FILE):
@@ -725,6 +750,11 @@ def main():
     util = measured_mfma_util()
     result["roofline"]["mfma_busy_pct"] = util.get("v3_gate_up")
     result["mfma_busy_pct_counters"] = util or None
+    # the clock the part ran the GEMMs at (power-limited below the 2.4 GHz of
+    # the published peak), from the committed counter run
+    clock = measured_clock()
+    result["roofline"]["clock_ghz"] = clock.get("v3_gate_up", {}).get("ghz")
+    result["clock_counters"] = clock or None
     print(json.dumps(result), flush=True)
 
 
