@@ -1,0 +1,63 @@
+"""The benchmark's readers of the committed rocprofv3 summaries, on the host:
+each summary parses, carries the hash of the kernel sources it was taken on,
+and a reader returns nothing once that hash no longer matches (a changed
+kernel must not be reported with another kernel's counters)."""
+
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+sys.path.insert(0, str(ROOT))
+
+import bench  # noqa: E402
+
+READERS = [
+    ("gate_up_v3_prefill_traffic.txt", bench.measured_traffic),
+    ("gate_up_v3_prefill_fp8_traffic.txt", bench.measured_traffic),
+    ("decode_v3_fp8_traffic.txt", bench.measured_traffic),
+    ("gemm_mfma_util.txt", bench.measured_mfma_util),
+    ("gemm_clock.txt", bench.measured_clock),
+]
+
+
+def _sha(path):
+    for line in path.read_text().splitlines():
+        if line.startswith("kernel_src_sha"):
+            return line.split("=", 1)[1].strip()
+    return None
+
+
+@pytest.mark.parametrize("name,reader", READERS, ids=[r[0] for r in READERS])
+def test_summary_has_command_and_hash(name, reader):
+    path = ROOT / "profiles" / name
+    text = path.read_text()
+    assert "rocprofv3" in text and "command:" in text
+    assert _sha(path) is not None
+
+
+@pytest.mark.parametrize("name,reader", READERS, ids=[r[0] for r in READERS])
+def test_reader_gated_by_source_hash(name, reader, tmp_path):
+    path = ROOT / "profiles" / name
+    value = reader(str(path))
+    if _sha(path) == bench.kernel_source_hash():
+        assert value  # current summary: a number or a non-empty table
+    else:
+        assert not value
+    stale = tmp_path / name
+    stale.write_text(path.read_text().replace(_sha(path), "0" * 16))
+    assert not reader(str(stale))
+
+
+def test_values_in_physical_range():
+    if _sha(ROOT / "profiles" / "gemm_clock.txt") != bench.kernel_source_hash():
+        pytest.skip("clock summary taken on other kernel sources")
+    clock = bench.measured_clock()
+    for name, c in clock.items():
+        assert 0.5 < c["ghz"] <= 2.45, name            # engine clock at most the 2.4 GHz peak
+        assert 0.0 < c["mfma_busy_pct"] <= 100.0, name
+        assert c["bf16_ceiling_TFLOPs"] <= bench.MFMA_BF16_PEAK_TFLOPS * 2.45 / 2.4
+    decode = bench.measured_traffic(bench.DECODE_TRAFFIC_FILE)
+    if decode:
+        assert 7.0e9 < decode < 1.0e10                  # 168 active experts x 44.09 MB, read once
