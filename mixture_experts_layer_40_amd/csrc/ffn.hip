@@ -132,8 +132,8 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
 
 // The K loop (MainLoop) and its building blocks are in gemm_core.hpp.
 
-template <int MODE, bool FP8, int BM, int NSA>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
+template <int MODE, bool FP8, int BM, int NSA, int RF = 1>
+__global__ __launch_bounds__(kThreads / RF) void grouped_gemm_mfma(GemmArgs args) {
   constexpr int NTF = BM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t bs0[BM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t bs1[BM * 64];
@@ -147,42 +147,41 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
   const int l = lane_id(), w = wave_id(), g = l >> 5, r32 = l & 31;
   const int ntf = (tl.mvalid + 31) >> 5;
 
-  // ---- this wave's 32-row weight fragment ----
-  // Rows layout: lane l reads row (l % 32) of the fragment, K-elements
+  // ---- this wave's RF 32-row weight fragments (rb0 .. rb0 + RF - 1) ----
+  // Rows layout: lane l reads row (l % 32) of a fragment, K-elements
   // 32g .. 32g+31 of each 64-wide stage (g = l / 32), 16 bytes at a time.
   // Tiled layout: fragment rb, stage ks is one contiguous tile of 32 x 64
   // weights; lane l's piece v sits at byte v * 1024 + 16 l of it.
-  int nrow0;        // gate/up: first of 16 intermediate columns; down: first of 32 rows
-  bool wvalid;
-  const uint8_t* aptr;
+  // Fragments past the weight rows read fragment 0 and store nothing.
+  const uint8_t* aptr[RF];
   constexpr int wbytes = FP8 ? 1 : 2;
   const int nk = a.kdim / 64;
-  int astage = 64 * wbytes, avs = 16;
-  const int rb = (MODE == kGateUp ? tl.nblk * kBNGate / 16 : tl.nblk * kBNDown / 32) + w;
-  nrow0 = MODE == kGateUp ? 16 * rb : 32 * rb;
-  wvalid = nrow0 < a.n;
-  const int rbv = wvalid ? rb : 0;
-  if (a.tiled) {
-    astage = 32 * 64 * wbytes;
-    avs = 1024;
-    aptr = static_cast<const uint8_t*>(a.wa) + static_cast<size_t>(tl.e) * a.wstride * wbytes +
-           static_cast<size_t>(rbv) * nk * astage + 16 * l;
-  } else if (MODE == kGateUp) {
-    const int row = 16 * rbv + (r32 & 15);
-    aptr = static_cast<const uint8_t*>(r32 < 16 ? a.wa : a.wb) +
-           (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
-  } else {
-    const int row = 32 * rbv + r32;
-    aptr = static_cast<const uint8_t*>(a.wa) +
-           (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
+  const int astage = a.tiled ? 32 * 64 * wbytes : 64 * wbytes, avs = a.tiled ? 1024 : 16;
+  const int rb0 = (MODE == kGateUp ? tl.nblk * kBNGate / 16 : tl.nblk * kBNDown / 32) + RF * w;
+  auto frag_row0 = [&](int f) { return MODE == kGateUp ? 16 * (rb0 + f) : 32 * (rb0 + f); };
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+    const int rbv = frag_row0(f) < a.n ? rb0 + f : 0;
+    if (a.tiled) {
+      aptr[f] = static_cast<const uint8_t*>(a.wa) + static_cast<size_t>(tl.e) * a.wstride * wbytes +
+                static_cast<size_t>(rbv) * nk * astage + 16 * l;
+    } else if (MODE == kGateUp) {
+      const int row = 16 * rbv + (r32 & 15);
+      aptr[f] = static_cast<const uint8_t*>(r32 < 16 ? a.wa : a.wb) +
+                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
+    } else {
+      const int row = 32 * rbv + r32;
+      aptr[f] = static_cast<const uint8_t*>(a.wa) +
+                (static_cast<size_t>(tl.e) * a.wstride + static_cast<size_t>(row) * a.kdim + 32 * g) * wbytes;
+    }
   }
 
-  f32x16 acc[NTF];
+  f32x16 acc[RF * NTF];
 #pragma unroll
-  for (int t = 0; t < NTF; ++t) acc[t] = f32x16{};
+  for (int t = 0; t < RF * NTF; ++t) acc[t] = f32x16{};
 
   const uint16_t* act = static_cast<const uint16_t*>(a.act);
-  using ML = MainLoop<FP8, NSA, BM>;
+  using ML = MainLoop<FP8, NSA, BM, false, RF>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
     case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, bs3, acc); break;
@@ -192,7 +191,11 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
     default: break;
   }
 
-  if (!wvalid) return;
+#pragma unroll
+  for (int f = 0; f < RF; ++f) {
+  const int nrow0 = frag_row0(f);  // gate/up: first of 16 intermediate columns; down: first of 32 rows
+  if (nrow0 >= a.n) continue;
+  f32x16* facc = acc + f * NTF;
   if (MODE == kGateUp) {
     uint16_t* h = static_cast<uint16_t*>(a.h);
 #pragma unroll
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
           float hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            hv[q] = silu_fast(acc[t][4 * i + q] * sg[q]) * (acc[t][4 * (i + 2) + q] * su[q]);
+            hv[q] = silu_fast(facc[t][4 * i + q] * sg[q]) * (facc[t][4 * (i + 2) + q] * su[q]);
           u32x2 v;
           v.x = pack_bf16x2(hv[0], hv[1]);
           v.y = pack_bf16x2(hv[2], hv[3]);
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float sc = FP8 ? a.sa[static_cast<size_t>(tl.e) * a.n + col + q] : 1.f;
-          ov[q] = (acc[t][4 * i + q] * sc) * gv;
+          ov[q] = (facc[t][4 * i + q] * sc) * gv;
         }
         const size_t o = static_cast<size_t>(slot) * a.n + col;
         if (a.out_f32) {
@@ -250,6 +253,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_mfma(GemmArgs args) {
         }
       }
     }
+  }
   }
 }
 
@@ -292,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f8b(GemmArgs args) {
   constexpr int astage = 32 * 128, avs = 1024;
   const uint8_t* aptr = static_cast<const uint8_t*>(a.wa) + static_cast<size_t>(tl.e) * a.wstride +
                         static_cast<size_t>(rbv) * nkb * astage + 16 * l;
+  const uint8_t* aps[1] = {aptr};
 
   // token tile scales (rows past the expert's end repeat its last row)
   for (int i = tid; i < BM * nkb; i += kThreads) {
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f8b(GemmArgs args) {
   using ML = MainLoop<false, NSA, BM, true>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
-    case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, kdim16, astage, avs, bs0, bs1, bs2, bs3, acc, post); break;
+    case n: if constexpr (n <= NTF) ML::template run<n>(aps, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, kdim16, astage, avs, bs0, bs1, bs2, bs3, acc, post); break;
     MOE_NT_CASE(1) MOE_NT_CASE(2) MOE_NT_CASE(3) MOE_NT_CASE(4)
 #undef MOE_NT_CASE
     default: break;
@@ -559,8 +564,9 @@ int pick_bm(int64_t rows_per_group) {
 
 // Build-time knobs: depth (K stages) of the weight register ring of the
 // 128/256-token kernels (MOE_NS_BIG) and of the 32-token ones
-// (MOE_NS_SMALL); 3 measured best or equal (deeper rings change nothing
-// for decode, and do not fit the registers of the 256-token tiles).
+// (MOE_NS_SMALL); 3 measured best or equal (2 is 12 % slower at two
+// fragments per wave; deeper rings change nothing for decode, and do not
+// fit the registers of the 256-token tiles).
 template <int MODE, bool FP8>
 void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
 #ifndef MOE_NS_BIG
@@ -571,11 +577,18 @@ void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
 #endif
   constexpr int NS_BIG = MOE_NS_BIG;
   constexpr int NS_SMALL = MOE_NS_SMALL;
+#ifndef MOE_RF
+#define MOE_RF 2
+#endif
+  // Weight fragments per wave of the 128/256-token kernels: 2 (4 waves, one
+  // per SIMD) measured 5 % faster on the V3-shape gate/up launch than 1
+  // (8 waves, two per SIMD), 3 % on the layer.
+  constexpr int RF = MOE_RF;
   switch (bm) {
     case 32: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 32, NS_SMALL>), gd, dim3(kThreads), 0, s, a); break;
     case 64: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 64, NS_SMALL>), gd, dim3(kThreads), 0, s, a); break;
-    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG>), gd, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG>), gd, dim3(kThreads), 0, s, a); break;
+    case 128: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 128, NS_BIG, RF>), gd, dim3(kThreads / RF), 0, s, a); break;
+    default: hipLaunchKernelGGL((grouped_gemm_mfma<MODE, FP8, 256, NS_BIG, RF>), gd, dim3(kThreads / RF), 0, s, a); break;
   }
 }
 

@@ -11,10 +11,13 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // bf16 activations, bf16 or fp8 weights, MFMA 32x32x16.
 //
-// A block (8 waves, two per SIMD) computes 256 weight rows x BM tokens
-// (BM = 32..256). Wave w owns one 32-row weight fragment and all BM tokens
-// (in the expert GEMMs, gate/up fragments hold 16 gate and the 16 up rows of
-// the same intermediate columns; see ffn.hip).
+// A block computes 256 weight rows (8 fragments of 32) x BM tokens
+// (BM = 32..256): either 8 waves, two per SIMD, each owning one fragment and
+// all BM tokens (RF = 1), or 4 waves, one per SIMD, each owning two
+// fragments (RF = 2: 512 registers per lane, the accumulators in AGPRs, and
+// each token fragment read from LDS feeds two MFMAs, which halves the LDS
+// reads per flop). In the expert GEMMs, gate/up fragments hold 16 gate and
+// the 16 up rows of the same intermediate columns (see ffn.hip).
 // Weight rows are never shared between waves: each lane streams its 64
 // bytes of a fragment per 64-wide K stage (lane group g = l/32 takes
 // K-elements 32g .. 32g+31 of the stage, 8 per MFMA step) straight into a
@@ -79,9 +82,15 @@ struct NoPost {
   __device__ __forceinline__ void operator()(N, int, A&) const {}
 };
 
-template <bool FP8, int NSA, int BM, bool F8B = false>
+template <bool FP8, int NSA, int BM, bool F8B = false, int RF = 1>
 struct MainLoop {
   static_assert(!(FP8 && F8B), "F8B takes fp8 codes on both sides; FP8 widens weights to bf16");
+  static_assert(RF == 1 || (RF == 2 && !F8B), "two fragments per wave: bf16 / fp8-row loops only");
+  // RF weight fragments per wave: kThreads / RF threads per block, so the
+  // block still covers 8 fragments (256 rows); with RF = 2 each token
+  // fragment read from LDS feeds two MFMAs.
+  static constexpr int TH = kThreads / RF;
+  static constexpr int NTF = BM / 32;
   static constexpr int AW = FP8 ? 2 : 4;       // 16-byte loads per fragment per stage
   static constexpr size_t WB = FP8 ? 1 : 2;    // bytes per weight
   static constexpr int ND = MOE_TOKEN_STAGES;  // LDS token stages (ND-1 in flight)
@@ -96,23 +105,23 @@ struct MainLoop {
   // kdim counts 16-bit units of a token row (fp8 rows: bytes / 2); one
   // stage is 64 such units.
   template <int NT>
-  __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
-                                             const int32_t* act_rows, int act_div, int mvalid,
-                                             int kdim, int astage, int avs,
+  __device__ __forceinline__ static void run(const uint8_t* const (&aptr)[RF], const uint16_t* act,
+                                             int row0, const int32_t* act_rows, int act_div,
+                                             int mvalid, int kdim, int astage, int avs,
                                              uint16_t* bs0, uint16_t* bs1, uint16_t* bs2,
-                                             uint16_t* bs3, f32x16 (&acc)[BM / 32]) {
+                                             uint16_t* bs3, f32x16 (&acc)[RF * NTF]) {
     run<NT>(aptr, act, row0, act_rows, act_div, mvalid, kdim, astage, avs, bs0, bs1, bs2, bs3,
             acc, NoPost{});
   }
 
   template <int NT, class Post>
-  __device__ __forceinline__ static void run(const uint8_t* aptr, const uint16_t* act, int row0,
-                                             const int32_t* act_rows, int act_div, int mvalid,
-                                             int kdim, int astage, int avs,
+  __device__ __forceinline__ static void run(const uint8_t* const (&aptr)[RF], const uint16_t* act,
+                                             int row0, const int32_t* act_rows, int act_div,
+                                             int mvalid, int kdim, int astage, int avs,
                                              uint16_t* bs0, uint16_t* bs1, uint16_t* bs2,
-                                             uint16_t* bs3, f32x16 (&acc)[BM / 32], Post&& post) {
+                                             uint16_t* bs3, f32x16 (&acc)[RF * NTF], Post&& post) {
     constexpr int CH = NT * 32 * 8;                     // 16-byte chunks per token stage
-    constexpr int BCH = (CH + kThreads - 1) / kThreads; // copies per thread per stage
+    constexpr int BCH = (CH + TH - 1) / TH;             // copies per thread per stage
     const int l = lane_id(), g = l >> 5, r32 = l & 31;
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int nk = kdim / 64;
@@ -124,7 +133,7 @@ struct MainLoop {
     int bdst[BCH];
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
-      const int q0 = (w * kWave + kThreads * i) % CH;
+      const int q0 = (w * kWave + TH * i) % CH;
       const int q = q0 + l, row = q >> 3, ch = (q & 7) ^ ((row >> 1) & 7);
       const int p = row0 + (row < mvalid ? row : mvalid - 1);
       const int src = act_rows ? max(act_rows[p], 0) / act_div : p;
@@ -132,14 +141,18 @@ struct MainLoop {
       bdst[i] = q0 * 8;
     }
 
-    u32x4 ra[NSA][AW];
-    // This lane's AW 16-byte pieces of K stage ks: at aptr + ks * astage +
-    // v * avs (rows layout: 16 consecutive bytes of its row; tiled layout:
-    // one 1 KB stripe per piece, so each load instruction reads 1 KB).
-    auto load_a = [&](u32x4 (&dst)[AW], int ks) {
-      const uint8_t* p = aptr + static_cast<size_t>(ks) * astage;
+    u32x4 ra[NSA][RF * AW];
+    // This lane's AW 16-byte pieces of K stage ks of fragment f: at
+    // aptr[f] + ks * astage + v * avs (rows layout: 16 consecutive bytes of
+    // its row; tiled layout: one 1 KB stripe per piece, so each load
+    // instruction reads 1 KB).
+    auto load_a = [&](u32x4 (&dst)[RF * AW], int ks) {
 #pragma unroll
-      for (int v = 0; v < AW; ++v) dst[v] = *reinterpret_cast<const u32x4*>(p + v * avs);
+      for (int f = 0; f < RF; ++f) {
+        const uint8_t* p = aptr[f] + static_cast<size_t>(ks) * astage;
+#pragma unroll
+        for (int v = 0; v < AW; ++v) dst[f * AW + v] = *reinterpret_cast<const u32x4*>(p + v * avs);
+      }
     };
     auto load_b = [&](uint16_t* buf, int ks) {
 #pragma unroll
@@ -154,7 +167,7 @@ struct MainLoop {
     // The stage's NV memory requests (issue(0 .. NV-1)) are spread evenly
     // over its 4*NT MFMAs: issued in one burst they queue at the CU's
     // address unit and hold every wave's MFMAs back behind them.
-    constexpr int NV = BCH + AW;
+    constexpr int NV = BCH + RF * AW;
     // F8B: the two 64-wide halves m of a 128-wide stage; lane group g takes
     // codes 32g .. 32g+31 of each half: weight pieces 2m, 2m+1 and token
     // chunks 4m+2g, 4m+2g+1 (the same K order on both operands).
@@ -164,7 +177,7 @@ struct MainLoop {
       dst[0] = *reinterpret_cast<const u32x4*>(row + ((c0 ^ sw) * 8));
       dst[1] = *reinterpret_cast<const u32x4*>(row + (((c0 + 1) ^ sw) * 8));
     };
-    auto compute8 = [&](const u32x4 (&src)[AW], const uint16_t* b0, f32x16 (&blk)[NT],
+    auto compute8 = [&](const u32x4 (&src)[RF * AW], const uint16_t* b0, f32x16 (&blk)[NT],
                         auto&& issue) {
       u32x4 bfr[2][NT][2];
 #pragma unroll
@@ -185,24 +198,29 @@ struct MainLoop {
         }
       }
     };
-    auto compute = [&](const u32x4 (&src)[AW], const uint16_t* b0, auto&& issue) {
+    auto compute = [&](const u32x4 (&src)[RF * AW], const uint16_t* b0, auto&& issue) {
       u32x4 bfr[2][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) read_b(bfr[0][t], b0, t, 0);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 op;
-        if constexpr (FP8) {
-          u32x4 lo, hi;
-          fp8x16_to_bf16x16(src[s >> 1], lo, hi);
-          op = (s & 1) ? hi : lo;
-        } else {
-          op = src[s];
+        u32x4 op[RF];
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+          if constexpr (FP8) {
+            u32x4 lo, hi;
+            fp8x16_to_bf16x16(src[f * AW + (s >> 1)], lo, hi);
+            op[f] = (s & 1) ? hi : lo;
+          } else {
+            op[f] = src[f * AW + s];
+          }
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if (s < 3) read_b(bfr[(s + 1) & 1][t], b0, t, s + 1);
-          acc[t] = mfma_32x32x16(op, bfr[s & 1][t], acc[t]);
+#pragma unroll
+          for (int f = 0; f < RF; ++f)
+            acc[f * NTF + t] = mfma_32x32x16(op[f], bfr[s & 1][t], acc[f * NTF + t]);
           const int i = s * NT + t;
           static_for<NV>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
@@ -211,6 +229,38 @@ struct MainLoop {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    // RF = 2: the 4*NT token-fragment reads of a stage, in (step, fragment)
+    // order, run LA reads ahead of the MFMA pairs that use them through a
+    // ring of LA + 1 registers (in place of a whole step's fragments).
+    auto compute2 = [&](const u32x4 (&src)[RF * AW], const uint16_t* b0, auto&& issue) {
+      constexpr int LA = 3, J = 4 * NT;
+      u32x4 bq[LA + 1];
+      static_for<(LA < J ? LA : J)>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        read_b(bq[j], b0, j % NT, j / NT);
+      });
+      static_for<J>([&](auto jc) {
+        constexpr int j = decltype(jc)::value, s = j / NT, t = j % NT;
+        if constexpr (j + LA < J) read_b(bq[(j + LA) % (LA + 1)], b0, (j + LA) % NT, (j + LA) / NT);
+#pragma unroll
+        for (int f = 0; f < RF; ++f) {
+          u32x4 op;
+          if constexpr (FP8) {
+            u32x4 lo, hi;
+            fp8x16_to_bf16x16(src[f * AW + (s >> 1)], lo, hi);
+            op = (s & 1) ? hi : lo;
+          } else {
+            op = src[f * AW + s];
+          }
+          acc[f * NTF + t] = mfma_32x32x16(op, bq[j % (LA + 1)], acc[f * NTF + t]);
+        }
+        static_for<NV>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          if constexpr ((k * J) / NV == j) issue(kc);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
     };
     auto buf = [&](int i) { return i == 0 ? bs0 : (i == 1 ? bs1 : (i == 2 ? bs2 : bs3)); };
 
@@ -235,13 +285,17 @@ struct MainLoop {
       constexpr int u = decltype(uc)::value;
       uint16_t* tdst = buf((u + ND - 1) % ND);          // its readers passed the last barrier
       const int ts = min(s + ND - 1, nk - 1);
-      u32x4 (&wdst)[AW] = ra[(u + NSA - 1) % NSA];      // consumed in the previous stage
-      const uint8_t* wsrc = aptr + static_cast<size_t>(min(s + NSA - 1, nk - 1)) * astage;
-      // requests 0 .. BCH-1: T(s+ND-1); BCH .. NV-1: W(s+NSA-1)
+      u32x4 (&wdst)[RF * AW] = ra[(u + NSA - 1) % NSA]; // consumed in the previous stage
+      const size_t woff = static_cast<size_t>(min(s + NSA - 1, nk - 1)) * astage;
+      // requests 0 .. BCH-1: T(s+ND-1); BCH .. NV-1: W(s+NSA-1), fragment by fragment
       auto issue = [&](auto kc) {
         constexpr int k = decltype(kc)::value;
-        if constexpr (k < BCH) dma16(bsrc[k] + ts * 64, tdst + bdst[k]);
-        else wdst[k - BCH] = *reinterpret_cast<const u32x4*>(wsrc + (k - BCH) * avs);
+        if constexpr (k < BCH) {
+          dma16(bsrc[k] + ts * 64, tdst + bdst[k]);
+        } else {
+          constexpr int f = (k - BCH) / AW, v = (k - BCH) % AW;
+          wdst[f * AW + v] = *reinterpret_cast<const u32x4*>(aptr[f] + woff + v * avs);
+        }
       };
       // W(s) landed: after its last piece came the requests of NSA-2 stages
       wait_vmcnt<(NSA - 2) * NV>();
@@ -249,6 +303,8 @@ struct MainLoop {
         f32x16 blk[NT];
         compute8(ra[u % NSA], buf(u % ND), blk, issue);
         post(IntC<NT>{}, s, blk);
+      } else if constexpr (RF == 2) {
+        compute2(ra[u % NSA], buf(u % ND), issue);
       } else {
         compute(ra[u % NSA], buf(u % ND), issue);
       }
@@ -257,7 +313,7 @@ struct MainLoop {
       // T and W of ND-2 stages. A plain barrier: the fence of __syncthreads
       // would wait for every copy in flight; this stage's LDS reads are
       // complete, their MFMAs issued.
-      wait_vmcnt<AW + (ND - 2) * NV>();
+      wait_vmcnt<RF * AW + (ND - 2) * NV>();
       __builtin_amdgcn_s_barrier();
     };
     // Whole groups of U stages, then the remainder, outside the loop so the

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void route_fused_bf16(
   if (tid < 256) hist[tid] = 0;
 
   const int row = min(32 * w + r32, E - 1);
-  const uint8_t* aptr = reinterpret_cast<const uint8_t*>(wr + static_cast<size_t>(row) * d + 32 * g);
+  const uint8_t* aptr[1] = {reinterpret_cast<const uint8_t*>(wr + static_cast<size_t>(row) * d + 32 * g)};
   f32x16 acc[1] = {f32x16{}};
   MainLoop<false, 3, BT>::template run<1>(aptr, x, t0, nullptr, 1, mvalid, d, 64 * 2, 16, bs0, bs1,
                                           bs2, bs3, acc);
