@@ -18,6 +18,7 @@
 //                    leader advances the expert's running row with one LDS
 //                    atomic whose old value is broadcast back.
 //   4. perm_gather : one wave per output row, 16-byte coalesced copies.
+//   perm_single    : 1-3 in one block when T*K <= 4096 (decode batches).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -135,6 +136,75 @@ __global__ __launch_bounds__(256) void perm_rank(const int32_t* __restrict__ idx
   }
 }
 
+// All of 1-3 in one block, for T*K <= kChunk (decode-sized batches): the
+// per-wave counts give the expert totals, their exclusive scan the offsets,
+// and the same ranking pass as perm_rank places every pair. One launch in
+// place of three; the result is the same stable order.
+__global__ __launch_bounds__(256) void perm_single(const int32_t* __restrict__ idx, int64_t TK,
+                                                   int E, int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ perm_slot) {
+  __shared__ int cnt[4][256];
+  __shared__ int tot[256];
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  for (int i = tid; i < 4 * 256; i += 256) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t wbase = static_cast<int64_t>(w) * kWaveChunk;
+  for (int i = l; i < kWaveChunk; i += kWave) {
+    const int64_t f = wbase + i;
+    if (f < TK) {
+      const int e = idx[f];
+      if (e >= 0 && e < E) atomicAdd(&cnt[w][e], 1);
+    }
+  }
+  __syncthreads();
+  const int mine = tid < E ? cnt[0][tid] + cnt[1][tid] + cnt[2][tid] + cnt[3][tid] : 0;
+  tot[tid] = mine;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive Hillis-Steele scan
+    const int v = tid >= o ? tot[tid - o] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    int run = tot[tid] - mine;
+    offsets[tid] = run;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const int c = cnt[ww][tid];
+      cnt[ww][tid] = run;
+      run += c;
+    }
+  }
+  const int total = tot[255];
+  if (tid == 0) offsets[E] = total;
+  for (int64_t p = total + tid; p < TK; p += 256) perm_slot[p] = -1;
+  __syncthreads();
+  for (int it = 0; it < kWaveChunk; it += kWave) {
+    const int64_t f = wbase + it + l;
+    int e = -1;
+    if (f < TK) {
+      e = idx[f];
+      if (e < 0 || e >= E) e = -1;
+    }
+    const bool part = e >= 0;
+    uint64_t peers = __ballot(part);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t m = __ballot((e >> b) & 1);
+      peers &= ((e >> b) & 1) ? m : ~m;
+    }
+    const int leader = part ? __ffsll(static_cast<long long>(peers)) - 1 : l;
+    int old = 0;
+    if (part && l == leader) old = atomicAdd(&cnt[w][e], __popcll(peers));
+    old = __shfl(old, leader, kWave);
+    if (part) {
+      const int64_t p = static_cast<int64_t>(old) + __popcll(peers & lanemask_lt());
+      if (p >= 0 && p < TK) perm_slot[p] = static_cast<int32_t>(f);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void perm_gather(const uint8_t* __restrict__ x,
                                                    const int32_t* __restrict__ perm_slot,
                                                    int64_t TK, int T, int K, int row_bytes,
@@ -200,14 +270,20 @@ hipError_t launch_permute(const moe_config& c, const int32_t* topk_idx, const vo
   if (TK == 0) {
     return launch_fill_i32(expert_offsets, 0, E + 1, s);
   }
-  hipLaunchKernelGGL(perm_hist, dim3(nblk), dim3(256), 0, s, topk_idx, TK, E, hist);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, s, hist, nblk, E, TK, expert_offsets,
-                     perm_slot);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(perm_rank, dim3(nblk), dim3(256), 0, s, topk_idx, TK, E, hist, perm_slot);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipError_t err;
+  if (nblk == 1) {
+    hipLaunchKernelGGL(perm_single, dim3(1), dim3(256), 0, s, topk_idx, TK, E, expert_offsets,
+                       perm_slot);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  } else {
+    hipLaunchKernelGGL(perm_hist, dim3(nblk), dim3(256), 0, s, topk_idx, TK, E, hist);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(perm_scan, dim3(1), dim3(256), 0, s, hist, nblk, E, TK, expert_offsets,
+                       perm_slot);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(perm_rank, dim3(nblk), dim3(256), 0, s, topk_idx, TK, E, hist, perm_slot);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   if (!x_perm) return hipSuccess;   // the caller reads x through perm_slot itself
   const int elem = c.act_dtype == MOE_DTYPE_F32 ? 4 : 2;
   const int row_bytes = c.hidden * elem;
