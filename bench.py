@@ -36,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -71,11 +72,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the GEMM kernel sources with comments and whitespace removed:
+    a committed counter summary stays valid across edits of comments only,
+    and is dropped as soon as any code changes."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            code = _COMMENT.sub(" ", f.read())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

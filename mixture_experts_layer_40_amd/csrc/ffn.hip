@@ -9,14 +9,16 @@
 //
 // CDNA4 design (bf16 / fp8 weights):
 //  * Orientation: weight rows are the first MFMA operand (v_mfma 32x32x16),
-//    token rows the second. A block (8 waves, two per SIMD) computes 256
-//    weight rows x up to 256 tokens of one expert; each wave owns one 32-row
-//    weight fragment and all tokens of the tile. Weight rows are never shared
-//    between waves, so every wave streams its rows from HBM straight into
-//    MFMA operand registers, two stages ahead (fp8 codes are widened to bf16
-//    in registers, exactly). In the tiled weight layout each of those loads
-//    reads a whole 1 KB stripe.
-//  * The token tile, which all 8 waves read, goes global -> LDS by direct
+//    token rows the second. A block computes 256 weight rows (8 fragments
+//    of 32) x up to 256 tokens of one expert. At 128/256-token tiles it is 4
+//    waves, one per SIMD, each owning two fragments and all tokens of the
+//    tile (accumulators in AGPRs; each token fragment read from LDS feeds
+//    two MFMAs); at 32/64-token tiles 8 waves, two per SIMD, one fragment
+//    each. Weight rows are never shared between waves, so every wave streams
+//    its rows from HBM straight into MFMA operand registers, two stages ahead
+//    (fp8 codes are widened to bf16 in registers, exactly). In the tiled
+//    weight layout each of those loads reads a whole 1 KB stripe.
+//  * The token tile, which all the block's waves read, goes global -> LDS by direct
 //    LDS loads (no registers), three stages deep; 16-byte chunks are
 //    XOR-swizzled by row pair so the 16 rows one ds_read_b128 serves land on
 //    16 distinct groups of the 64 banks.

@@ -21,7 +21,7 @@ namespace moe {
 // Weight rows are never shared between waves: each lane streams its 64
 // bytes of a fragment per 64-wide K stage (lane group g = l/32 takes
 // K-elements 32g .. 32g+31 of the stage, 8 per MFMA step) straight into a
-// register ring NSA stages deep. The token tile, read by all eight waves, goes
+// register ring NSA stages deep. The token tile, read by all the block's waves, goes
 // global -> LDS by direct loads, MOE_TOKEN_STAGES buffers deep; 16-byte
 // chunks are XOR-swizzled by row pair, so the 16 rows one ds_read_b128 serves
 // land on 16 distinct bank groups. Each stage's memory requests are spread

@@ -61,3 +61,15 @@ def test_values_in_physical_range():
     decode = bench.measured_traffic(bench.DECODE_TRAFFIC_FILE)
     if decode:
         assert 7.0e9 < decode < 1.0e10                  # 168 active experts x 44.09 MB, read once
+
+
+def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    base = "// header\nint f(int x) {\n  return x + 1;  /* inc */\n}\n"
+    src.write_text(base)
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
+    h0 = bench.kernel_source_hash()
+    src.write_text("// other words\n/* a block\n comment */ int f(int x) {\n    return x + 1;\n}\n")
+    assert bench.kernel_source_hash() == h0
+    src.write_text(base.replace("x + 1", "x + 2"))
+    assert bench.kernel_source_hash() != h0
