@@ -73,3 +73,15 @@ def test_source_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_source_hash() == h0
     src.write_text(base.replace("x + 1", "x + 2"))
     assert bench.kernel_source_hash() != h0
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}),
+                                      ([], {"WORLD_SIZE": "4"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    import os
+    import subprocess
+    e = dict(os.environ, **env)
+    p = subprocess.run([sys.executable, str(ROOT / "bench.py")] + argv, capture_output=True,
+                       text=True, env=e, timeout=300)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr and p.stdout == ""
