@@ -303,3 +303,22 @@ def test_fp8_block_entry_points_validate_on_host():
     assert dn(by(ok), *([None] + [fake] * 12), None, 0, None) == L.MOE_ERR_NULL
     z = _cfg(act_dtype="bf16", weight_dtype="fp8", weight_layout="tiled", d=256, I=256, Is=256, T=0)
     assert ex(by(z), *([None] * 17), None, 0, None) == L.MOE_OK
+
+
+def test_package_never_imports_the_oracle():
+    """The product path (the binding and its modules) neither names nor
+    imports the oracle: only the tests, smoke() and bench.py's cpu_baseline
+    use it."""
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    for src in (root / "mixture_experts_layer_40_amd").rglob("*.py"):
+        text = src.read_text()
+        assert "import oracle" not in text and "from oracle" not in text, src
+    code = ("import sys; import mixture_experts_layer_40_amd as m; m._lib.load_library(); "
+            "import mixture_experts_layer_40_amd.layer; "
+            "assert not any(k == 'oracle' or k.startswith('oracle.') for k in sys.modules), 'oracle imported'")
+    p = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    assert p.returncode == 0, p.stderr
