@@ -255,25 +255,36 @@ def spread(step_ms):
 
 
 def cpu_baseline(spec, inp, layer, bufs, n_tokens):
-    """The fp64 oracle on a bounded sample: route n_tokens tokens and compute
-    their layer outputs, decoding each touched expert's stored weights."""
+    """The fp64 oracle timed on the host's cores: routing of n_tokens tokens
+    of the batch (all of them by default: the full layer) and their layer
+    outputs, each routed expert's stored weights decoded to fp64 once. The
+    stored values are copied to host memory before the timed region. Then,
+    untimed, the parity of the GPU's output on the same tokens: every
+    selected set equal to the oracle's or, for a near-tie token, one the tie
+    leaves open (oracle.selection_valid), and y within 2e-2 x RMS of the
+    oracle evaluated on the GPU's set for near-tie tokens."""
     import oracle
     from threadpoolctl import threadpool_info
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(spec.T, n_tokens, replace=False))
+    T = spec.T
+    if n_tokens >= T:
+        rows = np.arange(T)
+    else:
+        rows = np.sort(np.random.default_rng(0).choice(T, n_tokens, replace=False))
     trow = torch.as_tensor(rows, device="cuda")
     host = synth.to_numpy_stored
     x = host(inp["x"][trow])
     wr = host(inp["wr"])
     bias = inp["bias"].cpu().numpy()
-    sc = lambda n, e: None if inp.get(n) is None else inp[n][e].cpu().numpy()
+    w = {n: host(inp[n]) for n in ("w1", "w3", "w2")}
+    sc = {n: None if inp.get(n) is None else inp[n].cpu().numpy() for n in ("s1", "s3", "s2")}
     shared = (host(inp["w1s"]), host(inp["w3s"]), host(inp["w2s"]),
               None if inp.get("s1s") is None else inp["s1s"].cpu().numpy(),
               None if inp.get("s3s") is None else inp["s3s"].cpu().numpy(),
               None if inp.get("s2s") is None else inp["s2s"].cpu().numpy())
+    pick = lambda n, e: None if sc[n] is None else sc[n][e]
     bank = oracle.ExpertBank(
-        fetch=lambda e: (host(inp["w1"][e]), host(inp["w3"][e]), host(inp["w2"][e]),
-                         sc("s1", e), sc("s3", e), sc("s2", e)),
+        fetch=lambda e: (w["w1"][e], w["w3"][e], w["w2"][e], pick("s1", e), pick("s3", e),
+                         pick("s2", e)),
         shared=shared, S=spec.S)
     t0 = time.perf_counter()
     x64 = oracle.decode_stored(x)
@@ -282,26 +293,43 @@ def cpu_baseline(spec, inp, layer, bufs, n_tokens):
     y_or = oracle.layer_rows(x64, r["sel"], r["gate"], bank)[0]
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    baseline = {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-                "sample": f"{n_tokens} tokens of the {spec.name} batch (routing + shared + "
-                          f"{len(np.unique(r['sel']))} routed experts decoded to fp64), {dt:.1f} s"}
-    # parity of the same tokens (outside the timed region): one plain layer
-    # step, then the GPU's y against the oracle's; a near-tie token (K-th and
-    # (K+1)-th keys within 1e-5) is evaluated on the GPU's selected set
+    n_exp = len(np.unique(r["sel"]))
+    what = (f"full layer: all {T} tokens" if len(rows) == T else f"{len(rows)} of {T} tokens")
+    baseline = {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                "sample": f"{what} of the {spec.name} batch (routing, shared expert, {n_exp} routed "
+                          f"experts decoded to fp64), {dt:.1f} s"}
+    # parity of the same tokens (outside the timed region): one plain layer step
     layer_step(layer, inp["x"], inp["bias"], bufs)
     torch.cuda.synchronize()
     gidx = layer.topk_idx[trow].cpu().numpy().astype(np.int64)
     near = r["near_tie"]
-    same = np.array([set(a) == set(b) for a, b in zip(gidx, r["sel"])])
+    valid = oracle.selection_valid(r, gidx, spec.K)
     if near.any():
         g_near = oracle.gate_values(r["scores"][near], gidx[near], spec.norm)
         y_or[near] = oracle.layer_rows(x64[near], gidx[near], g_near, bank)[0]
     y_gpu = layer.y[trow].double().cpu().numpy()
     rms = float(np.sqrt(np.mean(y_or ** 2)))
-    parity = {"tokens": n_tokens, "sets_equal_outside_near_ties": bool(np.all(same | near)),
-              "near_ties": int(near.sum()),
-              "max_abs_err_over_rms": float(np.abs(y_gpu - y_or).max() / rms), "tolerance": 2e-2}
+    err = float(np.abs(y_gpu - y_or).max() / rms)
+    parity = {"tokens": int(len(rows)), "selections_valid": bool(valid.all()),
+              "invalid_selections": int((~valid).sum()), "near_ties": int(near.sum()),
+              "max_abs_err_over_rms": err, "tolerance": 2e-2,
+              "pass": bool(valid.all() and err <= 2e-2)}
     return baseline, parity
+
+
+def bf16_slots_measure(layer, x, bias, bufs, steps, warmup):
+    """The same layer step with the routed slot rows held in bf16 (half their
+    bytes; each routed term then carries one bf16 rounding into the sum)."""
+    keep = layer.slot_dtype, layer.out_slots
+    layer.slot_dtype = "bf16"
+    layer.out_slots = torch.empty(keep[1].shape, dtype=torch.bfloat16, device="cuda")
+    try:
+        step_ms = []
+        sec = time_steps(layer, x, bias, bufs, steps, warmup, None, step_ms)
+    finally:
+        layer.slot_dtype, layer.out_slots = keep
+    return {"slot_dtype": "bf16", "ms_per_step": sec * 1e3, "tokens_per_s": x.shape[0] / sec,
+            **spread(step_ms)}
 
 
 def decode_measure(steps, warmup):
@@ -646,7 +674,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=40)
+    ap.add_argument("--cpu-tokens", type=int, default=None,
+                    help="tokens of the oracle baseline and parity check (default: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-grouped", action="store_true")
@@ -700,7 +729,7 @@ def main():
         "config": {"workload": WORKLOAD, "tokens": spec.T, "hidden": spec.d, "routed_experts": spec.E,
                    "top_k": spec.K, "inter": spec.I, "shared_experts": spec.S,
                    "shared_inter": spec.Is, "weights": "bf16", "output": "fp32",
-                   "parallelism": "single GPU"},
+                   "slots": layer.slot_dtype, "parallelism": "single GPU"},
         **spread(step_ms),
         "layer_TFLOPs": layer_tflops,
         "layer_frac_mfma_peak": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
@@ -719,6 +748,8 @@ def main():
                      "mfma_TFLOPs": achieved, "mfma_peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac": achieved / MFMA_BF16_PEAK_TFLOPS},
     }
+    log("[bench] the same step with bf16 slot rows")
+    result["bf16_slots"] = bf16_slots_measure(layer, x, bias, bufs, args.steps, args.warmup)
     plain_route = route_ms(layer, x, bias)
     result["route_ms"] = plain_route
     result["sequence_loads_ms"] = sequence_loads_ms(layer, spec, seq_len=4096)
@@ -726,9 +757,11 @@ def main():
     result["norm_residual"] = norm_residual_measure(layer, spec, x, bias, bufs, args.steps,
                                                     args.warmup)
     if not args.no_cpu_baseline:
-        log(f"[bench] oracle cpu baseline on {args.cpu_tokens} tokens")
+        n_cpu = spec.T if args.cpu_tokens is None else args.cpu_tokens
+        log(f"[bench] oracle cpu baseline on {n_cpu} tokens")
         result["cpu_baseline"], result["parity_sample"] = cpu_baseline(spec, inp, layer, bufs,
-                                                                       args.cpu_tokens)
+                                                                       n_cpu)
+        log(f"[bench] oracle {result['cpu_baseline']['sample']}; parity {result['parity_sample']}")
     del inp, layer, bufs
     torch.cuda.empty_cache()
     if not args.no_decode:
@@ -764,6 +797,9 @@ def main():
     result["roofline"]["clock_ghz"] = clock.get("v3_gate_up", {}).get("ghz")
     result["clock_counters"] = clock or None
     print(json.dumps(result), flush=True)
+    if not result.get("parity_sample", {"pass": True})["pass"]:
+        print("bench.py: the layer output does not match the oracle (parity_sample)", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -43,8 +43,9 @@
  *   - num_tokens == 0 is a no-op that returns MOE_OK (for moe_route the
  *     load vector is still zeroed).
  *   - `stream` is a hipStream_t passed as void* (0 = the null stream).
- *   - Activations (x, x_perm, out_slots) have the activation dtype of `cfg`
- *     (fp32 or bf16); the router weights have it too. The shared-expert
+ *   - Activations (x, x_perm, h) have the activation dtype of `cfg` (fp32 or
+ *     bf16); the router weights have it too. The routed slot rows out_slots
+ *     have cfg->slot_dtype (fp32 by default). The shared-expert
  *     output y_shared is always fp32 and the layer output y has
  *     cfg->out_dtype, so the sum of the shared and routed terms is formed
  *     and kept at fp32 accumulation precision. Expert weights have the weight dtype: fp32, bf16 (with
@@ -132,6 +133,11 @@ typedef struct moe_config {
                             = no group limit. Requires E % G == 0 and G <= 64.       */
   int32_t topk_groups;   /* M: groups kept per token (1..G, with M * E/G >= K); used
                             only when num_groups > 1.                                */
+  int32_t slot_dtype;    /* the gate-weighted routed rows out_slots: MOE_DTYPE_F32
+                            (0, the default: each routed term reaches the fp32 sum of
+                            moe_combine unrounded), or MOE_DTYPE_BF16 with bf16
+                            activations (half the bytes; each term then carries one
+                            bf16 rounding, up to 2^-8 of itself, into the sum). */
 } moe_config;
 
 /* Validate a configuration without touching the GPU. Returns a status code. */
@@ -231,7 +237,7 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
  * [E, I] and s2 [E, d] are the fp32 scales of each output row (the stored
  * code times the scale is the weight); they must be NULL otherwise.
  * x_perm, expert_offsets, perm_slot from moe_permute; topk_gate [T*K] from
- * moe_route; out_slots [T*K, d] act dtype. Accumulation is fp32; h is held
+ * moe_route; out_slots [T*K, d] slot dtype. Accumulation is fp32; h is held
  * in the activation dtype. Workspace: MOE_WS_FFN bytes. */
 int moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
                    const int32_t* perm_slot, const float* topk_gate,
@@ -279,7 +285,7 @@ int moe_shared_ffn(const moe_config* cfg, const void* x, const void* w1s, const 
  * x [T, d]; expert_offsets, perm_slot from moe_permute; topk_gate [T*K];
  * routed weights and scales as for moe_expert_ffn, shared ones as for
  * moe_shared_ffn (all NULL when num_shared == 0, y_shared too); out_slots
- * [T*K, d] act dtype; y_shared [T, d] fp32. bf16 activations only
+ * [T*K, d] slot dtype; y_shared [T, d] fp32. bf16 activations only
  * (MOE_ERR_DTYPE otherwise). Workspace: MOE_WS_EXPERTS bytes. */
 int moe_experts(const moe_config* cfg, const void* x, const int32_t* expert_offsets,
                 const int32_t* perm_slot, const float* topk_gate,
@@ -337,7 +343,7 @@ int moe_experts_down(const moe_config* cfg, const void* h, const void* hs,
  *   weight-block and token-tile scales), h = SiLU(g) * u in fp32, h
  *   quantised in 1 x 128 tiles exactly as moe_quantize_act does, then
  *   W2 h the same way; routed rows times their gate go to out_slots [T*K, d]
- *   (bf16), the shared experts' sum to y_shared [T, d] (fp32).
+ *   (slot dtype), the shared experts' sum to y_shared [T, d] (fp32).
  *   w13 / w13s: the MOE_PACK_GATE_UP tensors of W1, W3 (groups E / 1);
  *   w2 / w2s: the MOE_PACK_DOWN tensors; codes in both. Block scales (fp32):
  *   s1, s3 [E, I/128, d/128] of W1, W3 (block (i, j) covers rows 128i.. and
@@ -375,7 +381,7 @@ int moe_experts_fp8_down(const moe_config* cfg, const void* hq, const float* hs,
  *   y[t, :] = y_shared[t, :] + sum_{k=0..K-1} out_slots[t*K + k, :]
  * summed in fp32 in exactly this order (deterministic), rounded once to
  * cfg->out_dtype. y_shared may be NULL (then it counts as zero).
- * out_slots [T*K, d] act dtype; y_shared [T, d] fp32; y [T, d] out_dtype. */
+ * out_slots [T*K, d] slot dtype; y_shared [T, d] fp32; y [T, d] out_dtype. */
 int moe_combine(const moe_config* cfg, const void* out_slots, const void* y_shared,
                 void* y, void* stream);
 

@@ -71,6 +71,20 @@ int moe_peak_l2_read(const void* src, size_t region_bytes, int32_t blocks, int32
  * moe_peak_stream_read. */
 int moe_peak_stream_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream);
 
+/* Accuracy of the fp8 MFMA the fine-grained fp8 GEMMs use
+ * (v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3 codes, unit scales): for each
+ * of n problems p, D_p = A_p B_p^T + C_p with A_p = a[p] as [32 rows][64]
+ * E4M3 codes, B_p = b[p] as [32 columns][64] codes (2048 bytes each), C_p =
+ * c[p] and D_p = d[p] as [32][32] fp32, one instruction per problem. The
+ * caller compares D with the exact sums: fp8 GEMM accumulation inside the
+ * matrix unit keeps limited precision ("DeepSeekMoE架构解析" section 4.3,
+ * the reason its scheme promotes partial sums to fp32 every 128 elements),
+ * and the fine-grained fp8 parity check states the bound it assumes per
+ * instruction. a, b 16-byte aligned; codes 0x7F / 0xFF (NaN) give
+ * undefined results. MOE_ERR_NULL / MOE_ERR_SHAPE (n < 1, misaligned). */
+int moe_probe_fp8_mfma(const void* a, const void* b, const float* c, float* d, int32_t n,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

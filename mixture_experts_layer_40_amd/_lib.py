@@ -68,7 +68,7 @@ class moe_config(ctypes.Structure):
                 ("norm", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("weight_layout", ctypes.c_int32), ("num_groups", ctypes.c_int32),
-                ("topk_groups", ctypes.c_int32)]
+                ("topk_groups", ctypes.c_int32), ("slot_dtype", ctypes.c_int32)]
 
 
 RMS_EPS = 1e-6
@@ -81,23 +81,25 @@ _LA = {"rows": MOE_LAYOUT_ROWS, "tiled": MOE_LAYOUT_TILED}
 
 def make_config(T, d, E, K, I, S=0, Is=0, score="sigmoid", norm="selected", act_dtype="bf16",
                 weight_dtype="bf16", out_dtype="f32", weight_layout="rows", n_groups=0,
-                topk_groups=0) -> moe_config:
+                topk_groups=0, slot_dtype="f32") -> moe_config:
     return moe_config(int(T), int(d), int(E), int(K), int(I), int(S), int(Is),
                       _SC.get(score, score), _NO.get(norm, norm),
                       _DT.get(act_dtype, act_dtype), _DT.get(weight_dtype, weight_dtype),
                       _DT.get(out_dtype, out_dtype), _LA.get(weight_layout, weight_layout),
-                      int(n_groups), int(topk_groups))
+                      int(n_groups), int(topk_groups), _DT.get(slot_dtype, slot_dtype))
 
 
-def config_of(spec, T: Optional[int] = None, weight_layout: str = "rows") -> moe_config:
+def config_of(spec, T: Optional[int] = None, weight_layout: str = "rows",
+              slot_dtype: Optional[str] = None) -> moe_config:
     """moe_config from any object with the fields T, d, E, K, I, S, Is, score,
-    norm, act_dtype, weight_dtype (and optionally out_dtype, default fp32, and
-    n_groups / topk_groups, default no group limit), e.g. a workload
-    description."""
+    norm, act_dtype, weight_dtype (and optionally out_dtype and slot_dtype,
+    default fp32, and n_groups / topk_groups, default no group limit), e.g. a
+    workload description."""
     return make_config(spec.T if T is None else T, spec.d, spec.E, spec.K, spec.I, spec.S,
                        spec.Is, spec.score, spec.norm, spec.act_dtype, spec.weight_dtype,
                        getattr(spec, "out_dtype", "f32"), weight_layout,
-                       getattr(spec, "n_groups", 0), getattr(spec, "topk_groups", 0))
+                       getattr(spec, "n_groups", 0), getattr(spec, "topk_groups", 0),
+                       slot_dtype or getattr(spec, "slot_dtype", "f32"))
 
 
 _lib = None

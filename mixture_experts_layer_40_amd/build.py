@@ -12,6 +12,7 @@ feature, which is harmless.
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import glob
 import os
 import shutil
@@ -39,21 +40,38 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(srcs, path, verbose, extra_flags):
-    tmp = path + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-function",
-           f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp] + srcs + list(extra_flags or [])
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                     if "is not a recognized feature for this target" not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"{os.path.basename(path)} build failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
+    return res.returncode, out
+
+
+def _compile(srcs, path, verbose, extra_flags):
+    """Each source compiles to an object of its own, in parallel, then one
+    link step writes the shared object (replaced atomically)."""
+    flags = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"] + list(extra_flags or [])
+    tag = os.path.splitext(os.path.basename(path))[0]
+    objdir = os.path.join(ROOT, "_build", tag)
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
+    jobs = [[hipcc()] + flags + ["-c", s, "-o", o] for s, o in zip(srcs, objs)]
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), jobs))
+    for (rc, out), s in zip(results, srcs):
+        if rc != 0:
+            raise RuntimeError(f"{os.path.basename(s)} failed to compile:\n" + out)
+        if verbose and out.strip():
+            print(out)
+    tmp = path + ".tmp"
+    rc, out = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    if rc != 0:
+        raise RuntimeError(f"{os.path.basename(path)} link failed:\n" + out)
     os.replace(tmp, path)
     return path
 

@@ -75,6 +75,8 @@ int moe_validate(const moe_config* c) {
     return MOE_ERR_DTYPE;
   if (c->out_dtype != MOE_DTYPE_F32 && c->out_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
   if (c->act_dtype == MOE_DTYPE_F32 && c->out_dtype != MOE_DTYPE_F32) return MOE_ERR_DTYPE;
+  if (c->slot_dtype != MOE_DTYPE_F32 && c->slot_dtype != MOE_DTYPE_BF16) return MOE_ERR_DTYPE;
+  if (c->act_dtype == MOE_DTYPE_F32 && c->slot_dtype != MOE_DTYPE_F32) return MOE_ERR_DTYPE;
   if (c->weight_layout != MOE_LAYOUT_ROWS && c->weight_layout != MOE_LAYOUT_TILED)
     return MOE_ERR_SHAPE;
   if (c->weight_layout == MOE_LAYOUT_TILED && c->weight_dtype == MOE_DTYPE_F32)

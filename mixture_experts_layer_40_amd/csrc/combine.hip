@@ -17,9 +17,10 @@ namespace moe {
 
 namespace {
 
-// One thread per 8 consecutive features of one token: out_slots in the
-// activation dtype, y_shared fp32, y in the output dtype.
-template <bool SLOT_BF16, bool OUT_BF16>
+// One thread per 8 consecutive features of one token: out_slots in the slot
+// dtype, the residual in the activation dtype, y_shared fp32, y in the
+// output dtype.
+template <bool SLOT_BF16, bool RES_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ slots,
                                                       const float* __restrict__ ysh,
                                                       const void* __restrict__ res, int T, int K,
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ s
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
   if (res) {     // the residual stream (layer input), in the activation dtype
-    if (SLOT_BF16) {
+    if (RES_BF16) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(res) + t * d + c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -118,10 +119,14 @@ hipError_t launch_combine(const moe_config& c, const void* out_slots, const void
   const int64_t n = static_cast<int64_t>(T) * (d / 8);
   const dim3 grid(static_cast<unsigned>((n + 255) / 256)), block(256);
   const float* ysh = static_cast<const float*>(y_shared);
-  const bool sb = c.act_dtype == MOE_DTYPE_BF16, ob = c.out_dtype == MOE_DTYPE_BF16;
-  if (sb && ob) hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
-  else if (sb) hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
-  else hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
+  // fp32 activations come with fp32 slots and an fp32 output (moe_validate)
+  const bool sb = c.slot_dtype == MOE_DTYPE_BF16, ab = c.act_dtype == MOE_DTYPE_BF16;
+  const bool ob = c.out_dtype == MOE_DTYPE_BF16;
+  if (!ab) hipLaunchKernelGGL((combine_kernel<false, false, false>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
+  else if (sb && ob) hipLaunchKernelGGL((combine_kernel<true, true, true>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
+  else if (sb) hipLaunchKernelGGL((combine_kernel<true, true, false>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
+  else if (ob) hipLaunchKernelGGL((combine_kernel<false, true, true>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
+  else hipLaunchKernelGGL((combine_kernel<false, true, false>), grid, block, 0, s, out_slots, ysh, residual, T, K, d, y);
   return hipGetLastError();
 }
 

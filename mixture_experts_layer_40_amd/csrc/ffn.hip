@@ -74,7 +74,7 @@ struct GemmSet {
   const int32_t* perm_slot;   // down: row -> output row (null = identity)
   const float* gate;          // down: gate per output row (null = 1)
   void* out;                  // down output [slots, n]
-  int out_f32;                // down output is fp32 (else the activation dtype)
+  int out_f32;                // down output is fp32 (else bf16)
   int tiled;                  // weights in the tiled layout (wa only; see pack_tiles)
   // fine-grained fp8 (grouped_gemm_f8b): act holds E4M3 codes; sa / sb are
   // 128 x 128 block scales [E, n/128, kdim/128] of wa (W1 or W2) / W3
@@ -653,6 +653,7 @@ GemmSet routed_down(const moe_config& c, const Blocking& b, const void* h, const
   g.kdim = c.inter; g.n = c.hidden; g.nb = b.nb2;
   g.wstride = static_cast<int64_t>(c.hidden) * c.inter;
   g.perm_slot = perm_slot; g.gate = gate; g.out = out_slots;
+  g.out_f32 = c.slot_dtype == MOE_DTYPE_F32;
   g.tiled = tiled(c);
   return g;
 }
@@ -985,7 +986,7 @@ hipError_t launch_experts_fp8_down(const moe_config& c, const void* hq, const fl
     tiles += ((T + b.bm - 1) / b.bm) * bs.nb2;
   }
   a.s[a.nsets++] = f8b_down(c, b, hq, hs, expert_offsets, sched, c.inter, 0, perm_slot, topk_gate,
-                            w2, s2, out_slots, c.act_dtype == MOE_DTYPE_F32);
+                            w2, s2, out_slots, c.slot_dtype == MOE_DTYPE_F32);
   return run_f8b(kDown, b.bm, a, tiles, s);
 }
 

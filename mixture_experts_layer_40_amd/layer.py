@@ -35,7 +35,8 @@ _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 class MoELayer:
     def __init__(self, spec, weights: dict, max_tokens: Optional[int] = None,
                  shared_stream: bool = True, device=None, layout: Optional[str] = None,
-                 fused: Optional[bool] = None, pre_norm: bool = False, residual: bool = False):
+                 fused: Optional[bool] = None, pre_norm: bool = False, residual: bool = False,
+                 slot_dtype: Optional[str] = None):
         self.spec = spec
         self.device = torch.device(device) if device is not None else weights["wr"].device
         self.max_tokens = spec.T if max_tokens is None else max_tokens
@@ -48,6 +49,8 @@ class MoELayer:
         if self.fp8_block and (layout != "tiled" or not self.fused):
             raise ValueError("block-scaled fp8 experts run fused on the tiled layout")
         self.pre_norm, self.residual = pre_norm, residual
+        # out_slots: fp32 unless the workload (or the caller) asks for bf16
+        self.slot_dtype = slot_dtype or getattr(spec, "slot_dtype", "f32")
         self.w = dict(weights)
         if layout == "tiled":
             wd = spec.weight_dtype
@@ -58,7 +61,8 @@ class MoELayer:
                 self.w["w1s"] = L.pack_gate_up(weights["w1s"], weights["w3s"], wd)
                 self.w["w3s"] = None
                 self.w["w2s"] = L.pack_down(weights["w2s"], wd)
-        self.cfg_max = L.config_of(spec, T=self.max_tokens, weight_layout=layout)
+        self.cfg_max = L.config_of(spec, T=self.max_tokens, weight_layout=layout,
+                                   slot_dtype=self.slot_dtype)
         st = L.moe_validate(self.cfg_max)
         if st != L.MOE_OK:
             raise L.MoEError("MoELayer", st, L.moe_status_string(st))
@@ -70,7 +74,7 @@ class MoELayer:
         self.expert_offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         self.perm_slot = torch.empty((T * K,), dtype=torch.int32, device=dev)
         self.x_perm = torch.empty((T * K, d), dtype=self.act, device=dev)
-        self.out_slots = torch.empty((T * K, d), dtype=self.act, device=dev)
+        self.out_slots = torch.empty((T * K, d), dtype=_TORCH_DT[self.slot_dtype], device=dev)
         self.y_shared = torch.empty((T, d), dtype=torch.float32, device=dev) if spec.S > 0 else None
         self.y = torch.empty((T, d), dtype=_TORCH_DT[getattr(spec, "out_dtype", "f32")], device=dev)
         self.u = torch.empty((T, d), dtype=self.act, device=dev) if pre_norm else None
@@ -93,7 +97,7 @@ class MoELayer:
     def _cfg(self, T):
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens exceed the layer's buffers ({self.max_tokens})")
-        return L.config_of(self.spec, T=T, weight_layout=self.layout)
+        return L.config_of(self.spec, T=T, weight_layout=self.layout, slot_dtype=self.slot_dtype)
 
     def route(self, x, bias=None):
         T = x.shape[0]

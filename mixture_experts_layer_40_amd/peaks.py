@@ -31,7 +31,7 @@ FORMS = {
     "f32_fma": MOE_PEAK_FMA_F32,
 }
 EXPORTED = ("moe_peak_mfma", "moe_peak_mfma_flops", "moe_peak_stream_read",
-            "moe_peak_l2_read", "moe_peak_stream_copy")
+            "moe_peak_l2_read", "moe_peak_stream_copy", "moe_probe_fp8_mfma")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -58,6 +58,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_peak_l2_read.restype = ctypes.c_int
     lib.moe_peak_stream_copy.argtypes = [P, P, SZ, I32, P]
     lib.moe_peak_stream_copy.restype = ctypes.c_int
+    lib.moe_probe_fp8_mfma.argtypes = [P, P, P, P, I32, P]
+    lib.moe_probe_fp8_mfma.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -94,6 +96,17 @@ def moe_peak_l2_read(src: torch.Tensor, region_bytes: int, blocks: int, iters: i
 def moe_peak_stream_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks: int):
     _check("moe_peak_stream_copy", load_library().moe_peak_stream_copy(
         src.data_ptr(), dst.data_ptr(), nbytes, blocks, _stream()))
+
+
+def moe_probe_fp8_mfma(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor, d: torch.Tensor):
+    """D = A B^T + C by one fp8 MFMA per problem: a, b uint8 [n, 32, 64]
+    (E4M3 codes; b holds B's columns as rows), c, d fp32 [n, 32, 32]."""
+    n = a.shape[0]
+    for t, shape in ((a, (n, 32, 64)), (b, (n, 32, 64)), (c, (n, 32, 32)), (d, (n, 32, 32))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"moe_probe_fp8_mfma: expected a contiguous {shape} tensor")
+    _check("moe_probe_fp8_mfma", load_library().moe_probe_fp8_mfma(
+        a.data_ptr(), b.data_ptr(), c.data_ptr(), d.data_ptr(), n, _stream()))
 
 
 def _time_ms(call, reps: int) -> float:

@@ -213,6 +213,34 @@ double flops_of(int32_t blocks, int32_t iters) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// One v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit scales) per
+// wave: problem p reads A [32 rows][64] and B [32 columns][64] codes and
+// C [32][32] fp32 at its own offsets and writes D = A B^T + C. Lane l
+// supplies row / column l % 32, codes 32 (l / 32) .. +31 of each (the
+// layout of mfma_32x32x64_fp8); the result element 4i + j of lane l is
+// D[8i + 4(l / 32) + j][l % 32].
+__global__ __launch_bounds__(64) void fp8_mfma_once(const uint8_t* __restrict__ a,
+                                                    const uint8_t* __restrict__ b,
+                                                    const float* __restrict__ c,
+                                                    float* __restrict__ d) {
+  const int l = threadIdx.x, g = l >> 5, r = l & 31;
+  const size_t p = blockIdx.x;
+  const uint8_t* ap = a + p * 2048 + r * 64 + 32 * g;
+  const uint8_t* bp = b + p * 2048 + r * 64 + 32 * g;
+  const u32x4 a0 = *reinterpret_cast<const u32x4*>(ap), a1 = *reinterpret_cast<const u32x4*>(ap + 16);
+  const u32x4 b0 = *reinterpret_cast<const u32x4*>(bp), b1 = *reinterpret_cast<const u32x4*>(bp + 16);
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[4 * i + j] = c[p * 1024 + (8 * i + 4 * g + j) * 32 + r];
+  acc = mfma_32x32x64_fp8(a0, a1, b0, b1, acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[p * 1024 + (8 * i + 4 * g + j) * 32 + r] = acc[4 * i + j];
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -277,6 +305,16 @@ int moe_peak_stream_copy(const void* src, void* dst, size_t bytes, int32_t block
   hipLaunchKernelGGL(stream_copy, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads), 0,
                      reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                      static_cast<u32x4*>(dst), bytes / 16);
+  return status_of(hipGetLastError());
+}
+
+int moe_probe_fp8_mfma(const void* a, const void* b, const float* c, float* d, int32_t n,
+                       void* stream) {
+  if (!a || !b || !c || !d) return MOE_ERR_NULL;
+  if (n < 1 || !aligned16(a) || !aligned16(b)) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(fp8_mfma_once, dim3(static_cast<unsigned>(n)), dim3(64), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t*>(a),
+                     static_cast<const uint8_t*>(b), c, d);
   return status_of(hipGetLastError());
 }
 

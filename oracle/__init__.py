@@ -44,6 +44,7 @@ from .moe import (  # noqa: F401
     silu,
     swiglu_expert,
     route,
+    selection_valid,
     ExpertBank,
     layer_rows,
     bias_update,

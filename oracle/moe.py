@@ -232,6 +232,44 @@ def route(x: np.ndarray, wr: np.ndarray, bias: Optional[np.ndarray], K: int,
     return out
 
 
+def selection_valid(r: dict, idx: np.ndarray, K: int, groups: Optional[tuple] = None) -> np.ndarray:
+    """Which rows of another implementation's selection idx [T, K] the
+    routing r (from route(), same tokens) accepts. A set is accepted when it
+    holds K distinct experts and either equals the oracle's set, or the token
+    is a near-tie (r["near_tie"]) and the set is one the tie leaves open:
+    every chosen key within NEAR_TIE_GAP of the oracle's K-th key; with
+    node-limited routing (groups = (G, M)), at most M groups used, each with
+    an affinity within NEAR_TIE_GAP of the M-th largest, and every chosen key
+    within NEAR_TIE_GAP of the K-th largest key among the used groups'
+    experts. Returns a boolean vector [T]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    keys, sel, near = r["keys"], r["sel"], r["near_tie"]
+    T, E = keys.shape
+    inside = np.all((idx >= 0) & (idx < E), axis=1)
+    srt = np.sort(np.clip(idx, 0, E - 1), axis=1)
+    distinct = np.all(np.diff(srt, axis=1) > 0, axis=1) if K > 1 else np.ones(T, dtype=bool)
+    same = np.all(srt == np.sort(sel, axis=1), axis=1)
+    ok = inside & distinct & same
+    chosen = np.take_along_axis(keys, np.clip(idx, 0, E - 1), axis=1)
+    if groups is None or groups[0] <= 1:
+        kth = np.take_along_axis(keys, sel[:, K - 1:K], axis=1)[:, 0]
+        tie_ok = np.all(chosen >= kth[:, None] - NEAR_TIE_GAP, axis=1)
+    else:
+        G, M = groups
+        n = E // G
+        gs = r["group_scores"]
+        mth = -np.sort(-gs, axis=1)[:, M - 1]
+        tie_ok = np.zeros(T, dtype=bool)
+        for t in np.flatnonzero(near & inside & distinct):
+            used = np.unique(idx[t] // n)
+            if len(used) > M or np.any(gs[t, used] < mth[t] - NEAR_TIE_GAP):
+                continue
+            pool = keys[t, (used[:, None] * n + np.arange(n)[None, :]).ravel()]
+            kth_pool = np.sort(pool)[::-1][K - 1]
+            tie_ok[t] = bool(np.all(keys[t, idx[t]] >= kth_pool - NEAR_TIE_GAP))
+    return ok | (near & inside & distinct & tie_ok)
+
+
 @dataclass
 class ExpertBank:
     """Stored expert weights, decoded to float64 one expert at a time.

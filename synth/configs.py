@@ -36,6 +36,7 @@ class MoEConfig:
     act_dtype: str = "bf16"      # "f32" | "bf16"
     weight_dtype: str = "bf16"   # "f32" | "bf16" | "fp8"
     out_dtype: str = "f32"       # layer output y: "f32" | "bf16"
+    slot_dtype: str = "f32"      # gate-weighted routed rows out_slots: "f32" | "bf16"
     bias_range: Optional[float] = None   # None -> no bias tensor
     x_std: float = 1.0
     w_std: float = 0.02

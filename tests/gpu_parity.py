@@ -7,10 +7,10 @@ The bar (the tolerances of the layer's specification):
     those are counted and their GPU set must be valid within 1e-5;
   * permutation and offsets bit-exact (they are defined by the indices);
   * outputs: max |GPU - oracle| <= 2e-2 * RMS(oracle) for bf16/fp8 paths and
-    <= 1e-4 * RMS(oracle) for the fp32 path, beyond the rounding that
-    storing each routed slot row once in the activation dtype adds (at most
-    2^-8 of the slot in bf16, elementwise); near-tie tokens are compared
-    with the oracle evaluated on the GPU's selected set.
+    <= 1e-4 * RMS(oracle) for the fp32 path, elementwise over the layer
+    output y and the shared-expert output, with nothing added to the bar;
+    near-tie tokens are compared with the oracle evaluated on the GPU's
+    selected set.
 """
 
 from __future__ import annotations
@@ -97,31 +97,14 @@ def check_route(spec, r, idx, gate, load=None, rows=None):
         assert int(load.sum()) == idx.shape[0] * K, "a token was dropped"
     near = r["near_tie"]
     ok = ~near
-    mism = np.flatnonzero(np.any(srt[ok] != np.sort(r["sel"][ok], axis=1), axis=1))
-    assert mism.size == 0, f"{mism.size} non-near-tie tokens differ, e.g. {np.flatnonzero(ok)[mism[:5]]}"
+    # sets equal to the oracle's outside near-ties; inside them, one of the
+    # sets the tie leaves open (oracle.selection_valid)
+    valid = oracle.selection_valid(r, idx_r, K, groups_of(spec))
+    bad = np.flatnonzero(~valid)
+    assert bad.size == 0, (f"{bad.size} tokens have a selection the oracle does not accept, "
+                           f"e.g. {bad[:5]} (near-tie: {near[bad[:5]].tolist()})")
     assert np.array_equal(np.bincount(idx_r[ok].ravel(), minlength=E),
                           np.bincount(r["sel"][ok].ravel(), minlength=E))
-    keys = r["keys"]
-    kth = np.take_along_axis(keys, r["sel"][:, K - 1:K], axis=1)[:, 0]
-    chosen = np.take_along_axis(keys, idx_r, axis=1)
-    grp = groups_of(spec)
-    if near.any() and grp is None:
-        assert np.all(chosen[near] >= kth[near, None] - oracle.NEAR_TIE_GAP), "invalid near-tie selection"
-    elif near.any():
-        # node-limited: the GPU's experts come from at most M groups, each of
-        # them within the tolerance of the M-th group affinity, and they are
-        # the top K (within the tolerance) of the experts of the groups used
-        G, M = grp
-        n = E // G
-        gs = r["group_scores"]
-        mth = -np.sort(-gs, axis=1)[:, M - 1]
-        for t in np.flatnonzero(near):
-            used = np.unique(idx_r[t] // n)
-            assert len(used) <= M, "more than M groups used"
-            assert np.all(gs[t, used] >= mth[t] - oracle.NEAR_TIE_GAP), "invalid near-tie group"
-            pool = np.concatenate([np.arange(g * n, (g + 1) * n) for g in used])
-            kth_pool = np.sort(keys[t, pool])[::-1][K - 1]
-            assert np.all(keys[t, idx_r[t]] >= kth_pool - oracle.NEAR_TIE_GAP), "invalid near-tie selection"
     g_or = oracle.gate_values(r["scores"], idx_r, spec.norm)
     err = np.abs(gate_r - g_or).max()
     assert err <= GATE_ATOL, f"gate error {err}"
@@ -134,23 +117,27 @@ def check_permutation(spec, idx, offsets, perm):
     assert np.array_equal(perm, perm_or), "permutation differs"
 
 
-def rel_err(got, want, allowance=0.0):
-    """max(|got - want| - allowance) / RMS(want), and RMS(want)."""
+def rel_err(got, want):
+    """max |got - want| / RMS(want), and RMS(want)."""
     rms = float(np.sqrt(np.mean(want ** 2)))
-    return float((np.abs(got - want) - allowance).max()) / max(rms, 1e-300), rms
+    return float(np.abs(got - want).max()) / max(rms, 1e-300), rms
 
 
-# Relative rounding of one value stored in the activation dtype: bf16 keeps 8
-# significant bits (round to nearest: at most 2^-8 of the value), fp32 24.
+# Relative rounding of one value stored in a dtype: bf16 keeps 8 significant
+# bits (round to nearest: at most 2^-8 of the value), fp32 24.
 STORE_REL = {"bf16": 2.0 ** -8, "f32": 2.0 ** -24}
 
 
-def slot_storage_allowance(act_dtype, slots):
-    """Elementwise error that storing the K routed slot rows [.., K, d] once
-    in the activation dtype contributes to their sum: each is off by at most
-    STORE_REL of itself. (With one slot and no shared expert the output is a
-    single stored slot, so this rounding alone can reach 2^-8 max|y|.)"""
-    return STORE_REL[act_dtype] * np.abs(slots).sum(axis=-2)
+def check_slot_rows(osl, want, slot_dtype, tol):
+    """The routed slot rows [n, K, d] (an intermediate of the layer, held in
+    the slot dtype) against the oracle's gate-weighted expert outputs: each
+    (token, slot) row's error, beyond the element's own storage rounding in
+    the slot dtype, within tol of that row's RMS. Returns the worst ratio."""
+    rms_row = np.sqrt(np.mean(want ** 2, axis=2, keepdims=True))
+    excess = np.abs(osl - want) - STORE_REL[slot_dtype] * np.abs(want)
+    e_o = float((excess / np.maximum(rms_row, 1e-300)).max())
+    assert e_o <= tol, f"out_slots: {e_o:.3e}"
+    return e_o
 
 
 def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
@@ -175,8 +162,7 @@ def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
         # y = residual + expert sum: the error is measured against the
         # expert sum's own RMS (the residual itself enters exactly)
         y = y - residual[rows]
-    # the arithmetic error, beyond the rounding of the stored slot rows
-    e_y, rms = rel_err(y, y_or, slot_storage_allowance(spec.act_dtype, routed_or))
+    e_y, rms = rel_err(y, y_or)
     assert e_y <= tol, f"y: max err / RMS = {e_y:.3e} > {tol}"
     if spec.S > 0:
         ysh = oracle.decode_stored(host(layer.y_shared[trow].contiguous()))
@@ -190,14 +176,5 @@ def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
         aligned[i, og[i]] = routed_or[i, oo[i]]
     slot_rows = (trow[:, None] * K + torch.arange(K, device=x.device)[None, :]).reshape(-1)
     osl = oracle.decode_stored(host(layer.out_slots[slot_rows].contiguous())).reshape(len(rows), K, d)
-    # out_slots is an intermediate held in the activation dtype: each element
-    # also carries its own storage rounding (at most 2^-8 relative in bf16,
-    # 2^-24 in fp32) on top of the arithmetic budget of the output tolerance.
-    # Each (token, slot) row is one gate-scaled expert output, so its error
-    # is measured against that row's own RMS.
-    store = STORE_REL[spec.act_dtype]
-    rms_row = np.sqrt(np.mean(aligned ** 2, axis=2, keepdims=True))
-    excess = np.abs(osl - aligned) - store * np.abs(aligned)
-    e_o = float((excess / np.maximum(rms_row, 1e-300)).max())
-    assert e_o <= tol, f"out_slots: {e_o:.3e}"
-    return {"y_err": e_y, "y_rms": rms}
+    e_o = check_slot_rows(osl, aligned, layer.slot_dtype, tol)
+    return {"y_err": e_y, "y_rms": rms, "slot_err": e_o}

@@ -69,6 +69,9 @@ def test_validate_accepts_large_token_counts():
     (dict(out_dtype="bf16"), L.MOE_ERR_DTYPE),  # fp32 activations need an fp32 output
     (dict(out_dtype="fp8"), L.MOE_ERR_DTYPE),
     (dict(act_dtype="bf16", weight_dtype="bf16", out_dtype=5), L.MOE_ERR_DTYPE),
+    (dict(slot_dtype="bf16"), L.MOE_ERR_DTYPE),  # fp32 activations need fp32 slot rows
+    (dict(act_dtype="bf16", weight_dtype="bf16", slot_dtype="fp8"), L.MOE_ERR_DTYPE),
+    (dict(act_dtype="bf16", weight_dtype="bf16", slot_dtype=7), L.MOE_ERR_DTYPE),
     (dict(weight_layout=7), L.MOE_ERR_SHAPE),
     (dict(n_groups=3, topk_groups=1), L.MOE_ERR_SHAPE),      # E = 16 not a multiple of 3
     (dict(n_groups=4, topk_groups=0), L.MOE_ERR_SHAPE),
@@ -95,6 +98,8 @@ def test_validate_accepts_group_limits():
 
 def test_one_plus_norm_and_sequence_loads_validate():
     assert moe.moe_validate(_cfg(norm="one_plus")) == L.MOE_OK
+    for sd in ("f32", "bf16"):
+        assert moe.moe_validate(_cfg(act_dtype="bf16", weight_dtype="bf16", slot_dtype=sd)) == L.MOE_OK
     assert moe.moe_validate(_cfg(norm=3)) == L.MOE_ERR_SHAPE
     lib = moe.load_library()
     fake = ctypes.c_void_p(0x1000)

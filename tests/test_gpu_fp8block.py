@@ -1,16 +1,27 @@
 """Fine-grained fp8 experts ("DeepSeekMoE架构解析" section 4.3) against the
 oracle: moe_quantize_act bit-exact (codes and scales are decided in fp32 on
 both sides), and the layer through moe_quantize_act + moe_experts_fp8 with
-routing bit-exact up to near-ties and outputs within 2e-2 * RMS of the
-oracle's fp64 evaluation on the same quantised tokens and block-scaled
-weights. The intermediate h is quantised from each side's own value (fp32
-on the GPU, fp64 rounded to fp32 in the oracle), so an h code may differ by
-one step where the value sits near a rounding boundary. Such a code is an
-integer decided by floating point, checked like a routing near-tie: every
-differing code must be one the GPU can reach within the error bound of its
-fp8 MFMA accumulation (measured, see EPS_MFMA), and the outputs are
-compared with the oracle's down projection of the GPU's (validated) h
-codes."""
+routing bit-exact up to near-ties.
+
+The intermediate h is quantised from each side's own value (fp32 on the GPU
+from fp8 MFMA partial sums; float64 rounded to fp32 in the oracle), so an h
+code may differ by a step where the value sits near a rounding boundary: an
+integer decided by floating point, treated like a routing near-tie. Three
+comparisons:
+  * validity: every GPU h code the oracle does not produce lies within the
+    worst-case error window of its rounding interval, and every tile scale
+    within that window's effect; the window follows from the accuracy taken
+    per fp8 MFMA (EPS_MFMA, checked on the GPU by
+    test_fp8_mfma_accumulation_bound) and the oracle's operands;
+  * the outputs against the oracle's down projection of the GPU's
+    (validated) h codes, within 2e-2 x RMS (the down GEMM's arithmetic);
+  * the outputs against the oracle's own evaluation (its own h codes; no GPU
+    value on the expected side), within 2e-2 x RMS plus B: what the h codes
+    lying within the page's stated in-unit accumulation precision (about 14
+    bits) of a rounding boundary can move each output, one code range times
+    the scale, |W2| and the gate (an oracle-side quantity); at the full V3
+    shape also within the plain 2e-2 x RMS.
+"""
 
 import numpy as np
 import pytest
@@ -19,8 +30,8 @@ import torch
 import mixture_experts_layer_40_amd as moe
 import oracle
 import synth
-from gpu_parity import (STORE_REL, check_permutation, check_route, host, oracle_route, rel_err,
-                        run_steps, say, slot_storage_allowance)
+from gpu_parity import (check_permutation, check_route, check_slot_rows, host, oracle_route,
+                        rel_err, run_steps, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,28 +86,55 @@ CASES = {
     "two_shared": _cfg(T=200, d=384, E=16, K=4, I=128, S=2, Is=256),
 }
 
-# The fp8 MFMA of gfx950 (v_mfma_scale_f32_32x32x64_f8f6f4) aligns its 64
-# products and its C input to the largest before summing: measured on the
-# GPU, |error| <= 2^-12 (sum |a b| + |C|) per instruction (in-bounds probe,
-# random E4M3 codes of every binade; exact when the products share a
-# binade). The kernel sums each 128-wide block in two chained MFMAs from
-# zero and adds it to fp32 accumulators, so per block |error| <= 2 EPS
-# sum_block |x w|, EPS = 2^-11 leaving a factor 2 of margin.
+# Accuracy assumed of the fp8 MFMA. The page notes that fp8 GEMM
+# accumulation inside the matrix unit keeps only about 14 bits, which is why
+# its scheme promotes each 128-element partial sum to fp32. gfx950's
+# v_mfma_scale_f32_32x32x64_f8f6f4 aligns its products and C input to the
+# largest before summing; the bound taken per instruction is
+#   |D - (A B^T + C)| <= EPS_MFMA (sum_k |a_k b_k| + |C|),
+# which test_fp8_mfma_accumulation_bound checks on codes of every binade.
 EPS_MFMA = 2.0 ** -11
+U32 = 2.0 ** -24                      # fp32 unit roundoff
 _POS = oracle.E4M3_TABLE[:0x7F]
 
 
+def _g_bound(xd, w):
+    """|g_GPU - g| for g = xd @ w.T (float64 from the dequantised operands):
+    a 128-wide block is two chained MFMAs from zero, within
+    2 EPS (1 + EPS) sum_block |x w|; each block is then promoted by one fp32
+    product of the two scales and one fp32 FMA into the accumulator, within
+    2^-24 of the scaled block and of the running sum, <= 2 nb 2^-24 (1 + 3 EPS)
+    sum |x w| over the nb blocks."""
+    S = np.abs(xd) @ np.abs(w).T
+    nb = xd.shape[1] // 128
+    return (2 * EPS_MFMA * (1 + EPS_MFMA) + 2 * nb * U32 * (1 + 3 * EPS_MFMA)) * S
+
+
 def _h_bound(xd, w1, w3):
-    """Bound on |h_GPU - h_oracle| per element for dequantised tokens xd and
-    expert weights w1, w3 (float64): the MFMA bound on g and u, carried
-    through h = SiLU(g) u (|SiLU'| <= 1.1), plus the GPU's own fp32
-    rounding of g, u and h."""
-    ax = np.abs(xd)
+    """|h_GPU - h| per element for h = SiLU(g) u, g = xd w1^T, u = xd w3^T:
+    the bounds on g and u carried through SiLU (|SiLU'| <= 1.1) and the
+    product, plus the GPU's own evaluation of SiLU (fp32 exp and division)
+    and of the product, within 2^-20 of the value."""
     g, u = xd @ w1.T, xd @ w3.T
-    dg = 2 * EPS_MFMA * (ax @ np.abs(w1).T) + 2.0 ** -22 * np.abs(g)
-    du = 2 * EPS_MFMA * (ax @ np.abs(w3).T) + 2.0 ** -22 * np.abs(u)
-    sg = np.abs(oracle.silu(g))
-    return 1.1 * dg * (np.abs(u) + du) + sg * du + 2.0 ** -22 * sg * np.abs(u)
+    dg, du = _g_bound(xd, w1), _g_bound(xd, w3)
+    sg, au = np.abs(oracle.silu(g)), np.abs(u)
+    return 1.1 * dg * (au + du) + sg * du + 2.0 ** -20 * (sg + 1.1 * dg) * (au + du)
+
+
+# In-unit accumulation precision the page states for fp8 GEMMs: about 14
+# bits ("DeepSeekMoE架构解析" section 4.3). Read as: each sum the matrix unit
+# forms is within 2^-14 of the magnitudes it accumulates, so g and u are
+# within 2^-14 sum |x w| of their exact values.
+PAGE_BITS = 14
+
+
+def _h_page(xd, w1, w3):
+    """The page's precision carried to h = SiLU(g) u, to first order:
+    2^-14 (1.1 sum|x w1| |u| + |SiLU(g)| sum|x w3|), from the oracle's own
+    operands."""
+    g, u = xd @ w1.T, xd @ w3.T
+    s1, s3 = np.abs(xd) @ np.abs(w1).T, np.abs(xd) @ np.abs(w3).T
+    return 2.0 ** -PAGE_BITS * (1.1 * s1 * np.abs(u) + np.abs(oracle.silu(g)) * s3)
 
 
 def _code_interval(c):
@@ -109,31 +147,111 @@ def _code_interval(c):
     return np.where(neg, -hi, lo), np.where(neg, -lo, hi)
 
 
-def _check_h(gq, gs, h32, dh, counts):
-    """The GPU's quantised h rows against the oracle's h (fp32 values before
-    quantisation) and the bound dh on their difference: each tile scale
-    within the bound the max-abs can move (dh max / 448); codes equal,
-    except where the oracle's scaled value q lies within the bound of the
-    GPU code's rounding interval. Returns the oracle's codes and scales."""
+def _window(h32, dh):
+    """The oracle's quantisation of h (fp32 [n, C]) and what the GPU's may
+    differ by, from dh (bound on |h_GPU - h|, float64): returns (codes,
+    scales, dq, ds, delta) with dq the bound on the scaled value the code is
+    decided from, ds the bound on each tile scale, and delta the bound on
+    |h_GPU dequantised - h_oracle dequantised| per element: the codes
+    reachable within dq of the oracle's scaled value (rounding is monotone)
+    times the scale, plus the scale's own bound times the code."""
     oq, os_ = oracle.quantize_tiles(h32)
     n, C = h32.shape
-    ds = dh.reshape(n, C // 128, 128).max(axis=2) / 448.0 + 2.0 ** -23 * os_
+    h64 = h32.astype(np.float64)
+    dh = dh + U32 * np.abs(h64)                      # the oracle's own rounding to fp32
+    ds = dh.reshape(n, C // 128, 128).max(axis=2) / 448.0 * (1 + U32) + 2 * U32 * os_
+    sf = np.repeat(os_.astype(np.float64), 128, axis=1)
+    dsf = np.repeat(ds, 128, axis=1)
+    q = (h64 / sf).astype(np.float32).astype(np.float64)      # the oracle's decision input
+    dq = (dh + np.abs(q) * dsf) / (sf - dsf) * (1 + 4 * U32) + 4 * U32 * np.abs(q)
+    val = oracle.E4M3_TABLE
+    c_lo = oracle.e4m3_encode(np.clip(q - dq, -448.0, 448.0))
+    c_hi = oracle.e4m3_encode(np.clip(q + dq, -448.0, 448.0))
+    v0 = val[oq]
+    dval = np.maximum(np.abs(val[c_lo] - v0), np.abs(val[c_hi] - v0))
+    vmax = np.maximum(np.abs(val[c_lo]), np.abs(val[c_hi]))
+    delta = dval * (sf + dsf) + vmax * dsf
+    return oq, os_, dq, ds, delta, c_lo != c_hi
+
+
+def _check_h(gq, gs, h32, dh, dh_page, counts):
+    """The GPU's quantised h rows against the oracle's window (_window) for
+    dh, the bound on |h_GPU - h| that EPS_MFMA implies: each tile scale within
+    its bound; codes equal, except where the oracle's scaled value lies
+    within dq of the GPU code's rounding interval. Returns the oracle's
+    codes and scales and, for the window the page's accumulation precision
+    gives (dh_page), the per-element bound on what the GPU's dequantised h
+    may differ by."""
+    oq, os_, dq, ds, _, _ = _window(h32, dh)
+    _, _, _, _, delta, cand = _window(h32, dh_page)
     assert np.all(np.abs(gs.astype(np.float64) - os_) <= ds), "an h tile scale is outside its bound"
     diff = gq != oq
     counts[0] += int(diff.sum())
     counts[1] += diff.size
+    counts[2] += int(cand.sum())
+    counts[3] += int((diff & ~cand).sum())
     if diff.any():
-        sf = np.repeat(os_.astype(np.float64), 128, axis=1)
-        dsf = np.repeat(ds, 128, axis=1)
-        q = h32.astype(np.float64) / sf
-        dq = (dh + np.abs(q) * dsf) / (sf - dsf)
+        q = (h32.astype(np.float64) / np.repeat(os_.astype(np.float64), 128, axis=1))
         lo, hi = _code_interval(gq[diff])
         dist = np.maximum(0.0, np.maximum(lo - q[diff], q[diff] - hi))
         worst = int(np.argmax(dist / dq[diff]))
         assert np.all(dist <= dq[diff]), (
             f"an h code is outside the accumulation bound: GPU {int(gq[diff][worst])}, "
             f"oracle {int(oq[diff][worst])}, q {q[diff][worst]:.6g}, bound {dq[diff][worst]:.3g}")
-    return oq, os_
+    return oq, os_, delta
+
+
+def _codes(rng, shape, lo_exp=0, hi_exp=15):
+    """Random finite E4M3 codes with exponent fields in [lo_exp, hi_exp]
+    (0 = zero and subnormals, 15 = up to 448), random signs and mantissas."""
+    e = rng.integers(lo_exp, hi_exp + 1, size=shape)
+    m = rng.integers(0, 8, size=shape)
+    m = np.where(e == 15, np.minimum(m, 6), m)          # 0x7F / 0xFF are NaN
+    sgn = rng.integers(0, 2, size=shape)
+    return ((sgn << 7) | (e << 3) | m).astype(np.uint8)
+
+
+def test_fp8_mfma_accumulation_bound():
+    """The accuracy EPS_MFMA assumes of v_mfma_scale_f32_32x32x64_f8f6f4
+    (one instruction per problem through moe_probe_fp8_mfma): |D - (A B^T +
+    C)| <= EPS_MFMA (sum |a b| + |C|) against the exact sums (every product
+    of two E4M3 values, and every sum here, is exact in float64: products
+    are multiples of 2^-18 below 2^18, C a float32 of magnitude >= 2^-4 or
+    zero). Cases: codes of every binade with C = 0 (the first MFMA of a
+    block) and with C the size of such a sum (the second), codes of a few
+    neighbouring binades (the tile-scaled data of the GEMMs), and products
+    of one binade."""
+    from mixture_experts_layer_40_amd import peaks as pk
+    rng = np.random.default_rng(20260211)
+    n = 512
+    cases = {
+        "every binade, C = 0": (_codes(rng, (n, 32, 64)), _codes(rng, (n, 32, 64)), 0.0),
+        "every binade, C ~ sum": (_codes(rng, (n, 32, 64)), _codes(rng, (n, 32, 64)), 1.0),
+        "binades 10..15, C ~ sum": (_codes(rng, (n, 32, 64), 10), _codes(rng, (n, 32, 64), 10), 1.0),
+        "one binade, C = 0": (_codes(rng, (n, 32, 64), 7, 7), _codes(rng, (n, 32, 64), 7, 7), 0.0),
+    }
+    worst = 0.0
+    for name, (a, b, cmag) in cases.items():
+        av, bv = oracle.E4M3_TABLE[a], oracle.E4M3_TABLE[b]
+        prod = av @ np.swapaxes(bv, 1, 2)                            # [n, 32, 32], exact
+        mag = np.abs(av) @ np.swapaxes(np.abs(bv), 1, 2)
+        c = np.zeros((n, 32, 32), dtype=np.float32)
+        if cmag:
+            c = (rng.standard_normal((n, 32, 32)) * mag.mean()).astype(np.float32)
+            c = np.where(np.abs(c) < 2.0 ** -4, np.float32(2.0 ** -4), c).astype(np.float32)
+        d = torch.empty((n, 32, 32), dtype=torch.float32, device="cuda")
+        pk.moe_probe_fp8_mfma(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(),
+                              torch.from_numpy(c).cuda(), d)
+        torch.cuda.synchronize()
+        exact = prod + c.astype(np.float64)
+        err = np.abs(d.cpu().numpy().astype(np.float64) - exact)
+        denom = mag + np.abs(c)
+        assert np.all(err[denom == 0] == 0)
+        ratio = err / np.maximum(denom, 1e-300)
+        worst = max(worst, float(ratio.max()))
+        say(f"[fp8 mfma] {name}: max |err| / (sum |a b| + |C|) = 2^{np.log2(max(ratio.max(), 1e-300)):.2f}")
+        assert np.all(ratio <= EPS_MFMA), f"{name}: 2^{np.log2(ratio.max()):.2f} > EPS_MFMA"
+    say(f"[fp8 mfma] worst 2^{np.log2(max(worst, 1e-300)):.2f}, assumed 2^{np.log2(EPS_MFMA):.0f}")
 
 
 def _split_calls(layer, spec):
@@ -161,10 +279,12 @@ def _split_calls(layer, spec):
             None if hsq is None else hsq.cpu().numpy(), None if hss is None else hss.cpu().numpy())
 
 
-def _layer_check(spec, inp, rows=None):
+def _layer_check(spec, inp, rows=None, plain_pure=False):
     """Routing bit-exact up to near-ties; the quantised tokens bit-exact; h
     codes validated (_check_h); the outputs against the oracle's down
-    projection of the GPU's validated h codes, within 2e-2 x RMS."""
+    projection of the GPU's validated h codes within 2e-2 x RMS, and against
+    the oracle's own evaluation within 2e-2 x RMS + B (plain 2e-2 x RMS too
+    when plain_pure)."""
     layer, res = run_steps(spec, inp, bias=inp.get("bias"))
     r, _ = oracle_route(spec, inp["x"], inp["wr"], inp.get("bias"))
     n_near = check_route(spec, r, res["idx"], res["gate"], res["load"])
@@ -180,18 +300,22 @@ def _layer_check(spec, inp, rows=None):
     gate = oracle.gate_values(r["scores"][rows], gpu_idx, spec.norm)   # GPU slot order
     pos = np.empty(T * K, dtype=np.int64)
     pos[res["perm"]] = np.arange(T * K)                 # slot -> row of hq
-    counts = [0, 0]
+    counts = [0, 0, 0, 0]
     routed = np.zeros((len(rows), K, d))
     pure = np.zeros((len(rows), K, d))                  # the oracle with its own h codes
+    bound = np.zeros((len(rows), d))                    # B: what the window can move y by
     for e in np.unique(gpu_idx):
         ri, ks = np.nonzero(gpu_idx == e)
         w1, w3, w2 = bank.expert(int(e))
         h32 = oracle.expert_h_fp8(xq[ri], xs[ri], w1, w3)
         p = pos[rows[ri] * K + ks]
-        dh = _h_bound(oracle.dequantize_tiles(xq[ri], xs[ri]), w1, w3)
-        oq, os_ = _check_h(hq[p], hs[p], h32, dh, counts)
-        routed[ri, ks] = gate[ri, ks][:, None] * (oracle.dequantize_tiles(hq[p], hs[p]) @ w2.T)
-        pure[ri, ks] = gate[ri, ks][:, None] * (oracle.dequantize_tiles(oq, os_) @ w2.T)
+        xd = oracle.dequantize_tiles(xq[ri], xs[ri])
+        oq, os_, delta = _check_h(hq[p], hs[p], h32, _h_bound(xd, w1, w3), _h_page(xd, w1, w3),
+                                  counts)
+        g = gate[ri, ks][:, None]
+        routed[ri, ks] = g * (oracle.dequantize_tiles(hq[p], hs[p]) @ w2.T)
+        pure[ri, ks] = g * (oracle.dequantize_tiles(oq, os_) @ w2.T)
+        np.add.at(bound, ri, np.abs(g) * (delta @ np.abs(w2).T))
     y_sh = np.zeros((len(rows), d))
     y_sh_pure = np.zeros((len(rows), d))
     if spec.S > 0:
@@ -199,28 +323,36 @@ def _layer_check(spec, inp, rows=None):
         W1, W3, W2 = (np.concatenate(m, axis=a) for m, a in
                       zip(zip(*bank.shared_experts()), (0, 0, 1)))
         h32 = oracle.expert_h_fp8(xq, xs, W1, W3)
-        dh = _h_bound(oracle.dequantize_tiles(xq, xs), W1, W3)
-        oq, os_ = _check_h(hsq[rows], hss[rows], h32, dh, counts)
+        xd = oracle.dequantize_tiles(xq, xs)
+        oq, os_, delta = _check_h(hsq[rows], hss[rows], h32, _h_bound(xd, W1, W3),
+                                  _h_page(xd, W1, W3), counts)
         y_sh = oracle.dequantize_tiles(hsq[rows], hss[rows]) @ W2.T
         y_sh_pure = oracle.dequantize_tiles(oq, os_) @ W2.T
+        bound += delta @ np.abs(W2).T
         assert SI % 128 == 0
         e_s, _ = rel_err(layer.y_shared[torch.as_tensor(rows, device="cuda")].double().cpu().numpy(), y_sh)
         assert e_s <= TOL, f"y_shared: {e_s:.3e}"
     trow = torch.as_tensor(rows, device="cuda")
     y_or = y_sh + routed.sum(axis=1)
     y = res["y"][trow].double().cpu().numpy()
-    e_y, rms = rel_err(y, y_or, slot_storage_allowance("bf16", routed))
-    assert e_y <= TOL, f"y: max err / RMS = {e_y:.3e}"
+    e_y, rms = rel_err(y, y_or)
+    assert e_y <= TOL, f"y against the down projection of the GPU's h codes: {e_y:.3e}"
     slot_rows = (trow[:, None] * K + torch.arange(K, device="cuda")[None, :]).reshape(-1)
     osl = layer.out_slots[slot_rows].double().cpu().numpy().reshape(len(rows), K, d)
-    rms_row = np.sqrt(np.mean(routed ** 2, axis=2, keepdims=True))
-    excess = np.abs(osl - routed) - STORE_REL["bf16"] * np.abs(routed)
-    e_o = float((excess / np.maximum(rms_row, 1e-300)).max())
-    assert e_o <= TOL, f"out_slots: {e_o:.3e}"
-    e_pure, _ = rel_err(y, y_sh_pure + pure.sum(axis=1))
-    say(f"[fp8b] h codes within the accumulation bound of a boundary: {counts[0]} of {counts[1]}; "
-        f"y err / RMS {e_y:.2e} (against the oracle's own h codes: {e_pure:.2e})")
-    return n_near, e_y
+    check_slot_rows(osl, routed, layer.slot_dtype, TOL)
+    # the oracle's own evaluation: no GPU value on the expected side
+    y_pure = y_sh_pure + pure.sum(axis=1)
+    e_pure, rms_pure = rel_err(y, y_pure)
+    excess = float(((np.abs(y - y_pure) - bound) / rms_pure).max())
+    b_rel = float(bound.max() / rms_pure)
+    say(f"[fp8b] h codes: {counts[0]} of {counts[1]} differ from the oracle's, {counts[2]} lie "
+        f"within the page's accumulation precision of a rounding boundary ({counts[3]} differing codes "
+        f"outside it); y err / RMS {e_y:.2e} (GPU codes), {e_pure:.2e} (oracle's own codes; "
+        f"B <= {b_rel:.2e} x RMS, excess over B {excess:.2e})")
+    assert excess <= TOL, f"y against the oracle's own evaluation: {excess:.3e} x RMS beyond B"
+    if plain_pure:
+        assert e_pure <= TOL, f"y against the oracle's own evaluation: {e_pure:.3e} x RMS"
+    return n_near, e_y, e_pure
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -228,8 +360,8 @@ def test_fp8_block_layer_matches_oracle(name):
     spec = CASES[name]
     say(f"[fp8b] {name}")
     inp = synth.make_inputs(spec, "cuda")
-    n_near, e_y = _layer_check(spec, inp)
-    say(f"[fp8b] {name}: near-ties={n_near} y_err/rms={e_y:.3e}")
+    n_near, e_y, e_pure = _layer_check(spec, inp)
+    say(f"[fp8b] {name}: near-ties={n_near} y_err/rms={e_y:.3e} (oracle's own codes {e_pure:.3e})")
 
 
 @pytest.mark.timeout(600)
@@ -238,5 +370,5 @@ def test_fullsize_v3_fp8_block():
     inp = synth.make_inputs(spec, "cuda")
     rng = np.random.default_rng(0)
     rows = np.sort(rng.choice(spec.T, 10, replace=False))
-    n_near, e_y = _layer_check(spec, inp, rows=rows)
-    say(f"[fp8b] full V3: near-ties={n_near} y_err/rms={e_y:.3e}")
+    n_near, e_y, e_pure = _layer_check(spec, inp, rows=rows, plain_pure=True)
+    say(f"[fp8b] full V3: near-ties={n_near} y_err/rms={e_y:.3e} (oracle's own codes {e_pure:.3e})")

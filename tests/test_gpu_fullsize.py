@@ -2,9 +2,12 @@
 benchmark times (MoELayer.forward through the C ABI).
 
 Routing (indices, gates, loads) and the permutation are compared on every
-token; the gathered rows on the device; the layer output on sampled tokens
-the oracle computes one by one (token outputs are independent), always
-including near-tie tokens when there are any.
+token; the gathered rows on the device. The layer output is compared on
+every token for the tiny-to-V3 workloads of the specification (the 2024
+layout, the V3 prefill batch, the V3 decode batch), and for the others on
+the tokens that own the first and the last row of every token tile of every
+expert (the grouped GEMMs' split of each expert's rows), so every expert and
+every ragged tile tail is seen, plus a few random tokens and the near-ties.
 """
 
 import gc
@@ -32,12 +35,49 @@ def _sample_rows(T, n, near, seed=0):
     return np.array(sorted(rows))
 
 
-@pytest.mark.timeout(300)
-@pytest.mark.parametrize("name,n_rows", [("dsmoe2024_bf16", 96), ("v3_prefill_bf16", 12),
-                                         ("v3_decode_fp8", 16), ("v3_grouped_bf16", 12),
-                                         ("v3_ep8_shard_bf16", 12)])
-def test_fullsize_layer(name, n_rows):
+def _tile_bm(rows_per_expert):
+    """Token-tile height the grouped GEMMs pick for this many expected rows
+    per expert (32 / 64 / 128 / 256)."""
+    for bm in (32, 64, 128):
+        if rows_per_expert <= bm:
+            return bm
+    return 256
+
+
+def _tile_edge_tokens(offsets, perm, K, E, T):
+    """Tokens owning the first and the last row of every token tile of every
+    expert: an expert's m rows are split into ceil(m / bm) tiles of equal
+    height (a multiple of 32 rows), the last one ragged."""
+    bm = _tile_bm(-(-T * K // E))
+    toks = set()
+    for e in range(E):
+        m = int(offsets[e + 1] - offsets[e])
+        if m == 0:
+            continue
+        mt = -(-m // bm)
+        per = ((-(-m // mt)) + 31) & ~31
+        for j in range(mt):
+            for p in (j * per, min(m, (j + 1) * per) - 1):
+                toks.add(int(perm[offsets[e] + p]) // K)
+    return toks
+
+
+def _coverage_rows(res, spec, r, n_random=12):
+    toks = _tile_edge_tokens(res["offsets"], res["perm"], spec.K, spec.E, spec.T)
+    toks.update(_sample_rows(spec.T, n_random, r["near_tie"]).tolist())
+    return np.array(sorted(toks))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,coverage", [("dsmoe2024_bf16", "all"), ("v3_prefill_bf16", "all"),
+                                           ("v3_decode_fp8", "all"), ("v3_grouped_bf16", "tiles"),
+                                           ("v3_ep8_shard_bf16", "tiles"),
+                                           ("v3_prefill_bf16:bf16_slots", "tiles")])
+def test_fullsize_layer(name, coverage):
+    name, _, variant = name.partition(":")
     spec = synth.get_config(name)
+    if variant == "bf16_slots":          # the routed slot rows held in bf16
+        spec = synth.scaled_config(name, name=name + "_bf16_slots", slot_dtype="bf16")
     say(f"[full] {name}: generating inputs")
     inp = synth.make_inputs(spec, "cuda")
     layer, res = run_steps(spec, inp, bias=inp["bias"], side_stream=True)
@@ -48,23 +88,26 @@ def test_fullsize_layer(name, n_rows):
     layer.permute(layer._cfg(spec.T), inp["x"])      # the row gather, checked on its own
     perm = torch.as_tensor(res["perm"], device="cuda")
     assert torch.equal(layer.x_perm[:spec.T * spec.K], inp["x"][perm // spec.K])
-    rows = _sample_rows(spec.T, n_rows, r["near_tie"])
-    say(f"[full] {name}: near-ties={n_near}, oracle outputs for {len(rows)} tokens")
+    rows = None if coverage == "all" else _coverage_rows(res, spec, r)
+    n_rows = spec.T if rows is None else len(rows)
+    say(f"[full] {name}: near-ties={n_near}, oracle outputs for {n_rows} tokens ({coverage})")
     out = check_outputs(spec, layer, inp, res, r, rows=rows)
     load = res["load"]
-    say(f"[full] {name}: y err/rms={out['y_err']:.3e} active experts={int((load > 0).sum())} "
+    say(f"[full] {name}: y err/rms={out['y_err']:.3e} slot err/rms={out['slot_err']:.3e} "
+        f"({layer.slot_dtype} slots) over {n_rows} tokens; active experts={int((load > 0).sum())} "
         f"load max/mean={load.max() / load.mean():.2f}")
     del layer, inp, res
     _free()
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_fullsize_zipf_trajectory():
     """20 batches of the skewed-load workload, each followed by
     moe_bias_update: the bias after every step is bit-identical to the
     oracle's step from the same loads; routing is checked on every token of
-    the first and last batch and on a sample of the others; layer outputs on
-    sampled tokens of the first batch."""
+    the first and last batch and on a sample of the others; layer outputs of
+    the first batch on the tokens owning the first and last row of every
+    token tile (the hottest expert's tail included)."""
     spec = synth.get_config("zipf_stress_bf16")
     say("[zipf] generating weights")
     inp = synth.make_inputs(spec, "cuda")
@@ -86,11 +129,14 @@ def test_fullsize_zipf_trajectory():
         r, _ = oracle_route(spec, x, inp["wr"], bias, rows=trows)
         near_total += check_route(spec, r, idx, gate, load, rows=rows)
         if bt == 0:
-            res = {"idx": idx, "y": layer.y[:spec.T]}
-            check_permutation(spec, idx, layer.expert_offsets.cpu().numpy().astype(np.int64),
-                              layer.perm_slot.cpu().numpy().astype(np.int64))
-            out = check_outputs(spec, layer, inp, res, r, x=x, rows=_sample_rows(spec.T, 8, r["near_tie"]))
-            say(f"[zipf] batch 0 y err/rms={out['y_err']:.3e}")
+            res = {"idx": idx, "y": layer.y[:spec.T],
+                   "offsets": layer.expert_offsets.cpu().numpy().astype(np.int64),
+                   "perm": layer.perm_slot.cpu().numpy().astype(np.int64)}
+            check_permutation(spec, idx, res["offsets"], res["perm"])
+            rows = _coverage_rows(res, spec, r, n_random=8)
+            out = check_outputs(spec, layer, inp, res, r, x=x, rows=rows)
+            say(f"[zipf] batch 0 y err/rms={out['y_err']:.3e} over {len(rows)} tokens (every "
+                f"tile's first and last row; hottest expert {int(load.max())} rows)")
         layer.bias_update(bias)
         torch.cuda.synchronize()
         want = oracle.bias_update(b_before, load)

@@ -61,7 +61,7 @@ def test_split_fused_entry_points_equal_moe_experts():
     T, TK, SI = spec.T, spec.T * spec.K, spec.S * spec.Is
     h = torch.empty((TK, spec.I), dtype=torch.bfloat16, device="cuda")
     hs = torch.empty((T, SI), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((TK, spec.d), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((TK, spec.d), dtype=layer.out_slots.dtype, device="cuda")
     ysh = torch.empty((T, spec.d), dtype=torch.float32, device="cuda")
     moe.moe_experts_gate_up(cfg, inp["x"], layer.expert_offsets, layer.perm_slot[:TK], w["w1"],
                             w["w3"], w.get("s1"), w.get("s3"), w["w1s"], w["w3s"], w.get("s1s"),

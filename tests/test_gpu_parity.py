@@ -59,6 +59,13 @@ CASES = {
                             n_groups=4, topk_groups=2),
     "grouped_m1": _cfg("v3_prefill_bf16", T=150, d=128, E=32, K=4, I=64, Is=64,
                        n_groups=4, topk_groups=1),
+    # the routed slot rows held in bf16 (half their bytes) instead of fp32
+    "v3_gemm_bf16_slots": _cfg("v3_prefill_bf16", T=1000, d=1024, E=32, K=4, I=384, Is=256,
+                               slot_dtype="bf16"),
+    "dsmoe_bf16_slots": _cfg("dsmoe2024_bf16", T=300, d=256, E=64, K=6, I=192, Is=128,
+                             slot_dtype="bf16"),
+    "fp8_bf16_slots": _cfg("v3_decode_fp8", T=700, d=256, E=16, K=4, I=192, S=2, Is=64,
+                           slot_dtype="bf16"),
     # the "1 + sum" gate weighting, split-K and fused (with node-limited) routers
     "oneplus": _cfg("v3_prefill_bf16", T=400, d=256, E=64, K=6, I=128, Is=128, norm="one_plus"),
     "oneplus_grouped_fused": _cfg("v3_grouped_bf16", T=4096, d=128, E=256, K=8, I=64, Is=64,
@@ -110,7 +117,7 @@ def test_split_entry_points_equal_expert_ffn():
     TK = spec.T * spec.K
     layer.permute(layer._cfg(spec.T), inp["x"])        # fill x_perm
     h = torch.empty((TK, spec.I), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((TK, spec.d), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((TK, spec.d), dtype=layer.out_slots.dtype, device="cuda")
     moe.moe_expert_gate_up(cfg, layer.x_perm[:TK], layer.expert_offsets, inp["w1"], inp["w3"], None, None, h)
     moe.moe_expert_down(cfg, h, layer.expert_offsets, layer.perm_slot[:TK], layer.topk_gate, inp["w2"], None, out)
     torch.cuda.synchronize()

@@ -420,6 +420,38 @@ def test_near_tie_flag_threshold():
     assert (gap < oracle.NEAR_TIE_GAP).tolist() == [False, True]
 
 
+def _route_keys(keys, K, groups=None):
+    """A route() result whose scores are the given keys (no bias): logits =
+    logit(keys), identity router."""
+    keys = np.asarray(keys, dtype=np.float64)
+    return oracle.route(np.log(keys / (1.0 - keys)), np.eye(keys.shape[1]), None, K, "sigmoid",
+                        "selected", groups=groups)
+
+
+def test_selection_valid_accepts_only_the_open_sets_of_a_near_tie():
+    # token 0: a clear top-2 {0, 1}; token 1: 2nd and 3rd keys 5e-6 apart
+    # (a near-tie: {0, 1} and {0, 2} are both correct, {0, 3} is not)
+    r = _route_keys([[0.9, 0.7, 0.5, 0.3], [0.9, 0.7, 0.7 - 5e-6, 0.3]], 2)
+    assert r["near_tie"].tolist() == [False, True]
+    v = lambda idx: oracle.selection_valid(r, np.array(idx), 2).tolist()
+    assert v([[0, 1], [0, 1]]) == [True, True]
+    assert v([[1, 0], [2, 0]]) == [True, True]          # order is free; the tie's other set
+    assert v([[0, 2], [0, 3]]) == [False, False]        # not near: must equal; 0.3 is not within 1e-5
+    assert v([[0, 0], [0, 0]]) == [False, False]        # an expert twice
+    assert v([[0, 4], [0, -1]]) == [False, False]       # out of range
+
+
+def test_selection_valid_node_limited_near_tie():
+    # groups of 2 with sums 1.0, 1.0 - 2e-6, 0.3 and M = 1: the kept group is
+    # group 0 in the oracle, group 1 within the tolerance
+    r = _route_keys([[0.5, 0.5, 0.25, 0.75 - 2e-6, 0.1, 0.2]], 2, groups=(3, 1))
+    assert r["near_tie"][0]
+    v = lambda idx: bool(oracle.selection_valid(r, np.array([idx]), 2, groups=(3, 1))[0])
+    assert v([0, 1]) and v([2, 3])
+    assert not v([1, 3])                                # two groups used with M = 1
+    assert not v([4, 5])                                # group 2 is 0.7 below the kept one
+
+
 # ---- node-limited (group-limited) routing ("DeepSeekMoE架构解析" section 2.3) ----
 
 def _rand_route_inputs(rng, T, E, d=16):

@@ -16,7 +16,7 @@ ROOT = Path(__file__).resolve().parents[1]
 
 def test_exports_every_declared_symbol():
     header = (ROOT / "include" / "moe_peaks.h").read_text()
-    declared = set(re.findall(r"^(?:int|double)\s+(moe_peak_\w+)\(", header, re.M))
+    declared = set(re.findall(r"^(?:int|double)\s+(moe_(?:peak|probe)_\w+)\(", header, re.M))
     assert declared == set(pk.EXPORTED)
     lib = pk.load_library()
     for name in declared:
@@ -66,3 +66,8 @@ def test_bad_arguments_are_rejected_on_the_host():
     assert cp(fake, odd, 16, 1, None) == L.MOE_ERR_SHAPE
     assert cp(fake, ctypes.c_void_p(0x1010), 32, 1, None) == L.MOE_ERR_SHAPE   # overlap
     assert cp(fake, ctypes.c_void_p(0x2000), 40, 1, None) == L.MOE_ERR_SHAPE
+    pr = lib.moe_probe_fp8_mfma
+    assert pr(None, fake, fake, fake, 1, None) == L.MOE_ERR_NULL
+    assert pr(fake, fake, fake, None, 1, None) == L.MOE_ERR_NULL
+    assert pr(fake, fake, fake, fake, 0, None) == L.MOE_ERR_SHAPE
+    assert pr(odd, fake, fake, fake, 1, None) == L.MOE_ERR_SHAPE
