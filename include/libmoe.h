@@ -72,6 +72,8 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED  4  /* valid request this build does not implement  */
 #define MOE_ERR_WORKSPACE    5  /* workspace NULL or smaller than required      */
 #define MOE_ERR_HIP          6  /* the HIP runtime reported a launch error      */
+#define MOE_ERR_SCRATCH      7  /* needs more than moe_permute_noalloc's fixed
+                                   scratch array holds                         */
 
 /* ---- enums --------------------------------------------------------------- */
 #define MOE_SCORE_SIGMOID 0  /* s = sigmoid(u^T e_i), per expert ([DSMoE] eq. 15)          */
@@ -224,6 +226,26 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
 int moe_permute(const moe_config* cfg, const int32_t* topk_idx, const void* x,
                 int32_t* expert_offsets, int32_t* perm_slot, void* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---- moe_permute_noalloc --------------------------------------------------
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: moe_permute
+ * with the same arguments, results and kernels, minus the workspace. The
+ * counting sort's per-chunk histogram lives in a fixed 1 MiB device array
+ * inside the library instead (each GPU the library runs on holds its own
+ * copy until the process ends; its address is looked up once per device on
+ * the first call there). That bounds the request to moe_workspace_size(cfg,
+ * MOE_WS_PERMUTE) <= 1 MiB, i.e. ceil(T*K / 4096) * E <= 262144 (T*K up to
+ * 4,194,304 pairs at E = 256); a larger one returns MOE_ERR_SCRATCH before
+ * anything is enqueued. Nothing in the array needs clearing between calls
+ * (every entry a call reads was written earlier in the same call), and the
+ * call allocates nothing. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (on different streams) race and must be
+ * ordered by the caller. MOE_ERR_HIP if the device address cannot be
+ * found. */
+int moe_permute_noalloc(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                        int32_t* expert_offsets, int32_t* perm_slot, void* x_perm,
+                        void* stream);
 
 /* ---- moe_expert_ffn -------------------------------------------------------
  * The routed SwiGLU experts ([DSMoE] section 1: fine-grained experts of

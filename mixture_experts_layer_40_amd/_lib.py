@@ -25,6 +25,7 @@ MOE_ERR_DTYPE = 3
 MOE_ERR_UNSUPPORTED = 4
 MOE_ERR_WORKSPACE = 5
 MOE_ERR_HIP = 6
+MOE_ERR_SCRATCH = 7
 
 MOE_SCORE_SIGMOID = 0
 MOE_SCORE_SOFTMAX = 1
@@ -51,7 +52,7 @@ EXPORTED = ("moe_validate", "moe_workspace_size", "moe_status_string", "moe_rout
             "moe_shared_ffn", "moe_combine", "moe_bias_update", "moe_pack_weights",
             "moe_experts", "moe_experts_gate_up", "moe_experts_down", "moe_sequence_loads",
             "moe_rmsnorm", "moe_combine_residual", "moe_quantize_act", "moe_experts_fp8",
-            "moe_experts_fp8_gate_up", "moe_experts_fp8_down")
+            "moe_experts_fp8_gate_up", "moe_experts_fp8_down", "moe_permute_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -125,6 +126,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_route.argtypes = [CFG, P, P, P, P, P, P, P, SZ, P]
     lib.moe_permute.argtypes = [CFG, P, P, P, P, P, P, SZ, P]
+    lib.moe_permute_noalloc.argtypes = [CFG, P, P, P, P, P, P]
     lib.moe_expert_ffn.argtypes = [CFG, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_expert_gate_up.argtypes = [CFG, P, P, P, P, P, P, P, P, SZ, P]
     lib.moe_expert_down.argtypes = [CFG, P, P, P, P, P, P, P, P, SZ, P]
@@ -146,7 +148,8 @@ def load_library(path: str = LIB_PATH):
                "moe_expert_down", "moe_shared_ffn", "moe_combine", "moe_bias_update",
                "moe_pack_weights", "moe_experts", "moe_experts_gate_up", "moe_experts_down",
                "moe_sequence_loads", "moe_rmsnorm", "moe_combine_residual", "moe_quantize_act",
-               "moe_experts_fp8", "moe_experts_fp8_gate_up", "moe_experts_fp8_down"):
+               "moe_experts_fp8", "moe_experts_fp8_gate_up", "moe_experts_fp8_down",
+               "moe_permute_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -210,6 +213,14 @@ def moe_permute(cfg, topk_idx, x, expert_offsets, perm_slot, x_perm, ws=None, st
     _check("moe_permute", load_library().moe_permute(
         ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(expert_offsets), _ptr(perm_slot),
         _ptr(x_perm), _ptr(wsb), nbytes, _stream(stream)))
+
+
+def moe_permute_noalloc(cfg, topk_idx, x, expert_offsets, perm_slot, x_perm, stream=None):
+    """moe_permute with its workspace in the library's fixed scratch array
+    (for callers that cannot allocate)."""
+    _check("moe_permute_noalloc", load_library().moe_permute_noalloc(
+        ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(expert_offsets), _ptr(perm_slot),
+        _ptr(x_perm), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, x_perm, expert_offsets, perm_slot, topk_gate, w1, w3, w2, s1, s3, s2,

@@ -133,6 +133,9 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: not implemented";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, too small or misaligned";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: the HIP runtime reported an error";
+    case MOE_ERR_SCRATCH:
+      return "MOE_ERR_SCRATCH: the request needs more than the 1 MiB scratch array of "
+             "moe_permute_noalloc";
     default: return "unknown libmoe status";
   }
 }

@@ -327,3 +327,23 @@ def test_package_never_imports_the_oracle():
     p = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
                        timeout=300)
     assert p.returncode == 0, p.stderr
+
+
+def test_permute_noalloc_rejects_more_than_its_scratch_on_the_host():
+    """moe_permute_noalloc (for callers that cannot allocate) takes the
+    counting sort's histogram from a fixed 1 MiB array: a request whose
+    workspace would exceed it is refused before any device call, the ones
+    at the limit pass validation, and the usual argument checks apply."""
+    lib = moe.load_library()
+    fake = ctypes.c_void_p(0x10000)
+    big = _cfg(act_dtype="bf16", weight_dtype="bf16", T=1 << 20, K=8, E=256)   # 2048 chunks x 256
+    assert moe.moe_workspace_size(big, L.MOE_WS_PERMUTE) > (1 << 20)
+    assert lib.moe_permute_noalloc(ctypes.byref(big), fake, None, fake, fake, None, None) == L.MOE_ERR_SCRATCH
+    edge = _cfg(act_dtype="bf16", weight_dtype="bf16", T=1 << 19, K=8, E=256)   # 1024 x 256 x 4 B
+    assert moe.moe_workspace_size(edge, L.MOE_WS_PERMUTE) == (1 << 20)
+    assert lib.moe_permute_noalloc(ctypes.byref(edge), None, None, fake, fake, None, None) == L.MOE_ERR_NULL
+    assert lib.moe_permute_noalloc(ctypes.byref(edge), fake, None, fake, ctypes.c_void_p(0x10008),
+                                   None, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_permute_noalloc(ctypes.byref(_cfg(K=0)), fake, None, fake, fake, None, None) == L.MOE_ERR_SHAPE
+    assert lib.moe_permute_noalloc(ctypes.byref(edge), fake, None, None, fake, None, None) == L.MOE_ERR_NULL
+    assert moe.moe_status_string(L.MOE_ERR_SCRATCH).startswith("MOE_ERR_SCRATCH")
