@@ -87,6 +87,7 @@ struct GemmSet {
 struct GemmArgs {
   GemmSet s[2];
   int nsets;
+  const int32_t* xb;  // [kNumXcd + 1] first tile of each XCD's range (see ffn_schedule), or null
 };
 
 struct Tile {
@@ -97,16 +98,8 @@ __device__ __forceinline__ int set_tiles(const GemmSet& g, int bm) {
   return g.offsets ? g.sched[g.E] : ((g.fixed_m + bm - 1) / bm) * g.nb;
 }
 
-// Decode this block's tile; false when the block has no work.
-__device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) {
-  const int n0 = set_tiles(a.s[0], bm);
-  const int total = n0 + (a.nsets > 1 ? set_tiles(a.s[1], bm) : 0);
-  bool valid;
-  int tile = xcd_contiguous(blockIdx.x, total, valid);
-  if (!valid) return false;
-  t.set = tile < n0 ? 0 : 1;
-  if (t.set) tile -= n0;
-  const GemmSet& g = a.s[t.set];
+// Tile `tile` of one set: its expert, row range and weight block.
+__device__ __forceinline__ void decode_set_tile(const GemmSet& g, int bm, int tile, Tile& t) {
   int e = 0, local = tile, rbeg = 0, m = g.fixed_m;
   if (g.offsets) {
     int lo = 0, hi = g.E - 1;  // largest e with sched[e] <= tile
@@ -129,6 +122,37 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) 
   t.nblk = local / mt;
   t.row0 = rbeg + mb * per;
   t.mvalid = min(per, m - mb * per);
+}
+
+// Decode this block's tile; false when the block has no work. Block b runs
+// on XCD x = b % 8 (blocks are dealt to the XCDs in turn) as the j-th block
+// (j = b / 8) of that XCD, and takes the j-th tile of XCD x's range of the
+// launch's tiles (set 0's, then set 1's), so the tiles that share a weight
+// block run together on one L2. With a.xb the ranges are those ffn_schedule
+// balanced by estimated cost; else each set is cut into 8 equal slices,
+// XCD x taking slice x of set 0 and then slice x of set 1.
+__device__ __forceinline__ bool decode_tile(const GemmArgs& a, int bm, Tile& t) {
+  const int n0 = set_tiles(a.s[0], bm);
+  const int n1 = a.nsets > 1 ? set_tiles(a.s[1], bm) : 0;
+  const int x = blockIdx.x % kNumXcd, j = blockIdx.x / kNumXcd;
+  int tile;
+  if (a.xb) {
+    tile = a.xb[x] + j;
+    if (tile >= a.xb[x + 1]) return false;
+  } else {
+    const int p0 = (n0 + kNumXcd - 1) / kNumXcd, p1 = (n1 + kNumXcd - 1) / kNumXcd;
+    const int c0 = min(max(n0 - x * p0, 0), p0);     // set-0 tiles of this XCD
+    if (j < c0) {
+      tile = x * p0 + j;
+    } else {
+      const int k = j - c0;
+      if (k >= p1 || x * p1 + k >= n1) return false;
+      tile = n0 + x * p1 + k;
+    }
+  }
+  t.set = tile < n0 ? 0 : 1;
+  if (t.set) tile -= n0;
+  decode_set_tile(a.s[t.set], bm, tile, t);
   return true;
 }
 
@@ -479,27 +503,123 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(GemmArgs args) {
   }
 }
 
-// Tile schedule of one grouped GEMM from the expert row offsets (one block):
-// sched[e] = first tile of expert e, sched[E] = total tiles.
+// Estimated cost of a tile, in K stages times (kStageWeight + token
+// fragments): each stage streams the tile's weight rows whatever its token
+// count, then runs one MFMA chain per 32-token fragment. Measured at the V3
+// prefill shape, a one-fragment tile took 105 us (gate/up) and 34 us (down)
+// against 184 and 72 us for eight fragments; 7 sits between the two.
+constexpr int kStageWeight = 7;
+
+// One grouped launch's tile table: its routed set's nb weight blocks per
+// token tile and nk K stages, its shared set's nbs and nks (nbs = 0: no
+// shared set), the blocks each XCD has in the launch (cap), and where the
+// table goes: out[e] = the first routed tile of expert e, out[E] = routed
+// tiles, then out[E + 1 + x] (x = 0 .. kNumXcd) = the first tile of XCD x's
+// range in the launch's sequence (shared tiles first, then routed).
+struct SchedSpec {
+  int nb, nk, nbs, nks, cap;
+  int32_t* out;
+};
+
+// Token tiles of an expert with m rows (split as decode_set_tile does) and
+// the cost of one weight block over all of them, in the units above.
+__device__ __forceinline__ void tile_row_cost(int m, int bm, int& mt, int& ntf, int& cost) {
+  mt = (m + bm - 1) / bm;
+  ntf = 0;
+  cost = 0;
+  if (mt == 0) return;
+  const int per = (((m + mt - 1) / mt) + 31) & ~31;
+  ntf = per / 32;
+  const int ntl = (m - (mt - 1) * per + 31) / 32;
+  cost = (mt - 1) * (kStageWeight + ntf) + (kStageWeight + ntl);
+}
+
+// Tile tables of up to two grouped launches over the same expert rows (one
+// block; E <= 256): per expert its first tile, and the launch's tiles cut
+// into kNumXcd contiguous ranges of about equal estimated cost, so that no
+// XCD is left with more work than the others (the blocks of an XCD take its
+// range in order). A range never exceeds the blocks an XCD has in the
+// launch, so every tile is covered.
 __global__ __launch_bounds__(256) void ffn_schedule(const int32_t* __restrict__ offsets, int E,
-                                                    int bm, int nb, int32_t* __restrict__ sched) {
-  __shared__ int sc[256];
+                                                    int bm, int T, SchedSpec s1, SchedSpec s2) {
+  __shared__ int mt_[256], ntf_[256], rc_[256], before_[256];
+  __shared__ long long csum[256];
+  __shared__ int bound[kNumXcd + 1];
   const int tid = threadIdx.x;
-  int mine = 0;
-  if (tid < E) {
-    const int m = offsets[tid + 1] - offsets[tid];
-    mine = ((m + bm - 1) / bm) * nb;
-  }
-  sc[tid] = mine;
+  int mt = 0, ntf = 0, rc = 0;
+  if (tid < E) tile_row_cost(offsets[tid + 1] - offsets[tid], bm, mt, ntf, rc);
+  mt_[tid] = mt;
+  ntf_[tid] = ntf;
+  rc_[tid] = rc;
+  before_[tid] = mt;
   __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int v = tid >= o ? sc[tid - o] : 0;
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive scan of token tiles
+    const int v = tid >= o ? before_[tid - o] : 0;
     __syncthreads();
-    sc[tid] += v;
+    before_[tid] += v;
     __syncthreads();
   }
-  if (tid < E) sched[tid] = sc[tid] - mine;
-  if (tid == 0) sched[E] = sc[255];
+  const int all_mt = before_[255];
+  before_[tid] -= mt;                   // token tiles of the experts before this one
+  __syncthreads();
+  int mts = 0, ntfs = 0, rcs = 0;
+  tile_row_cost(T, bm, mts, ntfs, rcs);
+  for (int k = 0; k < 2; ++k) {
+    const SchedSpec& sp = k == 0 ? s1 : s2;
+    if (!sp.out) break;
+    if (tid < E) sp.out[tid] = before_[tid] * sp.nb;
+    if (tid == 0) sp.out[E] = all_mt * sp.nb;
+    csum[tid] = static_cast<long long>(sp.nb) * rc * sp.nk;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive scan of expert costs
+      const long long v = tid >= o ? csum[tid - o] : 0;
+      __syncthreads();
+      csum[tid] += v;
+      __syncthreads();
+    }
+    const int n_sh = sp.nbs > 0 ? mts * sp.nbs : 0;
+    const long long c_sh = sp.nbs > 0 ? static_cast<long long>(sp.nbs) * rcs * sp.nks : 0;
+    const int n_all = n_sh + all_mt * sp.nb;
+    const long long c_all = c_sh + csum[255];
+    if (tid >= 1 && tid < kNumXcd) {
+      const long long tau = c_all * tid / kNumXcd;
+      int bx;
+      if (tau < c_sh) {
+        bx = static_cast<int>(tau * n_sh / c_sh);        // shared tiles cost about the same
+      } else {
+        const long long r = tau - c_sh;
+        int lo = 0, hi = E - 1;                          // first expert whose inclusive cost > r
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (csum[mid] > r) hi = mid; else lo = mid + 1;
+        }
+        const int e = lo;
+        const long long q = r - (e > 0 ? csum[e - 1] : 0);
+        const long long row = static_cast<long long>(rc_[e]) * sp.nk;
+        int rows = row > 0 ? static_cast<int>(q / row) : 0;
+        rows = min(rows, sp.nb - 1);
+        const long long rem = q - rows * row;
+        const long long stc = static_cast<long long>(kStageWeight + ntf_[e]) * sp.nk;
+        const int j = max(0, min(mt_[e] - 1, static_cast<int>(stc > 0 ? rem / stc : 0)));
+        bx = n_sh + before_[e] * sp.nb + rows * mt_[e] + j;
+      }
+      bound[tid] = bx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int prev = 0;
+      sp.out[E + 1] = 0;
+      for (int x = 1; x < kNumXcd; ++x) {
+        const int lo = max(prev, n_all - (kNumXcd - x) * sp.cap);
+        const int hi = min(prev + sp.cap, n_all);
+        const int bx = min(max(bound[x], lo), hi);
+        sp.out[E + 1 + x] = bx;
+        prev = bx;
+      }
+      sp.out[E + 1 + kNumXcd] = n_all;
+    }
+    __syncthreads();
+  }
 }
 
 // Rows -> tiled weight layout (a pure relocation of 16-byte pieces).
@@ -545,9 +665,10 @@ __global__ __launch_bounds__(256) void pack_tiles(const uint8_t* __restrict__ a,
   }
 }
 
-int64_t grid_for(int64_t max_tiles) {
-  const int64_t per = (max_tiles + kNumXcd - 1) / kNumXcd;
-  return per * kNumXcd;
+// Blocks of a grouped launch whose sets have at most n0 and n1 tiles: every
+// XCD takes up to ceil(n0 / 8) + ceil(n1 / 8) of them (see decode_tile).
+int64_t grid_for(int64_t n0, int64_t n1 = 0) {
+  return kNumXcd * ((n0 + kNumXcd - 1) / kNumXcd + (n1 + kNumXcd - 1) / kNumXcd);
 }
 
 // Token-tile size for a group: the smallest of 32 / 64 / 128 / 256 that covers
@@ -594,9 +715,10 @@ void launch_mfma(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
   }
 }
 
-hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int64_t max_tiles,
-                    hipStream_t s) {
-  const int64_t grid = grid_for(max_tiles);
+// n0, n1: bounds on the tiles of the launch's first and second set.
+hipError_t run_gemm(int mode, bool f32, bool fp8, int bm, const GemmArgs& a, int64_t n0,
+                    int64_t n1, hipStream_t s) {
+  const int64_t grid = grid_for(n0, n1);
   if (grid <= 0) return hipSuccess;
   const dim3 gd(static_cast<unsigned>(grid)), bd(256);
   if (f32) {
@@ -679,14 +801,45 @@ GemmSet shared_down(const moe_config& c, const Blocking& b, const void* hs, cons
   return g;
 }
 
-hipError_t schedule(const int32_t* offsets, int E, int bm, int nb, int32_t* sched, hipStream_t s) {
-  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, offsets, E, bm, nb, sched);
+hipError_t schedule(const int32_t* offsets, int E, int bm, int T, const SchedSpec& s1,
+                    hipStream_t s, const SchedSpec& s2 = SchedSpec{0, 0, 0, 0, 0, nullptr}) {
+  hipLaunchKernelGGL(ffn_schedule, dim3(1), dim3(256), 0, s, offsets, E, bm, T, s1, s2);
   return hipGetLastError();
+}
+
+// Blocks per XCD of a launch with at most n0 and n1 tiles in its two sets.
+int xcd_cap(int64_t n0, int64_t n1) {
+  return static_cast<int>((n0 + kNumXcd - 1) / kNumXcd + (n1 + kNumXcd - 1) / kNumXcd);
 }
 
 int64_t routed_max_tiles(const moe_config& c, int bm, int nb) {
   const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
   return ((TK + bm - 1) / bm + c.num_experts) * nb;
+}
+
+// The tiles of a grouped launch (the shared expert's first, when it has one;
+// bs is then its blocking, with the routed token tile b.bm) and the spec of
+// its tile table, which ffn_schedule writes to `sched`.
+struct LaunchTiles {
+  int64_t n_shared, n_routed;  // bounds on the tiles of the two sets
+  SchedSpec spec;
+};
+
+LaunchTiles launch_tiles(const moe_config& c, const Blocking& b, const Blocking* bs, int mode,
+                         int32_t* sched) {
+  const int T = c.num_tokens, SI = c.num_shared * c.shared_inter;
+  LaunchTiles l{};
+  const int nb = mode == kGateUp ? b.nb1 : b.nb2;
+  l.n_routed = routed_max_tiles(c, b.bm, nb);
+  int nbs = 0;
+  if (bs) {
+    nbs = mode == kGateUp ? bs->nb1 : bs->nb2;
+    l.n_shared = static_cast<int64_t>((T + b.bm - 1) / b.bm) * nbs;
+  }
+  const int nk = (mode == kGateUp ? c.hidden : c.inter) / 64;
+  const int nks = (mode == kGateUp ? c.hidden : SI) / 64;
+  l.spec = SchedSpec{nb, nk, nbs, nks, xcd_cap(l.n_shared, l.n_routed), sched};
+  return l;
 }
 
 // ---- fine-grained fp8 (grouped_gemm_f8b) -----------------------------------
@@ -700,8 +853,8 @@ void launch_f8b_bm(int bm, dim3 gd, hipStream_t s, const GemmArgs& a) {
   }
 }
 
-hipError_t run_f8b(int mode, int bm, const GemmArgs& a, int64_t max_tiles, hipStream_t s) {
-  const int64_t grid = grid_for(max_tiles);
+hipError_t run_f8b(int mode, int bm, const GemmArgs& a, int64_t n0, int64_t n1, hipStream_t s) {
+  const int64_t grid = grid_for(n0, n1);
   if (grid <= 0) return hipSuccess;
   const dim3 gd(static_cast<unsigned>(grid));
   if (mode == kGateUp) launch_f8b_bm<kGateUp>(bm, gd, s, a);
@@ -762,15 +915,19 @@ int64_t grouped_tiles_bound(const moe_config& c) {
     const int64_t mts = (T + bs.bm - 1) / bs.bm;
     for (int down = 0; down < 2; ++down) {
       const int64_t nb = down ? b.nb2 : b.nb1, nbs = down ? bs.nb2 : bs.nb1;
-      int64_t tiles = (TK / b.bm + E + 1) * nb;                 // routed bound (as routed_max_tiles)
-      if (c.num_shared > 0) tiles += std::max(mt * nbs, mts * nbs);
-      m = std::max(m, grid_for(tiles));
+      const int64_t routed = (TK / b.bm + E + 1) * nb;          // routed bound (as routed_max_tiles)
+      const int64_t shared = c.num_shared > 0 ? std::max(mt * nbs, mts * nbs) : 0;
+      m = std::max(m, grid_for(shared, routed));
     }
   }
   return m;
 }
 
-size_t sched_ws_bytes(const moe_config& c) { return align_up(static_cast<size_t>(c.num_experts + 1) * 4, 256); }
+// The tile table of a grouped launch: E + 1 tile starts and the kNumXcd + 1
+// XCD range starts.
+size_t sched_ws_bytes(const moe_config& c) {
+  return align_up(static_cast<size_t>(c.num_experts + 1 + kNumXcd + 1) * 4, 256);
+}
 
 size_t h_bytes(const moe_config& c) {
   return align_up(static_cast<size_t>(c.num_tokens) * c.top_k * c.inter * elem_bytes(c), 256);
@@ -783,7 +940,7 @@ size_t shared_ws_bytes(const moe_config& c) {
 }
 
 size_t experts_ws_bytes(const moe_config& c) {
-  return h_bytes(c) + (c.num_shared > 0 ? shared_ws_bytes(c) : 0) + sched_ws_bytes(c);
+  return h_bytes(c) + (c.num_shared > 0 ? shared_ws_bytes(c) : 0) + 2 * sched_ws_bytes(c);
 }
 
 hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t* expert_offsets,
@@ -794,12 +951,14 @@ hipError_t launch_gate_up(const moe_config& c, const void* x_perm, const int32_t
   if (TK == 0) return hipSuccess;
   const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb1, sched, s);
+  const LaunchTiles lt = launch_tiles(c, b, nullptr, kGateUp, sched);
+  hipError_t err = schedule(expert_offsets, E, b.bm, c.num_tokens, lt.spec, s);
   if (err != hipSuccess) return err;
   GemmArgs a{};
   a.nsets = 1;
   a.s[0] = routed_gate_up(c, b, x_perm, nullptr, expert_offsets, sched, w1, w3, s1, s3, h);
-  return run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a, routed_max_tiles(c, b.bm, b.nb1), s);
+  a.xb = sched + E + 1;
+  return run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a, lt.n_routed, 0, s);
 }
 
 hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert_offsets,
@@ -810,12 +969,14 @@ hipError_t launch_down(const moe_config& c, const void* h, const int32_t* expert
   if (TK == 0) return hipSuccess;
   const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb2, sched, s);
+  const LaunchTiles lt = launch_tiles(c, b, nullptr, kDown, sched);
+  hipError_t err = schedule(expert_offsets, E, b.bm, c.num_tokens, lt.spec, s);
   if (err != hipSuccess) return err;
   GemmArgs a{};
   a.nsets = 1;
   a.s[0] = routed_down(c, b, h, expert_offsets, sched, perm_slot, topk_gate, w2, s2, out_slots);
-  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a, routed_max_tiles(c, b.bm, b.nb2), s);
+  a.xb = sched + E + 1;
+  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a, lt.n_routed, 0, s);
 }
 
 hipError_t launch_expert_ffn(const moe_config& c, const void* x_perm,
@@ -842,12 +1003,12 @@ hipError_t launch_shared_ffn(const moe_config& c, const void* x, const void* w1s
   GemmArgs a1{};
   a1.nsets = 1;
   a1.s[0] = shared_gate_up(c, b, x, w1s, w3s, s1s, s3s, ws);
-  hipError_t err = run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a1, mt * b.nb1, s);
+  hipError_t err = run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a1, mt * b.nb1, 0, s);
   if (err != hipSuccess) return err;
   GemmArgs a2{};
   a2.nsets = 1;
   a2.s[0] = shared_down(c, b, ws, w2s, s2s, y_shared);
-  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a2, mt * b.nb2, s);
+  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a2, mt * b.nb2, 0, s);
 }
 
 // Shared and routed experts in one gate/up and one down launch (shared tiles
@@ -857,47 +1018,43 @@ hipError_t launch_experts_gate_up(const moe_config& c, const void* x,
                                   const void* w1, const void* w3, const float* s1,
                                   const float* s3, const void* w1s, const void* w3s,
                                   const float* s1s, const float* s3s, void* h, void* hs,
-                                  void* ws, hipStream_t s) {
+                                  void* ws, hipStream_t s, bool scheduled) {
   const int E = c.num_experts, T = c.num_tokens, SI = c.num_shared * c.shared_inter;
   const int64_t TK = static_cast<int64_t>(T) * c.top_k;
   if (TK == 0) return hipSuccess;
   const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb1, sched, s);
+  const Blocking bs = c.num_shared > 0 ? blocking(c, SI, T) : Blocking{};  // its nb1 (token tile b.bm)
+  const LaunchTiles lt = launch_tiles(c, b, c.num_shared > 0 ? &bs : nullptr, kGateUp, sched);
+  hipError_t err = scheduled ? hipSuccess : schedule(expert_offsets, E, b.bm, T, lt.spec, s);
   if (err != hipSuccess) return err;
   GemmArgs a{};
-  int64_t tiles = routed_max_tiles(c, b.bm, b.nb1);
-  if (c.num_shared > 0) {
-    const Blocking bs = blocking(c, SI, T);   // its nb1 (the token tile stays b.bm)
-    a.s[a.nsets++] = shared_gate_up(c, bs, x, w1s, w3s, s1s, s3s, hs);
-    tiles += ((T + b.bm - 1) / b.bm) * bs.nb1;
-  }
+  if (c.num_shared > 0) a.s[a.nsets++] = shared_gate_up(c, bs, x, w1s, w3s, s1s, s3s, hs);
   a.s[a.nsets++] = routed_gate_up(c, b, x, perm_slot, expert_offsets, sched, w1, w3, s1, s3, h);
-  return run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a, tiles, s);
+  a.xb = sched + E + 1;
+  return run_gemm(kGateUp, is_f32(c), is_fp8(c), b.bm, a, lt.n_shared, lt.n_routed, s);
 }
 
 hipError_t launch_experts_down(const moe_config& c, const void* h, const void* hs,
                                const int32_t* expert_offsets, const int32_t* perm_slot,
                                const float* topk_gate, const void* w2, const float* s2,
                                const void* w2s, const float* s2s, void* out_slots,
-                               void* y_shared, void* ws, hipStream_t s) {
+                               void* y_shared, void* ws, hipStream_t s, bool scheduled) {
   const int E = c.num_experts, T = c.num_tokens, SI = c.num_shared * c.shared_inter;
   const int64_t TK = static_cast<int64_t>(T) * c.top_k;
   if (TK == 0) return hipSuccess;
   const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb2, sched, s);
+  const Blocking bs = c.num_shared > 0 ? blocking(c, SI, T) : Blocking{};
+  const LaunchTiles lt = launch_tiles(c, b, c.num_shared > 0 ? &bs : nullptr, kDown, sched);
+  hipError_t err = scheduled ? hipSuccess : schedule(expert_offsets, E, b.bm, T, lt.spec, s);
   if (err != hipSuccess) return err;
   GemmArgs a{};
-  int64_t tiles = routed_max_tiles(c, b.bm, b.nb2);
-  if (c.num_shared > 0) {
-    const Blocking bs = blocking(c, SI, T);
-    a.s[a.nsets++] = shared_down(c, bs, hs, w2s, s2s, y_shared);
-    tiles += ((T + b.bm - 1) / b.bm) * bs.nb2;
-  }
+  if (c.num_shared > 0) a.s[a.nsets++] = shared_down(c, bs, hs, w2s, s2s, y_shared);
   a.s[a.nsets++] = routed_down(c, b, h, expert_offsets, sched, perm_slot, topk_gate, w2, s2,
                                out_slots);
-  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a, tiles, s);
+  a.xb = sched + E + 1;
+  return run_gemm(kDown, is_f32(c), is_fp8(c), b.bm, a, lt.n_shared, lt.n_routed, s);
 }
 
 hipError_t launch_experts(const moe_config& c, const void* x, const int32_t* expert_offsets,
@@ -909,12 +1066,25 @@ hipError_t launch_experts(const moe_config& c, const void* x, const int32_t* exp
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   void* h = wsb;
   void* hs = c.num_shared > 0 ? wsb + h_bytes(c) : nullptr;
-  void* sched = wsb + h_bytes(c) + (c.num_shared > 0 ? shared_ws_bytes(c) : 0);
-  hipError_t err = launch_experts_gate_up(c, x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s,
-                                          w3s, s1s, s3s, h, hs, sched, s);
+  uint8_t* sched_up = wsb + h_bytes(c) + (c.num_shared > 0 ? shared_ws_bytes(c) : 0);
+  uint8_t* sched_down = sched_up + sched_ws_bytes(c);
+  const int E = c.num_experts;
+  const int64_t TK = static_cast<int64_t>(c.num_tokens) * c.top_k;
+  if (TK == 0) return hipSuccess;
+  // both launches' tile tables in one pass
+  const Blocking b = blocking(c, c.inter, (TK + E - 1) / E);
+  const int SI = c.num_shared * c.shared_inter;
+  const Blocking bs = c.num_shared > 0 ? blocking(c, SI, c.num_tokens) : Blocking{};
+  const Blocking* bsp = c.num_shared > 0 ? &bs : nullptr;
+  const LaunchTiles up = launch_tiles(c, b, bsp, kGateUp, reinterpret_cast<int32_t*>(sched_up));
+  const LaunchTiles down = launch_tiles(c, b, bsp, kDown, reinterpret_cast<int32_t*>(sched_down));
+  hipError_t err = schedule(expert_offsets, E, b.bm, c.num_tokens, up.spec, s, down.spec);
+  if (err != hipSuccess) return err;
+  err = launch_experts_gate_up(c, x, expert_offsets, perm_slot, w1, w3, s1, s3, w1s, w3s, s1s, s3s,
+                               h, hs, sched_up, s, true);
   if (err != hipSuccess) return err;
   return launch_experts_down(c, h, hs, expert_offsets, perm_slot, topk_gate, w2, s2, w2s, s2s,
-                             out_slots, y_shared, sched, s);
+                             out_slots, y_shared, sched_down, s, true);
 }
 
 // ---- fine-grained fp8 experts ------------------------------------------------
@@ -949,19 +1119,18 @@ hipError_t launch_experts_fp8_gate_up(const moe_config& c, const void* xq, const
   if (TK == 0) return hipSuccess;
   const Blocking b = blocking_f8b(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb1, sched, s);
+  const Blocking bs = c.num_shared > 0 ? blocking_f8b(c, SI, T) : Blocking{};
+  const LaunchTiles lt = launch_tiles(c, b, c.num_shared > 0 ? &bs : nullptr, kGateUp, sched);
+  hipError_t err = schedule(expert_offsets, E, b.bm, T, lt.spec, s);
   if (err != hipSuccess) return err;
   GemmArgs a{};
-  int64_t tiles = routed_max_tiles(c, b.bm, b.nb1);
-  if (c.num_shared > 0) {
-    const Blocking bs = blocking_f8b(c, SI, T);
+  if (c.num_shared > 0)
     a.s[a.nsets++] = f8b_gate_up(c, bs, xq, xs, nullptr, nullptr, nullptr, SI, T, w13s, s1s, s3s,
                                  hsq, hss);
-    tiles += ((T + b.bm - 1) / b.bm) * bs.nb1;
-  }
   a.s[a.nsets++] = f8b_gate_up(c, b, xq, xs, perm_slot, expert_offsets, sched, c.inter, 0, w13,
                                s1, s3, hq, hs);
-  return run_f8b(kGateUp, b.bm, a, tiles, s);
+  a.xb = sched + E + 1;
+  return run_f8b(kGateUp, b.bm, a, lt.n_shared, lt.n_routed, s);
 }
 
 hipError_t launch_experts_fp8_down(const moe_config& c, const void* hq, const float* hs,
@@ -975,19 +1144,18 @@ hipError_t launch_experts_fp8_down(const moe_config& c, const void* hq, const fl
   if (TK == 0) return hipSuccess;
   const Blocking b = blocking_f8b(c, c.inter, (TK + E - 1) / E);
   int32_t* sched = static_cast<int32_t*>(ws);
-  hipError_t err = schedule(expert_offsets, E, b.bm, b.nb2, sched, s);
+  const Blocking bs = c.num_shared > 0 ? blocking_f8b(c, SI, T) : Blocking{};
+  const LaunchTiles lt = launch_tiles(c, b, c.num_shared > 0 ? &bs : nullptr, kDown, sched);
+  hipError_t err = schedule(expert_offsets, E, b.bm, T, lt.spec, s);
   if (err != hipSuccess) return err;
   GemmArgs a{};
-  int64_t tiles = routed_max_tiles(c, b.bm, b.nb2);
-  if (c.num_shared > 0) {
-    const Blocking bs = blocking_f8b(c, SI, T);
+  if (c.num_shared > 0)
     a.s[a.nsets++] = f8b_down(c, bs, hsq, hss, nullptr, nullptr, SI, T, nullptr, nullptr, w2s, s2s,
                               y_shared, 1);
-    tiles += ((T + b.bm - 1) / b.bm) * bs.nb2;
-  }
   a.s[a.nsets++] = f8b_down(c, b, hq, hs, expert_offsets, sched, c.inter, 0, perm_slot, topk_gate,
                             w2, s2, out_slots, c.slot_dtype == MOE_DTYPE_F32);
-  return run_f8b(kDown, b.bm, a, tiles, s);
+  a.xb = sched + E + 1;
+  return run_f8b(kDown, b.bm, a, lt.n_shared, lt.n_routed, s);
 }
 
 hipError_t launch_experts_fp8(const moe_config& c, const void* xq, const float* xs,

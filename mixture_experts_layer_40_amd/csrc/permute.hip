@@ -139,7 +139,9 @@ __global__ __launch_bounds__(256) void perm_rank(const int32_t* __restrict__ idx
 // All of 1-3 in one block, for T*K <= kChunk (decode-sized batches): the
 // per-wave counts give the expert totals, their exclusive scan the offsets,
 // and the same ranking pass as perm_rank places every pair. One launch in
-// place of three; the result is the same stable order.
+// place of three; the result is the same stable order. The pairs are split
+// evenly over the four waves (in order: wave w takes the w-th quarter, whole
+// 64-pair groups), so a small batch keeps every wave busy.
 __global__ __launch_bounds__(256) void perm_single(const int32_t* __restrict__ idx, int64_t TK,
                                                    int E, int32_t* __restrict__ offsets,
                                                    int32_t* __restrict__ perm_slot) {
@@ -148,8 +150,9 @@ __global__ __launch_bounds__(256) void perm_single(const int32_t* __restrict__ i
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   for (int i = tid; i < 4 * 256; i += 256) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  const int64_t wbase = static_cast<int64_t>(w) * kWaveChunk;
-  for (int i = l; i < kWaveChunk; i += kWave) {
+  const int wchunk = static_cast<int>((TK + 4 * kWave - 1) / (4 * kWave)) * kWave;   // <= kWaveChunk
+  const int64_t wbase = static_cast<int64_t>(w) * wchunk;
+  for (int i = l; i < wchunk; i += kWave) {
     const int64_t f = wbase + i;
     if (f < TK) {
       const int e = idx[f];
@@ -180,7 +183,7 @@ __global__ __launch_bounds__(256) void perm_single(const int32_t* __restrict__ i
   if (tid == 0) offsets[E] = total;
   for (int64_t p = total + tid; p < TK; p += 256) perm_slot[p] = -1;
   __syncthreads();
-  for (int it = 0; it < kWaveChunk; it += kWave) {
+  for (int it = 0; it < wchunk; it += kWave) {
     const int64_t f = wbase + it + l;
     int e = -1;
     if (f < TK) {

@@ -206,8 +206,10 @@ __global__ __launch_bounds__(kThreads) void route_fused_bf16(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void route_logits_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
-    int stages_per_split, float* __restrict__ part) {
+    int stages_per_split, float* __restrict__ part, int32_t* __restrict__ load) {
   const int l = lane_id(), w = wave_id(), g = l >> 4, r16 = l & 15;
+  // the load counts the top-K kernel accumulates start from zero
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < E) load[threadIdx.x] = 0;
   const int ef = blockIdx.y * 4 + w;
   if (16 * ef >= E) return;
   const int nk = d / 64;
@@ -243,8 +245,11 @@ __global__ __launch_bounds__(256) void route_logits_bf16(
 // dot product over the hidden axis.
 __global__ __launch_bounds__(256) void route_logits_f32(const float* __restrict__ x,
                                                         const float* __restrict__ wr, int T,
-                                                        int d, int E, float* __restrict__ part) {
+                                                        int d, int E, float* __restrict__ part,
+                                                        int32_t* __restrict__ load) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  // the load counts the top-K kernel accumulates start from zero
+  if (blockIdx.x == 0 && threadIdx.x < E) load[threadIdx.x] = 0;
   if (i >= static_cast<int64_t>(T) * E) return;
   const int t = static_cast<int>(i / E), e = static_cast<int>(i % E);
   const float* a = x + static_cast<size_t>(t) * d;
@@ -320,8 +325,12 @@ size_t route_ws_bytes(const moe_config& c) {
 hipError_t launch_route(const moe_config& c, const void* x, const void* wr, const float* bias,
                         int32_t* topk_idx, float* topk_gate, int32_t* load, void* ws,
                         hipStream_t s) {
-  hipError_t err = launch_fill_i32(load, 0, c.num_experts, s);
-  if (err != hipSuccess || c.num_tokens == 0) return err;
+  hipError_t err;
+  if (c.num_tokens == 0 || route_uses_fused(c)) {
+    // (the split path's logits kernel clears the load counts itself)
+    err = launch_fill_i32(load, 0, c.num_experts, s);
+    if (err != hipSuccess || c.num_tokens == 0) return err;
+  }
   const int T = c.num_tokens, d = c.hidden, E = c.num_experts, K = c.top_k;
   const int G = c.num_groups > 1 ? c.num_groups : 1;
   const int M = G > 1 ? c.topk_groups : 1;
@@ -339,12 +348,12 @@ hipError_t launch_route(const moe_config& c, const void* x, const void* wr, cons
     const int sps = (nk + splits - 1) / splits;
     hipLaunchKernelGGL(route_logits_bf16, dim3((T + 15) / 16, (E + 63) / 64, splits), dim3(256),
                        0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                       T, d, E, sps, part);
+                       T, d, E, sps, part, load);
   } else {
     const int64_t n = static_cast<int64_t>(T) * E;
     hipLaunchKernelGGL(route_logits_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                        0, s, static_cast<const float*>(x), static_cast<const float*>(wr), T, d, E,
-                       part);
+                       part, load);
   }
   err = hipGetLastError();
   if (err != hipSuccess) return err;
