@@ -742,6 +742,13 @@ def main():
                      "bound": "hbm",
                      "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     # traffic is not counted in this run: it comes from the
+                     # committed FETCH_SIZE / WRITE_SIZE summary, and is null
+                     # unless that was taken on the current kernel sources
+                     "traffic_source": ("profiles/gate_up_v3_prefill_traffic.txt (rocprofv3 "
+                                        "FETCH_SIZE + WRITE_SIZE, kernel_src_sha "
+                                        f"{kernel_source_hash()})"
+                                        if measured_traffic() is not None else None),
                      "algorithmic_bytes_per_launch": gate_bytes,
                      "algorithmic_flops_per_launch": gate_flops, "avg_launch_ms": gate_ms,
                      "flop_per_byte": gate_flops / gate_bytes,
