@@ -69,7 +69,7 @@ extern "C" {
 #define MOE_ERR_NULL         1  /* a required pointer is NULL                  */
 #define MOE_ERR_SHAPE        2  /* sizes out of range or not supported          */
 #define MOE_ERR_DTYPE        3  /* dtype enum unknown or combination invalid    */
-#define MOE_ERR_UNSUPPORTED  4  /* valid request this build does not implement  */
+#define MOE_ERR_UNSUPPORTED  4  /* valid request the library does not implement */
 #define MOE_ERR_WORKSPACE    5  /* workspace NULL or smaller than required      */
 #define MOE_ERR_HIP          6  /* the HIP runtime reported a launch error      */
 #define MOE_ERR_SCRATCH      7  /* needs more than moe_permute_noalloc's fixed
