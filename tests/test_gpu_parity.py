@@ -50,6 +50,13 @@ CASES = {
     "e20": _cfg("v3_prefill_bf16", T=129, d=64, E=20, K=5, I=64, Is=64),
     "one_token": _cfg("v3_prefill_bf16", T=1, d=128, E=256, K=8, I=64, Is=64),
     "one_expert": _cfg("v3_prefill_bf16", T=33, d=64, E=1, K=1, I=64, S=0, Is=0),
+    # many slots per token: 64 of 256 experts (a wave's full record of
+    # selections), all 256 (every expert holds every token; 5120 pairs, a
+    # multi-chunk sort), and 64 under node-limited routing (4 of 8 groups)
+    "k64": _cfg("v3_prefill_bf16", T=100, d=128, E=256, K=64, I=64, Is=64),
+    "k_eq_e_256": _cfg("v3_prefill_bf16", T=20, d=64, E=256, K=256, I=64, Is=64),
+    "k64_grouped": _cfg("v3_prefill_bf16", T=120, d=128, E=256, K=64, I=64, Is=64,
+                        n_groups=8, topk_groups=4),
     # node-limited routing: split-K router, fused router (T >= 4096), softmax
     # scores, a single kept group
     "grouped_small": _cfg("v3_prefill_bf16", T=300, d=256, E=64, K=6, I=128, Is=128,
