@@ -207,7 +207,9 @@ __global__ __launch_bounds__(kThreads / RF) void grouped_gemm_mfma(GemmArgs args
   for (int t = 0; t < RF * NTF; ++t) acc[t] = f32x16{};
 
   const uint16_t* act = static_cast<const uint16_t*>(a.act);
-  using ML = MainLoop<FP8, NSA, BM, false, RF>;
+  // non-temporal weight loads for the few-token tiles, whose launches only
+  // stream weights (see MainLoop); the many-token tiles keep plain loads
+  using ML = MainLoop<FP8, NSA, BM, false, RF, (BM <= 64)>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
     case n: if constexpr (n <= NTF) ML::template run<n>(aptr, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, a.kdim, astage, avs, bs0, bs1, bs2, bs3, acc); break;
@@ -365,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_f8b(GemmArgs args) {
 
   const uint16_t* act = static_cast<const uint16_t*>(a.act);
   const int kdim16 = a.kdim / 2;                  // a row of codes in 16-bit units
-  using ML = MainLoop<false, NSA, BM, true>;
+  using ML = MainLoop<false, NSA, BM, true, 1, (BM <= 64)>;
   switch (ntf) {
 #define MOE_NT_CASE(n) \
     case n: if constexpr (n <= NTF) ML::template run<n>(aps, act, tl.row0, a.act_rows, a.act_div, tl.mvalid, kdim16, astage, avs, bs0, bs1, bs2, bs3, acc, post); break;
