@@ -532,8 +532,8 @@ def measured_peaks():
     """Achievable peaks on this GPU, beside the nominal ones. From the probes
     of libmoe_peaks.so: a loop of independent MFMAs of each instruction form
     (8 waves per block, 1024 blocks, operands changing from one instruction
-    to the next), an fp32 FMA loop, and a 16-byte-load streaming read and
-    copy of 2 GiB. For reference also torch's copy of 1 GiB and the vendor
+    to the next), an fp32 FMA loop, and a 16-byte-load streaming read (plain
+    and non-temporal loads) and copy of 2 GiB. For reference also torch's copy of 1 GiB and the vendor
     BLAS bf16 GEMM at 8192^3. Also the L2 -> CU read rate (each CU
     re-reading 64 KB), against which the GEMMs' L2 -> CU operand traffic
     can be set."""
@@ -557,7 +557,8 @@ def measured_peaks():
             "mfma_bf16_TFLOPs": max(loops["bf16_32x32x16"], loops["bf16_16x16x32"]),
             "mfma_fp8_TFLOPs": max(loops["fp8_32x32x64"], loops["fp8_16x16x128"]),
             "fma_f32_TFLOPs": loops["f32_fma"],
-            "stream_read_GBs": stream["read_GBs"], "stream_copy_GBs": stream["copy_GBs"],
+            "stream_read_GBs": stream["read_GBs"], "stream_read_nt_GBs": stream["read_nt_GBs"],
+            "stream_copy_GBs": stream["copy_GBs"],
             "l2_read_GBs": l2,
             "copy_GBs": 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9,
             "blas_bf16_TFLOPs": 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12,
@@ -578,8 +579,11 @@ def attach_measured_fractions(result, peaks):
     rl["mfma_frac_of_own_form_loop"] = rl["mfma_TFLOPs"] / peaks["mfma_loop_TFLOPs"]["bf16_32x32x16"]
     rl["mfma_frac_of_measured_blas"] = rl["mfma_TFLOPs"] / peaks["blas_bf16_TFLOPs"]
     if "decode" in result:
-        result["decode"]["frac_of_measured_read"] = result["decode"]["achieved_GBs"] / rd
-        result["decode"]["graph_frac_of_measured_read"] = result["decode"]["graph_achieved_GBs"] / rd
+        # the decode GEMMs load their weights with the non-temporal hint:
+        # set them against the streaming read of the same load form
+        rdn = peaks["stream_read_nt_GBs"]
+        result["decode"]["frac_of_measured_read"] = result["decode"]["achieved_GBs"] / rdn
+        result["decode"]["graph_frac_of_measured_read"] = result["decode"]["graph_achieved_GBs"] / rdn
     if "fp8_prefill" in result:
         f = result["fp8_prefill"]
         f["gate_up_frac_of_measured_read"] = f["gate_up_GBs"] / rd

@@ -55,6 +55,12 @@ double moe_peak_mfma_flops(int kind, int32_t blocks, int32_t iters);
 int moe_peak_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out,
                          void* stream);
 
+/* moe_peak_stream_read with the non-temporal hint on every load, the form
+ * the 32- and 64-token expert GEMMs use for their weights (same arguments,
+ * same result in out). */
+int moe_peak_stream_read_nt(const void* src, size_t bytes, int32_t blocks, uint32_t* out,
+                            void* stream);
+
 /* L2 -> CU read rate: block b re-reads its own region_bytes of src
  * (src + b * region_bytes; region_bytes a positive multiple of 64 KB, src
  * 16-byte aligned, blocks * region_bytes bytes readable) `iters` times with

@@ -31,7 +31,7 @@ FORMS = {
     "f32_fma": MOE_PEAK_FMA_F32,
 }
 EXPORTED = ("moe_peak_mfma", "moe_peak_mfma_flops", "moe_peak_stream_read",
-            "moe_peak_l2_read", "moe_peak_stream_copy", "moe_probe_fp8_mfma")
+            "moe_peak_stream_read_nt", "moe_peak_l2_read", "moe_peak_stream_copy", "moe_probe_fp8_mfma")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -54,6 +54,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_peak_mfma_flops.restype = ctypes.c_double
     lib.moe_peak_stream_read.argtypes = [P, SZ, I32, P, P]
     lib.moe_peak_stream_read.restype = ctypes.c_int
+    lib.moe_peak_stream_read_nt.argtypes = [P, SZ, I32, P, P]
+    lib.moe_peak_stream_read_nt.restype = ctypes.c_int
     lib.moe_peak_l2_read.argtypes = [P, SZ, I32, I32, P, P]
     lib.moe_peak_l2_read.restype = ctypes.c_int
     lib.moe_peak_stream_copy.argtypes = [P, P, SZ, I32, P]
@@ -84,6 +86,11 @@ def moe_peak_mfma_flops(kind: int, blocks: int, iters: int) -> float:
 
 def moe_peak_stream_read(src: torch.Tensor, nbytes: int, blocks: int, out: torch.Tensor):
     _check("moe_peak_stream_read", load_library().moe_peak_stream_read(
+        src.data_ptr(), nbytes, blocks, out.data_ptr(), _stream()))
+
+
+def moe_peak_stream_read_nt(src: torch.Tensor, nbytes: int, blocks: int, out: torch.Tensor):
+    _check("moe_peak_stream_read_nt", load_library().moe_peak_stream_read_nt(
         src.data_ptr(), nbytes, blocks, out.data_ptr(), _stream()))
 
 
@@ -132,8 +139,9 @@ def measure_mfma(form: str, blocks: int = 1024, iters: int = 2048, reps: int = 5
 
 def measure_stream(nbytes: int = 1 << 31, read_blocks: int = 4096,
                    copy_blocks: Optional[int] = None, reps: int = 5) -> dict:
-    """GB/s of a 16-byte-load streaming read of `nbytes` and of a streaming
-    copy of `nbytes` (read + written bytes). The read runs best as a
+    """GB/s of a 16-byte-load streaming read of `nbytes` (plain loads, and
+    loads with the non-temporal hint) and of a streaming copy of `nbytes`
+    (read + written bytes). The read runs best as a
     grid-stride loop over a few thousand blocks (6.1 TB/s on MI355X, against
     5.5 with one block per 32 KB chunk); the copy, by default, gets one
     block per chunk (5.4-5.5 TB/s, against 5.2-5.3 grid-stride)."""
@@ -144,9 +152,11 @@ def measure_stream(nbytes: int = 1 << 31, read_blocks: int = 4096,
     dst = torch.empty_like(src)
     out = torch.empty(read_blocks * 256, dtype=torch.int32, device="cuda")
     read_ms = _time_ms(lambda: moe_peak_stream_read(src, nbytes, read_blocks, out), reps)
+    read_nt_ms = _time_ms(lambda: moe_peak_stream_read_nt(src, nbytes, read_blocks, out), reps)
     copy_ms = _time_ms(lambda: moe_peak_stream_copy(src, dst, nbytes, copy_blocks), reps)
     del src, dst, out
     return {"read_GBs": nbytes / (read_ms * 1e-3) / 1e9,
+            "read_nt_GBs": nbytes / (read_nt_ms * 1e-3) / 1e9,
             "copy_GBs": 2.0 * nbytes / (copy_ms * 1e-3) / 1e9}
 
 

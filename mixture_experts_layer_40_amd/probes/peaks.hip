@@ -147,8 +147,12 @@ __global__ __launch_bounds__(kLoopThreads) void mfma_loop(int iters, float* __re
 constexpr int kUnroll = 8;
 constexpr size_t kChunk16 = static_cast<size_t>(kStreamThreads) * kUnroll;
 
+// NT: the loads carry the non-temporal hint (the form the decode GEMMs use
+// for their weights).
+template <bool NT>
 __global__ __launch_bounds__(kStreamThreads) void stream_read(const u32x4* __restrict__ src,
                                                              size_t n16, uint32_t* __restrict__ out) {
+  auto ld = [&](size_t i) { return NT ? __builtin_nontemporal_load(src + i) : src[i]; };
   const size_t nchunks = (n16 + kChunk16 - 1) / kChunk16;
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (size_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
@@ -156,12 +160,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_read(const u32x4* __res
     if ((c + 1) * kChunk16 <= n16) {
       u32x4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = src[base + u * kStreamThreads];
+      for (int u = 0; u < kUnroll; ++u) v[u] = ld(base + u * kStreamThreads);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
     } else {
       for (int u = 0; u < kUnroll; ++u)
-        if (base + u * kStreamThreads < n16) acc ^= src[base + u * kStreamThreads];
+        if (base + u * kStreamThreads < n16) acc ^= ld(base + u * kStreamThreads);
     }
   }
   out[static_cast<size_t>(blockIdx.x) * kStreamThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
@@ -279,8 +283,18 @@ int moe_peak_stream_read(const void* src, size_t bytes, int32_t blocks, uint32_t
                          void* stream) {
   if (!src || !out) return MOE_ERR_NULL;
   if (blocks < 1 || bytes == 0 || bytes % 16 != 0 || !aligned16(src)) return MOE_ERR_SHAPE;
-  hipLaunchKernelGGL(stream_read, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+  hipLaunchKernelGGL(stream_read<false>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                     0, reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
+                     bytes / 16, out);
+  return status_of(hipGetLastError());
+}
+
+int moe_peak_stream_read_nt(const void* src, size_t bytes, int32_t blocks, uint32_t* out,
+                            void* stream) {
+  if (!src || !out) return MOE_ERR_NULL;
+  if (blocks < 1 || bytes == 0 || bytes % 16 != 0 || !aligned16(src)) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(stream_read<true>, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                     0, reinterpret_cast<hipStream_t>(stream), static_cast<const u32x4*>(src),
                      bytes / 16, out);
   return status_of(hipGetLastError());
 }

@@ -1,4 +1,5 @@
-"""The achievable-peak probes on the GPU: the streaming and L2 reads touch
+"""The achievable-peak probes on the GPU: the streaming reads (plain and
+non-temporal loads) and the L2 read touch
 every word (their per-thread XORs combine to the XOR of the buffer) and the
 streaming copy is exact, on sizes that leave a ragged grid-stride tail; the
 MFMA and FMA loops give finite, non-zero, run-to-run identical results and a
@@ -23,12 +24,15 @@ def test_stream_read_and_copy_touch_every_word(n16, blocks):
     src = host.cuda()
     out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
     pk.moe_peak_stream_read(src, n16 * 16, blocks, out)
+    out_nt = torch.empty_like(out)
+    pk.moe_peak_stream_read_nt(src, n16 * 16, blocks, out_nt)
     dst = torch.zeros_like(src)
     pk.moe_peak_stream_copy(src, dst, n16 * 16, blocks)
     torch.cuda.synchronize()
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert got == want
+    assert np.bitwise_xor.reduce(out_nt.cpu().numpy().view(np.uint32)) == want
     assert torch.equal(dst, src)
 
 

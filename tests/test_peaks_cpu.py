@@ -54,6 +54,12 @@ def test_bad_arguments_are_rejected_on_the_host():
     assert rd(fake, 24, 1, fake, None) == L.MOE_ERR_SHAPE
     assert rd(odd, 16, 1, fake, None) == L.MOE_ERR_SHAPE
     assert rd(fake, 16, 0, fake, None) == L.MOE_ERR_SHAPE
+    rn = lib.moe_peak_stream_read_nt
+    assert rn(None, 16, 1, fake, None) == L.MOE_ERR_NULL
+    assert rn(fake, 16, 1, None, None) == L.MOE_ERR_NULL
+    assert rn(fake, 24, 1, fake, None) == L.MOE_ERR_SHAPE
+    assert rn(odd, 16, 1, fake, None) == L.MOE_ERR_SHAPE
+    assert rn(fake, 16, 0, fake, None) == L.MOE_ERR_SHAPE
     l2 = lib.moe_peak_l2_read
     assert l2(None, 65536, 1, 1, fake, None) == L.MOE_ERR_NULL
     assert l2(fake, 65536, 1, 1, None, None) == L.MOE_ERR_NULL
