@@ -562,6 +562,7 @@ __global__ __launch_bounds__(256) void ffn_schedule(const int32_t* __restrict__ 
     __syncthreads();
   }
   const int all_mt = before_[255];
+  __syncthreads();                      // every thread has read the total before it changes
   before_[tid] -= mt;                   // token tiles of the experts before this one
   __syncthreads();
   int mts = 0, ntfs = 0, rcs = 0;
