@@ -159,8 +159,16 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
 // activation dtype. A thread keeps its row elements (16-byte pieces) in
 // registers between the two passes and writes back the same pieces, so u may
 // alias x.
+// For bf16 output each element is first formed in float as
+// (x * (1 / root)) * w, within 3.1 float units in the last place of the
+// double result (three roundings of 2^-24); a bf16 rounding boundary lies
+// 2^15 such units from the nearest representable values, so unless the
+// float value is within 8 units of one (or tiny) it rounds to the bf16 value
+// the double result rounds to. The pieces with such an element (a few in a
+// thousand) are left unwritten and redone through the double path at the
+// end. Six waves per SIMD (the launch bound) hide the row loads' latency.
 template <bool BF16>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x,
+__global__ __launch_bounds__(256, 6) void rmsnorm_kernel(const void* __restrict__ x,
                                                       const float* __restrict__ w, int d,
                                                       double eps, void* u) {
   constexpr int kMaxPieces = 8;                 // d <= 256 threads * 8 pieces * 8 (bf16)
@@ -198,25 +206,55 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void* __restrict__ x
   __syncthreads();
   const double ss = (part[0] + part[1]) + (part[2] + part[3]);
   const double root = sqrt(ss / d + eps);
+  const float rinv32 = static_cast<float>(1.0 / root);
   u32x4* dst = reinterpret_cast<u32x4*>(static_cast<char*>(u) + t * d * (BF16 ? 2 : 4));
+  uint32_t redo = 0;   // pieces to redo through the double path
 #pragma unroll
   for (int i = 0; i < kMaxPieces; ++i) {
     const int p = tid + 256 * i;
     if (p < npieces) {
       u32x4 o;
       const int j0 = p * EPP;
+      bool near = false;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (BF16) {
-          const double a = bf16_to_f32(static_cast<uint16_t>(keep[i][q] & 0xFFFFu));
-          const double c = bf16_to_f32(static_cast<uint16_t>(keep[i][q] >> 16));
-          const uint32_t lo = f64_to_bf16_rne((a / root) * static_cast<double>(w[j0 + 2 * q]));
-          const uint32_t hi = f64_to_bf16_rne((c / root) * static_cast<double>(w[j0 + 2 * q + 1]));
+          const float a = bf16_to_f32(static_cast<uint16_t>(keep[i][q] & 0xFFFFu));
+          const float c = bf16_to_f32(static_cast<uint16_t>(keep[i][q] >> 16));
+          const float ya = (a * rinv32) * w[j0 + 2 * q];
+          const float yc = (c * rinv32) * w[j0 + 2 * q + 1];
+          const uint32_t ba = __float_as_uint(ya), bc = __float_as_uint(yc);
+          near |= abs(static_cast<int>(ba & 0xFFFFu) - 0x8000) <= 8 || fabsf(ya) < 0x1p-120f;
+          near |= abs(static_cast<int>(bc & 0xFFFFu) - 0x8000) <= 8 || fabsf(yc) < 0x1p-120f;
+          const uint32_t lo = (ba + 0x7FFFu + ((ba >> 16) & 1u)) >> 16;
+          const uint32_t hi = (bc + 0x7FFFu + ((bc >> 16) & 1u)) >> 16;
           o[q] = lo | (hi << 16);
         } else {
           const double a = __uint_as_float(keep[i][q]);
           o[q] = __float_as_uint(__double2float_rn((a / root) * static_cast<double>(w[j0 + q])));
         }
+      }
+      if (BF16 && near) redo |= 1u << i;   // left unwritten: x stays readable there
+      else dst[p] = o;
+    }
+  }
+  if (BF16 && redo) {
+    // each element (x / root) * w, correctly rounded to bf16; x is re-read
+    // from memory, which holds it still when u aliases x (these pieces were
+    // not written above, and no other thread writes them)
+#pragma unroll 1
+    for (int i = 0; i < kMaxPieces; ++i) {
+      if (!((redo >> i) & 1u)) continue;
+      const int p = tid + 256 * i, j0 = p * EPP;
+      const u32x4 xv = src[p];
+      u32x4 o;
+#pragma unroll 1
+      for (int q = 0; q < 4; ++q) {
+        const double a = bf16_to_f32(static_cast<uint16_t>(xv[q] & 0xFFFFu));
+        const double c = bf16_to_f32(static_cast<uint16_t>(xv[q] >> 16));
+        const uint32_t lo = f64_to_bf16_rne((a / root) * static_cast<double>(w[j0 + 2 * q]));
+        const uint32_t hi = f64_to_bf16_rne((c / root) * static_cast<double>(w[j0 + 2 * q + 1]));
+        o[q] = lo | (hi << 16);
       }
       dst[p] = o;
     }

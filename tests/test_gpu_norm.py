@@ -65,6 +65,39 @@ def test_rmsnorm_matches_oracle(base, kw):
     assert torch.equal(inplace, u)
 
 
+
+def test_rmsnorm_at_bf16_rounding_boundaries():
+    """Outputs placed on bf16 rounding midpoints: rows of ones (root =
+    sqrt(1 + eps)) with w = midpoint * root, so (x / root) * w lies within a
+    float rounding of a midpoint between two bf16 values and its rounding is
+    decided below float precision; plus random rows. Both the float-formed
+    elements and the ones redone in double must equal the oracle's bit for
+    bit, out of place and in place."""
+    spec = _cfg("v3_prefill_bf16", T=64, d=256)
+    cfg = moe.config_of(spec)
+    d = spec.d
+    root = np.sqrt(1.0 + 1e-6)
+    k = np.arange(d) % 128
+    mid = (1.0 + (2 * k + 1) * 2.0 ** -8) * np.where(np.arange(d) < 128, 1.0, -0.5)
+    w = torch.from_numpy((mid * root).astype(np.float32)).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    x = torch.randn((spec.T, d), device="cuda", generator=g).to(torch.bfloat16)
+    x[: spec.T // 2] = 1.0
+    u = torch.empty_like(x)
+    moe.moe_rmsnorm(cfg, x, w, u)
+    inplace = x.clone()
+    moe.moe_rmsnorm(cfg, inplace, w, inplace)
+    torch.cuda.synchronize()
+    want = _oracle_u(spec, x, w)
+    got = host(u)
+    assert np.array_equal(got, want), f"{int((got != want).sum())} of {got.size} differ"
+    assert torch.equal(inplace, u)
+    # the ones rows really sit on midpoints: their float64 values are within
+    # 2^-20 (relative) of one
+    u64 = oracle.rmsnorm(f64(x[: spec.T // 2]), w.cpu().numpy().astype(np.float64))
+    assert np.all(np.abs(u64 / mid - 1) < 2.0 ** -20)
+
 CASES = {
     "v3_small": _cfg("v3_prefill_bf16", T=300, d=256, E=64, K=6, I=128, Is=128),
     "v3_fused": _cfg("v3_prefill_bf16", T=4100, d=128, E=256, K=8, I=128, Is=128),
