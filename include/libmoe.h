@@ -201,7 +201,12 @@ int moe_pack_weights(int which, int32_t groups, int32_t rows, int32_t cols, int3
  * bias [E] fp32 or NULL; topk_idx [T, K] int32; topk_gate [T, K] fp32;
  * load [E] int32. Logits are accumulated in fp32; scores and keys are fp32.
  * Workspace: moe_workspace_size(cfg, MOE_WS_ROUTE) bytes (may be 0, then ws
- * may be NULL). */
+ * may be NULL): the split-K partial logits (fp32 activations, or fewer than
+ * 4096 tokens), or on the fused bf16 path with E a multiple of 32 a copy of
+ * w_router that the call writes in the tiled layout of moe_pack_weights
+ * (MOE_PACK_DOWN, one group) and reads instead, each weight load then being
+ * one contiguous 1 KB stripe (a relocation only: results are unchanged).
+ * The size for cfg also serves the same call with fewer tokens. */
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
               int32_t* topk_idx, float* topk_gate, int32_t* load,
               void* ws, size_t ws_bytes, void* stream);

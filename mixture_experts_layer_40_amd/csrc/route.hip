@@ -150,9 +150,13 @@ __device__ void topk_token(const float (&lg)[4], int t, int E, int K, int G, int
 // router rows 32w .. 32w+31 into MFMA operands, the 32-token tile is shared
 // through LDS. The logits stay in LDS; each wave then runs the top-K of 4
 // tokens. Rows past E (E < 256) are computed on a repeated row and dropped.
+// wr_tiled: the router rows in the tiled layout of the expert weights (see
+// pack_tiles; E a multiple of 32), so that each weight load instruction
+// reads one contiguous 1 KB stripe instead of 16 bytes from each of 64 row
+// pieces; else row-major.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void route_fused_bf16(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int wr_tiled,
     const float* __restrict__ bias, int T, int d, int E, int K, int G, int M, int score_fn,
     int norm, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     int32_t* __restrict__ load) {
@@ -169,11 +173,18 @@ __global__ __launch_bounds__(kThreads) void route_fused_bf16(
   const int mvalid = min(BT, T - t0);
   if (tid < 256) hist[tid] = 0;
 
-  const int row = min(32 * w + r32, E - 1);
-  const uint8_t* aptr[1] = {reinterpret_cast<const uint8_t*>(wr + static_cast<size_t>(row) * d + 32 * g)};
+  const uint8_t* aptr[1];
+  if (wr_tiled) {
+    const int rb = 32 * w < E ? w : 0;   // fragments past E compute fragment 0 (dropped)
+    aptr[0] = reinterpret_cast<const uint8_t*>(wr) + static_cast<size_t>(rb) * (d / 64) * 4096 + 16 * l;
+  } else {
+    const int row = min(32 * w + r32, E - 1);
+    aptr[0] = reinterpret_cast<const uint8_t*>(wr + static_cast<size_t>(row) * d + 32 * g);
+  }
   f32x16 acc[1] = {f32x16{}};
-  MainLoop<false, 3, BT>::template run<1>(aptr, x, t0, nullptr, 1, mvalid, d, 64 * 2, 16, bs0, bs1,
-                                          bs2, bs3, acc);
+  MainLoop<false, 3, BT>::template run<1>(aptr, x, t0, nullptr, 1, mvalid, d,
+                                          wr_tiled ? 4096 : 64 * 2, wr_tiled ? 1024 : 16, bs0,
+                                          bs1, bs2, bs3, acc);
   // acc[0][4i + j] = logit of expert 32w + 8i + 4g + j for token t0 + r32
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -317,9 +328,33 @@ int route_k_splits(const moe_config& c) {
   return (nk + sps - 1) / sps;
 }
 
-size_t route_ws_bytes(const moe_config& c) {
+// The fused router reads a tiled copy of the router rows that it writes to
+// the workspace on each call (E * d act elements, a pure relocation).
+bool route_tiles_router(const moe_config& c) {
+  return route_uses_fused(c) && c.num_experts % 32 == 0;
+}
+
+// Workspace of one call with exactly c.num_tokens tokens.
+size_t route_ws_bytes_at(const moe_config& c) {
+  if (route_tiles_router(c)) return align_up(static_cast<size_t>(c.num_experts) * c.hidden * 2, 256);
   if (route_uses_fused(c)) return 0;
   return align_up(static_cast<size_t>(route_k_splits(c)) * c.num_tokens * c.num_experts * 4, 256);
+}
+
+// The largest of route_ws_bytes_at over 1 .. c.num_tokens tokens, so that a
+// workspace sized for a batch also serves every smaller one (the split-K
+// partials do not grow monotonically with T, and the fused path below them
+// needs a different amount).
+size_t route_ws_bytes(const moe_config& c) {
+  size_t m = route_ws_bytes_at(c);
+  moe_config t = c;
+  const int top = c.num_tokens < kFusedMinTokens ? c.num_tokens : kFusedMinTokens - 1;
+  for (int n = 1; n <= top; ++n) {
+    t.num_tokens = n;
+    const size_t b = route_ws_bytes_at(t);
+    if (b > m) m = b;
+  }
+  return m;
 }
 
 hipError_t launch_route(const moe_config& c, const void* x, const void* wr, const float* bias,
@@ -335,9 +370,15 @@ hipError_t launch_route(const moe_config& c, const void* x, const void* wr, cons
   const int G = c.num_groups > 1 ? c.num_groups : 1;
   const int M = G > 1 ? c.topk_groups : 1;
   if (route_uses_fused(c)) {
+    const int tiled = route_tiles_router(c);
+    if (tiled) {
+      err = launch_pack(1, 1, E, d, 2, wr, nullptr, ws, s);
+      if (err != hipSuccess) return err;
+    }
     hipLaunchKernelGGL(route_fused_bf16, dim3((T + kFusedTokens - 1) / kFusedTokens), dim3(kThreads),
-                       0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                       bias, T, d, E, K, G, M, c.score_fn, c.norm, topk_idx, topk_gate, load);
+                       0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(tiled ? ws : wr), tiled, bias, T, d, E, K, G, M,
+                       c.score_fn, c.norm, topk_idx, topk_gate, load);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(ws);

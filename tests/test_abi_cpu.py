@@ -117,7 +117,13 @@ def test_validate_null():
 
 def test_workspace_sizes():
     c = _cfg(act_dtype="bf16", weight_dtype="bf16", T=4096, d=7168, E=256, K=8, I=2048, Is=2048)
-    assert moe.moe_workspace_size(c, moe.MOE_WS_ROUTE) == 0          # fused router
+    # fused router: a tiled copy of the router rows (E * d bf16), and enough
+    # for every smaller batch, which may take the split-K path
+    route = moe.moe_workspace_size(c, moe.MOE_WS_ROUTE)
+    assert route >= 256 * 7168 * 2 and route % 256 == 0
+    for t in (1, 17, 500, 2047, 4095):
+        assert moe.moe_workspace_size(_cfg(act_dtype="bf16", weight_dtype="bf16", T=t, d=7168, E=256,
+                                           K=8, I=2048, Is=2048), moe.MOE_WS_ROUTE) <= route
     assert moe.moe_workspace_size(c, moe.MOE_WS_FFN) >= 4096 * 8 * 2048 * 2
     assert moe.moe_workspace_size(c, moe.MOE_WS_SHARED) >= 4096 * 2048 * 2
     assert moe.moe_workspace_size(c, moe.MOE_WS_GEMM) >= 257 * 4
