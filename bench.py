@@ -317,18 +317,21 @@ def cpu_baseline(spec, inp, layer, bufs, n_tokens):
     return baseline, parity
 
 
-def bf16_slots_measure(layer, x, bias, bufs, steps, warmup):
-    """The same layer step with the routed slot rows held in bf16 (half their
-    bytes; each routed term then carries one bf16 rounding into the sum)."""
+def other_slots_measure(layer, x, bias, bufs, steps, warmup):
+    """The same layer step with the routed slot rows in the other dtype: fp32
+    (the library default, twice the bytes, no rounding of the routed terms)
+    when the workload holds them in bf16, and the other way round."""
     keep = layer.slot_dtype, layer.out_slots
-    layer.slot_dtype = "bf16"
-    layer.out_slots = torch.empty(keep[1].shape, dtype=torch.bfloat16, device="cuda")
+    other = "f32" if keep[0] == "bf16" else "bf16"
+    layer.slot_dtype = other
+    layer.out_slots = torch.empty(keep[1].shape, dtype=torch.float32 if other == "f32" else torch.bfloat16,
+                                  device="cuda")
     try:
         step_ms = []
         sec = time_steps(layer, x, bias, bufs, steps, warmup, None, step_ms)
     finally:
         layer.slot_dtype, layer.out_slots = keep
-    return {"slot_dtype": "bf16", "ms_per_step": sec * 1e3, "tokens_per_s": x.shape[0] / sec,
+    return {"slot_dtype": other, "ms_per_step": sec * 1e3, "tokens_per_s": x.shape[0] / sec,
             **spread(step_ms)}
 
 
@@ -759,8 +762,9 @@ def main():
                      "mfma_TFLOPs": achieved, "mfma_peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                      "mfma_frac": achieved / MFMA_BF16_PEAK_TFLOPS},
     }
-    log("[bench] the same step with bf16 slot rows")
-    result["bf16_slots"] = bf16_slots_measure(layer, x, bias, bufs, args.steps, args.warmup)
+    other = other_slots_measure(layer, x, bias, bufs, args.steps, args.warmup)
+    log(f"[bench] the same step with {other['slot_dtype']} slot rows: {other['ms_per_step']:.3f} ms")
+    result[f"{other['slot_dtype']}_slots"] = other
     plain_route = route_ms(layer, x, bias)
     result["route_ms"] = plain_route
     result["sequence_loads_ms"] = sequence_loads_ms(layer, spec, seq_len=4096)

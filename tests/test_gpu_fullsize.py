@@ -72,12 +72,12 @@ def _coverage_rows(res, spec, r, n_random=12):
 @pytest.mark.parametrize("name,coverage", [("dsmoe2024_bf16", "all"), ("v3_prefill_bf16", "all"),
                                            ("v3_decode_fp8", "all"), ("v3_grouped_bf16", "tiles"),
                                            ("v3_ep8_shard_bf16", "tiles"),
-                                           ("v3_prefill_bf16:bf16_slots", "tiles")])
+                                           ("v3_prefill_bf16:f32_slots", "tiles")])
 def test_fullsize_layer(name, coverage):
     name, _, variant = name.partition(":")
     spec = synth.get_config(name)
-    if variant == "bf16_slots":          # the routed slot rows held in bf16
-        spec = synth.scaled_config(name, name=name + "_bf16_slots", slot_dtype="bf16")
+    if variant == "f32_slots":           # the routed slot rows in fp32 (the library default)
+        spec = synth.scaled_config(name, name=name + "_f32_slots", slot_dtype="f32")
     say(f"[full] {name}: generating inputs")
     inp = synth.make_inputs(spec, "cuda")
     layer, res = run_steps(spec, inp, bias=inp["bias"], side_stream=True)
