@@ -178,3 +178,46 @@ def check_outputs(spec, layer, inp, res, r, x=None, rows=None, residual=None):
     osl = oracle.decode_stored(host(layer.out_slots[slot_rows].contiguous())).reshape(len(rows), K, d)
     e_o = check_slot_rows(osl, aligned, layer.slot_dtype, tol)
     return {"y_err": e_y, "y_rms": rms, "slot_err": e_o}
+
+
+def sample_rows(T, n, near, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(T, min(n, T), replace=False).tolist())
+    rows.update(np.flatnonzero(near)[:4].tolist())
+    return np.array(sorted(rows))
+
+
+def tile_bm(rows_per_expert):
+    """Token-tile height the grouped GEMMs pick for this many expected rows
+    per expert (32 / 64 / 128 / 256; the fine-grained fp8 kernels stop at
+    128)."""
+    for bm in (32, 64, 128):
+        if rows_per_expert <= bm:
+            return bm
+    return 256
+
+
+def tile_edge_tokens(offsets, perm, K, E, T, max_bm=256):
+    """Tokens owning the first and the last row of every token tile of every
+    expert: an expert's m rows are split into ceil(m / bm) tiles of equal
+    height (a multiple of 32 rows), the last one ragged."""
+    bm = min(tile_bm(-(-T * K // E)), max_bm)
+    toks = set()
+    for e in range(E):
+        m = int(offsets[e + 1] - offsets[e])
+        if m == 0:
+            continue
+        mt = -(-m // bm)
+        per = ((-(-m // mt)) + 31) & ~31
+        for j in range(mt):
+            for p in (j * per, min(m, (j + 1) * per) - 1):
+                toks.add(int(perm[offsets[e] + p]) // K)
+    return toks
+
+
+def coverage_rows(offsets, perm, spec, near_tie, n_random=12, max_bm=256):
+    """The tokens owning every token tile's first and last row, a few random
+    tokens and the first near-ties, sorted."""
+    toks = tile_edge_tokens(offsets, perm, spec.K, spec.E, spec.T, max_bm)
+    toks.update(sample_rows(spec.T, n_random, near_tie).tolist())
+    return np.array(sorted(toks))

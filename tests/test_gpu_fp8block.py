@@ -6,21 +6,28 @@ routing bit-exact up to near-ties.
 The intermediate h is quantised from each side's own value (fp32 on the GPU
 from fp8 MFMA partial sums; float64 rounded to fp32 in the oracle), so an h
 code may differ by a step where the value sits near a rounding boundary: an
-integer decided by floating point, treated like a routing near-tie. Three
-comparisons:
-  * validity: every GPU h code the oracle does not produce lies within the
-    worst-case error window of its rounding interval, and every tile scale
-    within that window's effect; the window follows from the accuracy taken
-    per fp8 MFMA (EPS_MFMA, checked on the GPU by
-    test_fp8_mfma_accumulation_bound) and the oracle's operands;
+integer decided by floating point, treated like a routing near-tie. The
+window for that comes from the page alone: fp8 GEMM accumulation inside the
+matrix unit keeps about 14 bits (section 4.3), read as g and u within
+2^-14 sum |x w| of their exact values, plus the fp32 promotion of each
+128-wide block and the fp32 SiLU and product, carried through h from the
+oracle's own operands. Three comparisons:
+  * validity: every GPU h code the oracle does not produce lies within that
+    window of its rounding interval, and every tile scale within the
+    window's effect;
   * the outputs against the oracle's down projection of the GPU's
     (validated) h codes, within 2e-2 x RMS (the down GEMM's arithmetic);
   * the outputs against the oracle's own evaluation (its own h codes; no GPU
     value on the expected side), within 2e-2 x RMS plus B: what the h codes
-    lying within the page's stated in-unit accumulation precision (about 14
-    bits) of a rounding boundary can move each output, one code range times
-    the scale, |W2| and the gate (an oracle-side quantity); at the full V3
-    shape also within the plain 2e-2 x RMS.
+    inside the window can move each output, the reachable code range times
+    the scale, |W2| and the gate (an oracle-side quantity). The plain
+    2e-2 x RMS does not hold here at any width: one code flipped at the top
+    of a tile moves h by 32/448 of the tile's max, and the shared expert's
+    output carries it unweighted (3.9e-2 x RMS measured at the full V3
+    shape over the tokens of every tile edge).
+The accuracy of a single fp8 MFMA instruction on this part is measured by
+test_fp8_mfma_accumulation_bound; it is what makes the per-block fp32
+promotion necessary, and none of the three comparisons uses it.
 """
 
 import numpy as np
@@ -30,8 +37,8 @@ import torch
 import mixture_experts_layer_40_amd as moe
 import oracle
 import synth
-from gpu_parity import (check_permutation, check_route, check_slot_rows, host, oracle_route,
-                        rel_err, run_steps, say)
+from gpu_parity import (check_permutation, check_route, check_slot_rows, coverage_rows, host,
+                        oracle_route, rel_err, run_steps, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,55 +93,42 @@ CASES = {
     "two_shared": _cfg(T=200, d=384, E=16, K=4, I=128, S=2, Is=256),
 }
 
-# Accuracy assumed of the fp8 MFMA. The page notes that fp8 GEMM
-# accumulation inside the matrix unit keeps only about 14 bits, which is why
-# its scheme promotes each 128-element partial sum to fp32. gfx950's
+# Accuracy of one fp8 MFMA instruction, measured on codes of every binade
+# by test_fp8_mfma_accumulation_bound: gfx950's
 # v_mfma_scale_f32_32x32x64_f8f6f4 aligns its products and C input to the
-# largest before summing; the bound taken per instruction is
-#   |D - (A B^T + C)| <= EPS_MFMA (sum_k |a_k b_k| + |C|),
-# which test_fp8_mfma_accumulation_bound checks on codes of every binade.
-EPS_MFMA = 2.0 ** -11
+# largest before summing, within
+#   |D - (A B^T + C)| <= MFMA_EPS (sum_k |a_k b_k| + |C|).
+# The parity checks below do not use it.
+MFMA_EPS = 2.0 ** -11
 U32 = 2.0 ** -24                      # fp32 unit roundoff
 _POS = oracle.E4M3_TABLE[:0x7F]
 
+# In-unit accumulation precision the page states for fp8 GEMMs: about 14
+# bits ("DeepSeekMoE架构解析" section 4.3). Read as: each 128-wide block sum
+# the matrix unit forms is within 2^-14 of the magnitudes it accumulates.
+PAGE_BITS = 14
 
-def _g_bound(xd, w):
-    """|g_GPU - g| for g = xd @ w.T (float64 from the dequantised operands):
-    a 128-wide block is two chained MFMAs from zero, within
-    2 EPS (1 + EPS) sum_block |x w|; each block is then promoted by one fp32
-    product of the two scales and one fp32 FMA into the accumulator, within
-    2^-24 of the scaled block and of the running sum, <= 2 nb 2^-24 (1 + 3 EPS)
-    sum |x w| over the nb blocks."""
+
+def _g_page(xd, w):
+    """|g_GPU - g| for g = xd @ w.T (float64 from the dequantised operands)
+    under the page's precision: each 128-wide block within 2^-14 of its
+    sum |x w|, then promoted by one fp32 product of the two scales and one
+    fp32 FMA into the accumulator (within 2^-24 of the scaled block and of
+    the running sum): (2^-14 + 2 nb 2^-24) sum |x w| over the nb blocks."""
     S = np.abs(xd) @ np.abs(w).T
     nb = xd.shape[1] // 128
-    return (2 * EPS_MFMA * (1 + EPS_MFMA) + 2 * nb * U32 * (1 + 3 * EPS_MFMA)) * S
+    return (2.0 ** -PAGE_BITS + 2 * nb * U32) * S
 
 
-def _h_bound(xd, w1, w3):
+def _h_page(xd, w1, w3):
     """|h_GPU - h| per element for h = SiLU(g) u, g = xd w1^T, u = xd w3^T:
     the bounds on g and u carried through SiLU (|SiLU'| <= 1.1) and the
     product, plus the GPU's own evaluation of SiLU (fp32 exp and division)
     and of the product, within 2^-20 of the value."""
     g, u = xd @ w1.T, xd @ w3.T
-    dg, du = _g_bound(xd, w1), _g_bound(xd, w3)
+    dg, du = _g_page(xd, w1), _g_page(xd, w3)
     sg, au = np.abs(oracle.silu(g)), np.abs(u)
     return 1.1 * dg * (au + du) + sg * du + 2.0 ** -20 * (sg + 1.1 * dg) * (au + du)
-
-
-# In-unit accumulation precision the page states for fp8 GEMMs: about 14
-# bits ("DeepSeekMoE架构解析" section 4.3). Read as: each sum the matrix unit
-# forms is within 2^-14 of the magnitudes it accumulates, so g and u are
-# within 2^-14 sum |x w| of their exact values.
-PAGE_BITS = 14
-
-
-def _h_page(xd, w1, w3):
-    """The page's precision carried to h = SiLU(g) u, to first order:
-    2^-14 (1.1 sum|x w1| |u| + |SiLU(g)| sum|x w3|), from the oracle's own
-    operands."""
-    g, u = xd @ w1.T, xd @ w3.T
-    s1, s3 = np.abs(xd) @ np.abs(w1).T, np.abs(xd) @ np.abs(w3).T
-    return 2.0 ** -PAGE_BITS * (1.1 * s1 * np.abs(u) + np.abs(oracle.silu(g)) * s3)
 
 
 def _code_interval(c):
@@ -174,29 +168,26 @@ def _window(h32, dh):
     return oq, os_, dq, ds, delta, c_lo != c_hi
 
 
-def _check_h(gq, gs, h32, dh, dh_page, counts):
+def _check_h(gq, gs, h32, dh, counts):
     """The GPU's quantised h rows against the oracle's window (_window) for
-    dh, the bound on |h_GPU - h| that EPS_MFMA implies: each tile scale within
-    its bound; codes equal, except where the oracle's scaled value lies
-    within dq of the GPU code's rounding interval. Returns the oracle's
-    codes and scales and, for the window the page's accumulation precision
-    gives (dh_page), the per-element bound on what the GPU's dequantised h
-    may differ by."""
-    oq, os_, dq, ds, _, _ = _window(h32, dh)
-    _, _, _, _, delta, cand = _window(h32, dh_page)
+    dh, the bound on |h_GPU - h| the page's accumulation precision gives:
+    each tile scale within its bound; codes equal, except where the oracle's
+    scaled value lies within dq of the GPU code's rounding interval. Returns
+    the oracle's codes and scales and the per-element bound on what the
+    GPU's dequantised h may differ by."""
+    oq, os_, dq, ds, delta, cand = _window(h32, dh)
     assert np.all(np.abs(gs.astype(np.float64) - os_) <= ds), "an h tile scale is outside its bound"
     diff = gq != oq
     counts[0] += int(diff.sum())
     counts[1] += diff.size
     counts[2] += int(cand.sum())
-    counts[3] += int((diff & ~cand).sum())
     if diff.any():
         q = (h32.astype(np.float64) / np.repeat(os_.astype(np.float64), 128, axis=1))
         lo, hi = _code_interval(gq[diff])
         dist = np.maximum(0.0, np.maximum(lo - q[diff], q[diff] - hi))
         worst = int(np.argmax(dist / dq[diff]))
         assert np.all(dist <= dq[diff]), (
-            f"an h code is outside the accumulation bound: GPU {int(gq[diff][worst])}, "
+            f"an h code is outside the page's accumulation window: GPU {int(gq[diff][worst])}, "
             f"oracle {int(oq[diff][worst])}, q {q[diff][worst]:.6g}, bound {dq[diff][worst]:.3g}")
     return oq, os_, delta
 
@@ -212,9 +203,9 @@ def _codes(rng, shape, lo_exp=0, hi_exp=15):
 
 
 def test_fp8_mfma_accumulation_bound():
-    """The accuracy EPS_MFMA assumes of v_mfma_scale_f32_32x32x64_f8f6f4
+    """The accuracy MFMA_EPS states of v_mfma_scale_f32_32x32x64_f8f6f4
     (one instruction per problem through moe_probe_fp8_mfma): |D - (A B^T +
-    C)| <= EPS_MFMA (sum |a b| + |C|) against the exact sums (every product
+    C)| <= MFMA_EPS (sum |a b| + |C|) against the exact sums (every product
     of two E4M3 values, and every sum here, is exact in float64: products
     are multiples of 2^-18 below 2^18, C a float32 of magnitude >= 2^-4 or
     zero). Cases: codes of every binade with C = 0 (the first MFMA of a
@@ -250,8 +241,8 @@ def test_fp8_mfma_accumulation_bound():
         ratio = err / np.maximum(denom, 1e-300)
         worst = max(worst, float(ratio.max()))
         say(f"[fp8 mfma] {name}: max |err| / (sum |a b| + |C|) = 2^{np.log2(max(ratio.max(), 1e-300)):.2f}")
-        assert np.all(ratio <= EPS_MFMA), f"{name}: 2^{np.log2(ratio.max()):.2f} > EPS_MFMA"
-    say(f"[fp8 mfma] worst 2^{np.log2(max(worst, 1e-300)):.2f}, assumed 2^{np.log2(EPS_MFMA):.0f}")
+        assert np.all(ratio <= MFMA_EPS), f"{name}: 2^{np.log2(ratio.max()):.2f} > MFMA_EPS"
+    say(f"[fp8 mfma] worst 2^{np.log2(max(worst, 1e-300)):.2f}, stated 2^{np.log2(MFMA_EPS):.0f}")
 
 
 def _split_calls(layer, spec):
@@ -279,17 +270,19 @@ def _split_calls(layer, spec):
             None if hsq is None else hsq.cpu().numpy(), None if hss is None else hss.cpu().numpy())
 
 
-def _layer_check(spec, inp, rows=None, plain_pure=False):
+def _layer_check(spec, inp, rows=None):
     """Routing bit-exact up to near-ties; the quantised tokens bit-exact; h
     codes validated (_check_h); the outputs against the oracle's down
     projection of the GPU's validated h codes within 2e-2 x RMS, and against
-    the oracle's own evaluation within 2e-2 x RMS + B (plain 2e-2 x RMS too
-    when plain_pure)."""
+    the oracle's own evaluation within 2e-2 x RMS + B. rows: the tokens whose outputs are checked (all by
+    default), or a function of the GPU's routing results that picks them."""
     layer, res = run_steps(spec, inp, bias=inp.get("bias"))
     r, _ = oracle_route(spec, inp["x"], inp["wr"], inp.get("bias"))
     n_near = check_route(spec, r, res["idx"], res["gate"], res["load"])
     check_permutation(spec, res["idx"], res["offsets"], res["perm"])
     T, K, d = spec.T, spec.K, spec.d
+    if callable(rows):
+        rows = rows(res, r)
     rows = np.arange(T) if rows is None else np.asarray(rows)
     xq, xs = oracle.quantize_x(host(inp["x"][torch.as_tensor(rows, device="cuda")]))
     assert np.array_equal(layer.xq[:T].cpu().numpy()[rows], xq)
@@ -300,7 +293,7 @@ def _layer_check(spec, inp, rows=None, plain_pure=False):
     gate = oracle.gate_values(r["scores"][rows], gpu_idx, spec.norm)   # GPU slot order
     pos = np.empty(T * K, dtype=np.int64)
     pos[res["perm"]] = np.arange(T * K)                 # slot -> row of hq
-    counts = [0, 0, 0, 0]
+    counts = [0, 0, 0]
     routed = np.zeros((len(rows), K, d))
     pure = np.zeros((len(rows), K, d))                  # the oracle with its own h codes
     bound = np.zeros((len(rows), d))                    # B: what the window can move y by
@@ -310,8 +303,7 @@ def _layer_check(spec, inp, rows=None, plain_pure=False):
         h32 = oracle.expert_h_fp8(xq[ri], xs[ri], w1, w3)
         p = pos[rows[ri] * K + ks]
         xd = oracle.dequantize_tiles(xq[ri], xs[ri])
-        oq, os_, delta = _check_h(hq[p], hs[p], h32, _h_bound(xd, w1, w3), _h_page(xd, w1, w3),
-                                  counts)
+        oq, os_, delta = _check_h(hq[p], hs[p], h32, _h_page(xd, w1, w3), counts)
         g = gate[ri, ks][:, None]
         routed[ri, ks] = g * (oracle.dequantize_tiles(hq[p], hs[p]) @ w2.T)
         pure[ri, ks] = g * (oracle.dequantize_tiles(oq, os_) @ w2.T)
@@ -324,8 +316,7 @@ def _layer_check(spec, inp, rows=None, plain_pure=False):
                       zip(zip(*bank.shared_experts()), (0, 0, 1)))
         h32 = oracle.expert_h_fp8(xq, xs, W1, W3)
         xd = oracle.dequantize_tiles(xq, xs)
-        oq, os_, delta = _check_h(hsq[rows], hss[rows], h32, _h_bound(xd, W1, W3),
-                                  _h_page(xd, W1, W3), counts)
+        oq, os_, delta = _check_h(hsq[rows], hss[rows], h32, _h_page(xd, W1, W3), counts)
         y_sh = oracle.dequantize_tiles(hsq[rows], hss[rows]) @ W2.T
         y_sh_pure = oracle.dequantize_tiles(oq, os_) @ W2.T
         bound += delta @ np.abs(W2).T
@@ -346,12 +337,10 @@ def _layer_check(spec, inp, rows=None, plain_pure=False):
     excess = float(((np.abs(y - y_pure) - bound) / rms_pure).max())
     b_rel = float(bound.max() / rms_pure)
     say(f"[fp8b] h codes: {counts[0]} of {counts[1]} differ from the oracle's, {counts[2]} lie "
-        f"within the page's accumulation precision of a rounding boundary ({counts[3]} differing codes "
-        f"outside it); y err / RMS {e_y:.2e} (GPU codes), {e_pure:.2e} (oracle's own codes; "
-        f"B <= {b_rel:.2e} x RMS, excess over B {excess:.2e})")
+        f"within the page's accumulation precision of a rounding boundary; y err / RMS {e_y:.2e} "
+        f"(GPU codes), {e_pure:.2e} (oracle's own codes; B <= {b_rel:.2e} x RMS, excess over B "
+        f"{excess:.2e}) over {len(rows)} tokens")
     assert excess <= TOL, f"y against the oracle's own evaluation: {excess:.3e} x RMS beyond B"
-    if plain_pure:
-        assert e_pure <= TOL, f"y against the oracle's own evaluation: {e_pure:.3e} x RMS"
     return n_near, e_y, e_pure
 
 
@@ -368,7 +357,9 @@ def test_fp8_block_layer_matches_oracle(name):
 def test_fullsize_v3_fp8_block():
     spec = synth.get_config("v3_prefill_fp8b")
     inp = synth.make_inputs(spec, "cuda")
-    rng = np.random.default_rng(0)
-    rows = np.sort(rng.choice(spec.T, 10, replace=False))
-    n_near, e_y, e_pure = _layer_check(spec, inp, rows=rows, plain_pure=True)
+    # the tokens owning the first and last row of every token tile (128-row
+    # tiles in these kernels) of every expert, a few random ones, near-ties
+    def rows(res, r):
+        return coverage_rows(res["offsets"], res["perm"], spec, r["near_tie"], max_bm=128)
+    n_near, e_y, e_pure = _layer_check(spec, inp, rows=rows)
     say(f"[fp8b] full V3: near-ties={n_near} y_err/rms={e_y:.3e} (oracle's own codes {e_pure:.3e})")

@@ -18,7 +18,8 @@ import torch
 
 import oracle
 import synth
-from gpu_parity import check_outputs, check_permutation, check_route, oracle_route, run_steps, say
+from gpu_parity import (check_outputs, check_permutation, check_route, coverage_rows, oracle_route,
+                        run_steps, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,44 +29,8 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _sample_rows(T, n, near, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(T, min(n, T), replace=False).tolist())
-    rows.update(np.flatnonzero(near)[:4].tolist())
-    return np.array(sorted(rows))
-
-
-def _tile_bm(rows_per_expert):
-    """Token-tile height the grouped GEMMs pick for this many expected rows
-    per expert (32 / 64 / 128 / 256)."""
-    for bm in (32, 64, 128):
-        if rows_per_expert <= bm:
-            return bm
-    return 256
-
-
-def _tile_edge_tokens(offsets, perm, K, E, T):
-    """Tokens owning the first and the last row of every token tile of every
-    expert: an expert's m rows are split into ceil(m / bm) tiles of equal
-    height (a multiple of 32 rows), the last one ragged."""
-    bm = _tile_bm(-(-T * K // E))
-    toks = set()
-    for e in range(E):
-        m = int(offsets[e + 1] - offsets[e])
-        if m == 0:
-            continue
-        mt = -(-m // bm)
-        per = ((-(-m // mt)) + 31) & ~31
-        for j in range(mt):
-            for p in (j * per, min(m, (j + 1) * per) - 1):
-                toks.add(int(perm[offsets[e] + p]) // K)
-    return toks
-
-
 def _coverage_rows(res, spec, r, n_random=12):
-    toks = _tile_edge_tokens(res["offsets"], res["perm"], spec.K, spec.E, spec.T)
-    toks.update(_sample_rows(spec.T, n_random, r["near_tie"]).tolist())
-    return np.array(sorted(toks))
+    return coverage_rows(res["offsets"], res["perm"], spec, r["near_tie"], n_random)
 
 
 @pytest.mark.timeout(900)
