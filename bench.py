@@ -3,18 +3,21 @@
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-decode]
                     [--no-grouped] [--no-fp8] [--no-stress] [--no-ep8]
 
-One step = one whole layer call on one batch already resident in HBM:
-router GEMM + sigmoid + biased top-K + gates + loads, the stable permutation,
-the grouped gate/up and down SwiGLU GEMMs over the routed experts and the
-shared expert (one launch each, routed token rows read through the
-permutation), and the combine. The workload is the V3-shape prefill layer:
+One step = one whole layer call on one batch already resident in HBM, in
+the call sequence of MoELayer.forward: the shared expert's SwiGLU FFN on a
+second stream from the start of the call, and on the caller's stream the
+router GEMM + sigmoid + biased top-K + gates + loads, the stable
+permutation, the grouped gate/up and down SwiGLU GEMMs over the routed
+experts (one launch each, token rows read through the permutation), then,
+once both streams are done, the combine. The workload is the V3-shape prefill layer:
 T = 8192 tokens, d = 7168, 256 routed experts of intermediate 2048 (top-8,
 score + bias selection) plus 1 shared expert, bf16, synthetic seeded inputs,
 expert weights relocated once into the tiled layout before timing.
 
 Printed: one JSON line with tokens/s (mean over the timed region, and the
 median and minimum of per-step event timings), the roofline of the dominant
-kernel (the grouped gate/up GEMM, timed live with HIP events on its stream,
+kernel (the routed experts' grouped gate/up GEMM, timed live with HIP
+events on its stream,
 as a fraction of the nominal peaks and of measured ones), the fp64 oracle
 timed on a bounded
 sample on the host's cores with the GPU's error on those tokens, and the
@@ -66,6 +69,11 @@ DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_v3_fp8_traffic.txt"
 CLOCK_FILE = os.path.join(ROOT, "profiles", "gemm_clock.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "mixture_experts_layer_40_amd", "csrc", f)
                   for f in ("ffn.hip", "gemm_core.hpp", "common.hpp")]
+# The call sequence the bf16 / row-scaled fp8 summaries were taken on: the
+# shared experts' FFN on the layer's second stream and the routed experts'
+# two grouped launches on the caller's. A summary of another sequence
+# describes other launches and is not read.
+LAYER_SEQUENCE = "shared-ffn-on-second-stream"
 
 
 def log(*a):
@@ -87,18 +95,30 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_mfma_util(path=MFMA_UTIL_FILE):
-    """Matrix-core busy percentages of the grouped GEMM launches from the
-    committed rocprofv3 counter run (MfmaUtil), if it was taken on the
-    current kernel source; else an empty dict."""
+def read_summary(path, sequence=LAYER_SEQUENCE):
+    """The key = value lines of a committed summary, if it was taken on the
+    current kernel sources (and, with `sequence`, on that call sequence of
+    the layer); else None."""
     if not os.path.exists(path):
-        return {}
+        return None
     kv = {}
     for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
     if kv.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    if sequence is not None and kv.get("layer_sequence") != sequence:
+        return None
+    return kv
+
+
+def measured_mfma_util(path=MFMA_UTIL_FILE):
+    """Matrix-core busy percentages of the grouped GEMM launches from the
+    committed rocprofv3 counter run (MfmaUtil), if it was taken on the
+    current kernel source and call sequence; else an empty dict."""
+    kv = read_summary(path)
+    if kv is None:
         return {}
     return {k[len("mfma_util_"):]: float(v) for k, v in kv.items() if k.startswith("mfma_util_")}
 
@@ -108,14 +128,8 @@ def measured_clock(path=CLOCK_FILE):
     launches from the committed rocprofv3 counter run (GRBM_GUI_ACTIVE over
     each dispatch's duration), if it was taken on the current kernel source;
     with the dense bf16 MFMA rate at that clock. Else an empty dict."""
-    if not os.path.exists(path):
-        return {}
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_src_sha") != kernel_source_hash():
+    kv = read_summary(path)
+    if kv is None:
         return {}
     out = {}
     for k, v in kv.items():
@@ -130,15 +144,10 @@ def measured_clock(path=CLOCK_FILE):
 def measured_traffic(path=TRAFFIC_FILE):
     """HBM bytes from a committed rocprofv3 counter summary (per gate/up launch,
     or per decode layer call for the decode one), if the counters were taken on
-    the current kernel source; else None."""
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            kv[k.strip()] = v.strip()
-    if kv.get("kernel_src_sha") != kernel_source_hash():
+    the current kernel source (and call sequence, except for the fine-grained
+    fp8 layer, which keeps the shared experts in its launches); else None."""
+    kv = read_summary(path, None if path == TRAFFIC_FILE_FP8 else LAYER_SEQUENCE)
+    if kv is None:
         return None
     try:
         return float(kv["decode_gemm_bytes_per_call"] if "decode_gemm_bytes_per_call" in kv
@@ -167,47 +176,61 @@ class Timed:
         return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
 
 
-def gate_up_bytes(spec) -> float:
-    """Algorithmic HBM bytes of one gate/up launch (routed and shared experts):
-    W1 and W3 of every routed expert and of the shared experts once, x once,
-    H and the shared H written once (bf16)."""
-    TK, SI = spec.T * spec.K, spec.S * spec.Is
+def gate_up_bytes(spec, shared=True) -> float:
+    """Algorithmic HBM bytes of one gate/up launch: W1 and W3 of every routed
+    expert (and of the shared experts, when the launch holds them) once, x
+    once, H (and the shared H) written once (bf16)."""
+    TK, SI = spec.T * spec.K, (spec.S * spec.Is if shared else 0)
     return float(spec.E * 2 * spec.I * spec.d * 2 + 2 * SI * spec.d * 2 + spec.T * spec.d * 2
                  + TK * spec.I * 2 + spec.T * SI * 2)
 
 
-def gate_up_flops(spec) -> float:
-    return 4.0 * spec.d * (spec.I * spec.T * spec.K + spec.S * spec.Is * spec.T)
+def gate_up_flops(spec, shared=True) -> float:
+    return 4.0 * spec.d * (spec.I * spec.T * spec.K + (spec.S * spec.Is * spec.T if shared else 0))
 
 
 def layer_step(layer, x, bias, bufs, gate_timer=None):
-    """One full layer call (the fused path of MoELayer.forward), with the
-    expert FFNs issued as their two grouped launches so the gate/up launch
-    can be bracketed by events on its stream."""
+    """One full layer call (the fused path of MoELayer.forward: the shared
+    expert on the layer's second stream, the routed experts on the caller's),
+    with the routed experts issued as their two grouped launches so the
+    gate/up launch can be bracketed by events on its stream."""
     h, hs, ws_gemm = bufs
     cfg = layer._cfg(x.shape[0])
     residual = x if layer.residual else None
     if layer.pre_norm:
         moe.moe_rmsnorm(cfg, x, layer.w["norm_w"], layer.u[:x.shape[0]])
         x = layer.u[:x.shape[0]]
-    layer.route(x, bias)
-    layer.permute(cfg, x, gather=False)
     T, K, w = cfg.num_tokens, cfg.top_k, layer.w
     TK = T * K
+    cur = torch.cuda.current_stream()
+    side = layer.side
+    if side is not None:
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            layer.shared(cfg, x, stream=side)
+    layer.route(x, bias)
+    layer.permute(cfg, x, gather=False)
+    shared_here = side is None and spec_has_shared(layer)   # else on the side stream
+    ecfg = cfg if side is None else layer.routed_cfg(T)
 
     def gate_up():
-        moe.moe_experts_gate_up(cfg, x, layer.expert_offsets, layer.perm_slot[:TK], w["w1"],
-                                w["w3"], w.get("s1"), w.get("s3"), w.get("w1s"), w.get("w3s"),
-                                w.get("s1s"), w.get("s3s"), h, hs, ws=ws_gemm)
+        moe.moe_experts_gate_up(ecfg, x, layer.expert_offsets, layer.perm_slot[:TK], w["w1"],
+                                w["w3"], w.get("s1"), w.get("s3"),
+                                *((w.get("w1s"), w.get("w3s"), w.get("s1s"), w.get("s3s"), h, hs)
+                                  if shared_here else (None, None, None, None, h, None)),
+                                ws=ws_gemm)
     if gate_timer is not None:
         with gate_timer:
             gate_up()
     else:
         gate_up()
-    moe.moe_experts_down(cfg, h, hs, layer.expert_offsets, layer.perm_slot[:TK],
-                         layer.topk_gate[:T], w["w2"], w.get("s2"), w.get("w2s"), w.get("s2s"),
-                         layer.out_slots[:TK], layer.y_shared[:T] if spec_has_shared(layer) else None,
-                         ws=ws_gemm)
+    moe.moe_experts_down(ecfg, h, hs if shared_here else None, layer.expert_offsets,
+                         layer.perm_slot[:TK], layer.topk_gate[:T], w["w2"], w.get("s2"),
+                         w.get("w2s") if shared_here else None,
+                         w.get("s2s") if shared_here else None, layer.out_slots[:TK],
+                         layer.y_shared[:T] if shared_here else None, ws=ws_gemm)
+    if side is not None:
+        cur.wait_stream(side)
     layer.combine(cfg, residual)
 
 
@@ -441,7 +464,7 @@ def ep8_measure(steps, warmup):
     sec = time_steps(layer, x, bias, bufs, steps, warmup, timer, step_ms)
     gms = timer.mean_ms()
     tf = spec.flops() / sec / 1e12
-    gtf = gate_up_flops(spec) / (gms * 1e-3) / 1e12
+    gtf = gate_up_flops(spec, shared=layer.side is None) / (gms * 1e-3) / 1e12
     out = {"workload": EP8, "tokens_per_s": spec.T / sec, "ms_per_step": sec * 1e3,
            **spread(step_ms), "routed_rows": spec.T * spec.K,
            "layer_TFLOPs": tf, "layer_frac_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
@@ -719,8 +742,9 @@ def main():
     sec = time_steps(layer, x, bias, bufs, args.steps, args.warmup, gate_timer, step_ms)
     tokens_per_s = spec.T / sec
     gate_ms = gate_timer.mean_ms()
-    gate_flops = gate_up_flops(spec)
-    gate_bytes = gate_up_bytes(spec)
+    shared_in_launch = layer.side is None   # else the shared FFN runs on the second stream
+    gate_flops = gate_up_flops(spec, shared_in_launch)
+    gate_bytes = gate_up_bytes(spec, shared_in_launch)
     achieved = gate_flops / (gate_ms * 1e-3) / 1e12
     achieved_gbs = gate_bytes / (gate_ms * 1e-3) / 1e9
     layer_tflops = spec.flops() / sec / 1e12
@@ -741,11 +765,12 @@ def main():
         "layer_TFLOPs": layer_tflops,
         "layer_frac_mfma_peak": layer_tflops / MFMA_BF16_PEAK_TFLOPS,
         "load_max_over_mean": float(load.max() / load.mean()),
-        # The gate/up launch (shared + routed experts) does 4*d*I flops per
-        # (token, slot) on weights it must stream once: 279 flop/B at this
-        # shape, below the MI355X ridge (2500 TFLOP/s / 8 TB/s = 312 flop/B), so
-        # the roofline that binds it is HBM; the MFMA view is reported beside it.
-        "roofline": {"kernel": "grouped_gemm_mfma<gate/up, bf16, 256-token tiles, shared + routed>",
+        # The routed experts' gate/up launch does 4*d*I flops per (token,
+        # slot) on weights it must stream once: 250 flop/B at this shape,
+        # below the MI355X ridge (2500 TFLOP/s / 8 TB/s = 312 flop/B), so the
+        # roofline that binds it is HBM; the MFMA view is reported beside it.
+        "roofline": {"kernel": ("grouped_gemm_mfma<gate/up, bf16, 256-token tiles, "
+                                + ("shared + routed>" if shared_in_launch else "routed>")),
                      "bound": "hbm",
                      "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),

@@ -1,7 +1,9 @@
 """The benchmark's readers of the committed rocprofv3 summaries, on the host:
 each summary parses, carries the hash of the kernel sources it was taken on,
 and a reader returns nothing once that hash no longer matches (a changed
-kernel must not be reported with another kernel's counters)."""
+kernel must not be reported with another kernel's counters), nor when a
+summary of the bf16 / row-scaled fp8 launches was taken on another call
+sequence of the layer (other launches)."""
 
 import sys
 from pathlib import Path
@@ -22,11 +24,24 @@ READERS = [
 ]
 
 
-def _sha(path):
+def _key(path, key):
     for line in path.read_text().splitlines():
-        if line.startswith("kernel_src_sha"):
+        if line.startswith(key):
             return line.split("=", 1)[1].strip()
     return None
+
+
+def _sha(path):
+    return _key(path, "kernel_src_sha")
+
+
+def _current(path):
+    """Taken on the current kernel sources and, but for the fine-grained fp8
+    traffic (its launches hold the shared experts), on the current call
+    sequence."""
+    seq_ok = (path.name == "gate_up_v3_prefill_fp8_traffic.txt"
+              or _key(path, "layer_sequence") == bench.LAYER_SEQUENCE)
+    return _sha(path) == bench.kernel_source_hash() and seq_ok
 
 
 @pytest.mark.parametrize("name,reader", READERS, ids=[r[0] for r in READERS])
@@ -41,18 +56,22 @@ def test_summary_has_command_and_hash(name, reader):
 def test_reader_gated_by_source_hash(name, reader, tmp_path):
     path = ROOT / "profiles" / name
     value = reader(str(path))
-    if _sha(path) == bench.kernel_source_hash():
+    if _current(path):
         assert value  # current summary: a number or a non-empty table
     else:
         assert not value
     stale = tmp_path / name
     stale.write_text(path.read_text().replace(_sha(path), "0" * 16))
     assert not reader(str(stale))
+    if name != "gate_up_v3_prefill_fp8_traffic.txt" and _current(path):
+        other = tmp_path / ("seq_" + name)
+        other.write_text(path.read_text().replace(bench.LAYER_SEQUENCE, "another-sequence"))
+        assert not reader(str(other))
 
 
 def test_values_in_physical_range():
-    if _sha(ROOT / "profiles" / "gemm_clock.txt") != bench.kernel_source_hash():
-        pytest.skip("clock summary taken on other kernel sources")
+    if not _current(ROOT / "profiles" / "gemm_clock.txt"):
+        pytest.skip("clock summary taken on other kernel sources or another call sequence")
     clock = bench.measured_clock()
     for name, c in clock.items():
         assert 0.5 < c["ghz"] <= 2.45, name            # engine clock at most the 2.4 GHz peak
