@@ -1,7 +1,9 @@
 """moe_experts (shared and routed experts in one pair of grouped launches,
 routed rows read from x through perm_slot) against the separate calls
-moe_permute (with the row gather) + moe_expert_ffn + moe_shared_ffn: the
-same arithmetic on the same rows, so every output must match bit for bit.
+moe_permute (with the row gather) + moe_expert_ffn + moe_shared_ffn, and
+against the layer's default call sequence (moe_shared_ffn on a second
+stream, moe_experts over the routed experts only): the same arithmetic on
+the same rows, so every output must match bit for bit.
 Also moe_experts_gate_up + moe_experts_down == moe_experts, and the
 argument checks that need a device-free call."""
 
@@ -40,16 +42,19 @@ def test_fused_matches_separate_calls(name, layout):
     say(f"[fused] {name} {layout}")
     inp = synth.make_inputs(spec, "cuda")
     sep = moe.MoELayer(spec, inp, layout=layout, fused=False, shared_stream=False)
-    fus = moe.MoELayer(spec, inp, layout=layout, fused=True)
+    one = moe.MoELayer(spec, inp, layout=layout, fused=True, shared_stream=False)
+    two = moe.MoELayer(spec, inp, layout=layout, fused=True)      # the default sequence
+    assert (two.side is not None) == (spec.S > 0) and one.side is None
     _, a = run_steps(spec, inp, bias=inp["bias"], layer=sep)
-    _, b = run_steps(spec, inp, bias=inp["bias"], layer=fus)
-    for k in ("idx", "gate", "load", "offsets", "perm"):
-        assert np.array_equal(a[k], b[k]), k
     TK = spec.T * spec.K
-    assert torch.equal(sep.out_slots[:TK], fus.out_slots[:TK])
-    if spec.S > 0:
-        assert torch.equal(sep.y_shared, fus.y_shared)
-    assert torch.equal(a["y"], b["y"])
+    for fus in (one, two):
+        _, b = run_steps(spec, inp, bias=inp["bias"], layer=fus)
+        for k in ("idx", "gate", "load", "offsets", "perm"):
+            assert np.array_equal(a[k], b[k]), k
+        assert torch.equal(sep.out_slots[:TK], fus.out_slots[:TK])
+        if spec.S > 0:
+            assert torch.equal(sep.y_shared, fus.y_shared)
+        assert torch.equal(a["y"], b["y"])
 
 
 def test_split_fused_entry_points_equal_moe_experts():
