@@ -58,3 +58,16 @@ def test_to_numpy_stored_bf16_bits():
     t = torch.tensor([1.0, -2.0, 0.5], dtype=torch.bfloat16)
     bits = synth.to_numpy_stored(t)
     assert bits.dtype == np.uint16 and bits.tolist() == [0x3F80, 0xC000, 0x3F00]
+
+
+def test_slot_dtype_of_named_and_reduced_workloads():
+    """The full-size bf16 workloads hold their routed slot rows in bf16; a
+    reduced shape derived from one goes back to the library default (fp32)
+    unless it asks, and the fp32 and fp8 workloads keep fp32."""
+    for name in ("v3_prefill_bf16", "v3_grouped_bf16", "zipf_stress_bf16", "v3_ep8_shard_bf16",
+                 "dsmoe2024_bf16"):
+        assert synth.get_config(name).slot_dtype == "bf16", name
+        assert synth.scaled_config(name, T=64).slot_dtype == "f32", name
+        assert synth.scaled_config(name, T=64, slot_dtype="bf16").slot_dtype == "bf16", name
+    for name in ("tiny_f32", "v3_decode_fp8", "v3_prefill_fp8b"):
+        assert synth.get_config(name).slot_dtype == "f32", name
